@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""MoE decode-step benchmark on one MI355X.
+
+Workload: a GLM-scale MoE layer (hidden 6144, 256 routed experts of
+intermediate 2048 with FP8 E4M3 weights and 128x128 fp32 block scales, top-8,
+one always-on FP8 shared expert of intermediate 2048), decoded for 1 row; the
+same layer is also timed at 4 and 8 independent rows.  All inputs are seeded,
+synthetic and already resident in HBM when the timed region starts.  Eight
+copies of the layer's weights are rotated step by step so that no step finds
+another step's weights in the 256 MB MALL or the L2s; a pool of 16 token rows
+varies the routing.
+
+One step = one moe_decode_step call (router + up/gate + down kernels).  Value =
+algorithmic bytes of the step (each distinct expert counted once, read from
+the step's own dedup table, plus the shared expert, router, gamma, x and out)
+divided by the step time.  The dominant kernel (up/gate) is also timed on its
+own with HIP events recorded by the library around each kernel, on the step's
+stream.  The fp64 CPU oracle is timed on the host for a bounded sample of the
+1-row workload.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE decode layer µs/step + weight-stream HBM GB/s (% of peak) at 1/4/8 rows"
+PEAK_GBS = 8000.0  # MI355X HBM3E, published
+POOL = 16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fp8_matrix_bytes(n, k):
+    return n * k + (n // 128) * (k // 128) * 4
+
+
+def step_bytes(layer, rows, d):
+    H, I, E, Is = layer.hidden, layer.inter, layer.n_experts, layer.shared_inter
+    expert = 2 * fp8_matrix_bytes(I, H) + fp8_matrix_bytes(H, I)
+    shared = (2 * fp8_matrix_bytes(Is, H) + fp8_matrix_bytes(H, Is)) if Is else 0
+    return d * expert + shared + E * H * 2 + H * 2 + 2 * rows * H * 2
+
+
+def upgate_bytes(layer, rows, d):
+    H, I, Is = layer.hidden, layer.inter, layer.shared_inter
+    return (d * 2 * fp8_matrix_bytes(I, H) + (2 * fp8_matrix_bytes(Is, H) if Is else 0)
+            + rows * H + rows * (H // 128) * 4)
+
+
+def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base):
+    stream = torch.cuda.current_stream()
+    runner = B.LayerRunner(layer, rows, stream=stream)
+    weights = [B.LayerRunner.weights_for(c) for c in copies]
+    pool = [S.make_x(rows, layer.hidden, seed=seed_base + t).cuda() for t in range(POOL)]
+    out = torch.empty(rows, layer.hidden, dtype=torch.bfloat16, device="cuda")
+    # distinct experts of each pool entry (selection does not depend on the copy)
+    dvals = []
+    for t in range(POOL):
+        runner.ctx.step(pool[t], rows, weights[0], out, stream)
+        torch.cuda.synchronize()
+        dvals.append(runner.debug(rows)["n_groups"])
+    for i in range(warmup):
+        runner.ctx.step(pool[i % POOL], rows, weights[i % len(weights)], out, stream)
+    nk = B.N_KERNELS
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        runner.ctx.set_timing(evs[i])
+        runner.ctx.step(pool[i % POOL], rows, weights[i % len(weights)], out, stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    runner.ctx.set_timing(None)
+    ms = t0.elapsed_time(t1) / steps
+    kern = [sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(steps)) / steps
+            for k in range(nk)]
+    d_mean = sum(dvals[i % POOL] for i in range(steps)) / steps
+    nbytes = sum(step_bytes(layer, rows, dvals[i % POOL]) for i in range(steps)) / steps
+    ug_bytes = sum(upgate_bytes(layer, rows, dvals[i % POOL]) for i in range(steps)) / steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    ug_gbs = ug_bytes / (kern[1] * 1e-3) / 1e9
+    return dict(rows=rows, us_per_step=ms * 1e3, gbs=gbs, frac=gbs / PEAK_GBS, d_mean=d_mean,
+                bytes_per_step=nbytes, kernel_us=dict(router=kern[0] * 1e3, upgate=kern[1] * 1e3,
+                                                      down=kern[2] * 1e3),
+                upgate_gbs=ug_gbs, upgate_bytes=ug_bytes, runner=runner, pool=pool,
+                weights=weights, dvals=dvals)
+
+
+def cpu_baseline(torch, layer, res, seconds):
+    from oracle import oracle as O
+    from tests import parity as P
+    cores = min(16, len(os.sched_getaffinity(0)))
+    runner, pool = res["runner"], res["pool"]
+    cache = {}
+    done, t_used, nbytes, errs = 0, 0.0, 0.0, []
+    out = torch.empty(1, layer.hidden, dtype=torch.bfloat16, device="cuda")
+    while done < POOL and (done == 0 or t_used < seconds):
+        x = pool[done]
+        runner.ctx.step(x, 1, res["weights"][0], out)
+        torch.cuda.synchronize()
+        gpu = runner.debug(1)
+        ids = sorted(set(int(e) for e in gpu["ids"].ravel()))
+        for e in ids:
+            if e not in cache:
+                cache[e] = P.expert_host(layer, e)
+        xc = x.cpu()
+        t = time.perf_counter()
+        ref_out, ref = P.oracle_for(layer, xc, gpu["logits"], nthreads=cores, host_cache=cache)
+        t_used += time.perf_counter() - t
+        nbytes += step_bytes(layer, 1, gpu["n_groups"])
+        rep = P.compare(layer, xc, gpu, out, ref_out, ref)
+        errs.append(rep["out_err_rel_max"])
+        done += 1
+    gbs = nbytes / t_used / 1e9
+    return dict(value=gbs, unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{done} full 1-row GLM-scale steps (router, 8 routed + shared expert, "
+                       f"combine) in {t_used:.1f} s; fp64, {cores} OpenMP threads",
+                ms_per_step=t_used / done * 1e3), max(errs)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rows", default="1,4,8")
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the decode step has no multi-GPU path in this "
+              "library (how it would shard is described in DESIGN.md); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_moe_decode_amd import binding as B
+    from bit_moe_decode_amd import synth as S
+
+    B.lib()
+    torch.cuda.set_device(0)
+    log("generating GLM-scale layer")
+    base = S.make_layer("glm", seed=1001, device="cuda")
+    copies = [base]
+    for _ in range(args.copies - 1):
+        c = S.Layer(base.shape, base.hidden, base.inter, base.n_experts, base.shared_inter,
+                    base.rms_eps, base.gamma.clone(), base.router_w.clone(),
+                    S.ExpertWeights(base.routed.fmt, *[tuple(t.clone() for t in m) for m in
+                                                       (base.routed.gate, base.routed.up,
+                                                        base.routed.down)]),
+                    S.ExpertWeights(base.shared.fmt, *[tuple(t.clone() for t in m) for m in
+                                                       (base.shared.gate, base.shared.up,
+                                                        base.shared.down)]))
+        copies.append(c)
+    torch.cuda.synchronize()
+    log(f"{len(copies)} layer copies resident")
+
+    results = {}
+    for rows in [int(r) for r in args.rows.split(",")]:
+        log(f"timing rows={rows}")
+        results[rows] = time_rows(torch, B, S, base, copies, rows, args.steps, args.warmup,
+                                  seed_base=5000 + 100 * rows)
+        r = results[rows]
+        log(f"rows={rows}: {r['us_per_step']:.1f} us/step, {r['gbs']:.0f} GB/s "
+            f"({100 * r['frac']:.1f}% of peak), D={r['d_mean']:.1f}, kernels {r['kernel_us']}")
+
+    main_rows = 1 if 1 in results else min(results)
+    m = results[main_rows]
+    cpu, err = (None, None)
+    if not args.no_cpu_baseline and main_rows == 1:
+        log("timing the oracle on the host")
+        cpu, err = cpu_baseline(torch, base, m, args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": round(m["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["us_per_step"] / 1e3, 5),
+        "us_per_step": round(m["us_per_step"], 2),
+        "frac_of_peak": round(m["frac"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"GLM-scale MoE decode layer, {main_rows} row: hidden 6144, "
+                               "256 routed experts (top-8) of intermediate 2048 + 1 shared "
+                               "expert of 2048, FP8 E4M3 weights with 128x128 fp32 scales, "
+                               "FP8 activations and mid, bf16 in/out",
+                   "rows": main_rows, "layer_copies": len(copies), "x_pool": POOL},
+        "roofline": {"bound": "hbm", "kernel": "moe_upgate_kernel",
+                     "achieved": round(m["upgate_gbs"], 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(m["upgate_gbs"] / PEAK_GBS, 4),
+                     "bytes_per_launch": int(m["upgate_bytes"]),
+                     "us_per_launch": round(m["kernel_us"]["upgate"], 2), "traffic": None},
+        "cpu_baseline": cpu,
+        "oracle_check_out_err_rel_max": err,
+        "by_rows": {str(r): {"us_per_step": round(v["us_per_step"], 2), "gbs": round(v["gbs"], 1),
+                             "frac_of_peak": round(v["frac"], 4), "distinct_experts": v["d_mean"],
+                             "bytes_per_step": int(v["bytes_per_step"]),
+                             "kernel_us": {k: round(t, 2) for k, t in v["kernel_us"].items()},
+                             "upgate_gbs": round(v["upgate_gbs"], 1)}
+                    for r, v in results.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

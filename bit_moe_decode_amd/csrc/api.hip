@@ -1,0 +1,323 @@
+// api.hip -- host side of the C ABI declared in include/moe_decode.h:
+// argument validation, workspace layout and kernel launches.  All checks are
+// host-only and run before anything is enqueued.
+#include "moe_decode.h"
+
+#include <new>
+
+#include "device_common.h"
+
+namespace moe {
+hipError_t launch_router(const uint16_t* x, const Weights& w, const Ws& ws, const Dims& d,
+                         hipStream_t stream);
+hipError_t launch_upgate(int ks, int rfmt, int max_groups, const Weights& w, const Ws& ws,
+                         const Dims& d, hipStream_t stream);
+hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws, const Dims& d,
+                       uint16_t* out, hipStream_t stream);
+int upgate_block_rows(int ks);
+hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
+                            hipStream_t stream);
+
+__global__ void moe_fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+constexpr uint32_t kKnownFlags = MOE_F_NO_DEDUP;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+  int H, I, E, Is, R, imax, groups, slots, nc, chunk, ks;
+  size_t off_ctrl_router, off_ctrl_upgate, off_ctrl_down, ctrl_words;
+  size_t off_part, off_ss, off_logits, off_rstd, off_ids, off_gates, off_ngroups, off_gexpert,
+      off_gowner, off_gmask, off_gslot, off_grows, off_gnrows, off_actq, off_acts, off_mid,
+      off_midq, off_midqs, off_ybuf, total;
+};
+
+bool is_mult(int v, int m) { return v > 0 && v % m == 0; }
+
+moe_status plan_config(const moe_decode_config* c, Plan* p) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->top_k != 8) return MOE_ERR_UNSUPPORTED;
+  if (!is_mult(c->hidden, 128) || c->hidden > 16384) return MOE_ERR_UNSUPPORTED;
+  if (!is_mult(c->inter, 128) || c->inter > 16384) return MOE_ERR_UNSUPPORTED;
+  if (c->shared_inter < 0 || c->shared_inter % 128 || c->shared_inter > 16384)
+    return MOE_ERR_UNSUPPORTED;
+  if (!is_mult(c->n_experts, 16) || c->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
+  if (c->max_rows < 1 || c->max_rows > 8) return MOE_ERR_INVALID_ARG;
+  if (c->routed_fmt != MOE_FMT_FP8_E4M3_B128) return MOE_ERR_UNSUPPORTED;
+  if (c->shared_inter > 0 && c->shared_fmt != MOE_FMT_FP8_E4M3_B128) return MOE_ERR_UNSUPPORTED;
+  if (c->flags & ~kKnownFlags) return MOE_ERR_UNSUPPORTED;
+  if (!(c->rms_eps >= 0.0f) || c->rms_eps > 1.0f) return MOE_ERR_INVALID_ARG;
+
+  p->H = c->hidden;
+  p->I = c->inter;
+  p->E = c->n_experts;
+  p->Is = c->shared_inter;
+  p->R = c->max_rows;
+  p->imax = p->I > p->Is ? p->I : p->Is;
+  const int picks = 8 * p->R;
+  p->groups = (c->flags & MOE_F_NO_DEDUP) ? picks : (picks < p->E ? picks : p->E);
+  p->slots = 1 + p->groups;
+  // router K chunks: about 16 chunks of a multiple of 128, at most 1024 wide
+  const int nkb = p->H / 128;
+  int cb = nkb / 16 > 0 ? nkb / 16 : 1;
+  while (nkb % cb) cb--;
+  while (cb * 128 > 1024) {
+    cb--;
+    while (nkb % cb) cb--;
+  }
+  p->chunk = cb * 128;
+  p->nc = p->H / p->chunk;
+  // up/gate K split: halves when the K blocks split evenly
+  p->ks = (nkb % 2 == 0) ? 2 : 1;
+
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  const size_t R = p->R, E = p->E, H = p->H, G = p->groups, S = p->slots, IM = p->imax;
+  p->ctrl_words = 1 + S * (IM / 128) + H / 64;
+  p->off_ctrl_router = take(p->ctrl_words * 4);
+  p->off_ctrl_upgate = p->off_ctrl_router + 4;
+  p->off_ctrl_down = p->off_ctrl_upgate + S * (IM / 128) * 4;
+  p->off_part = take((size_t)p->nc * R * E * 4);
+  p->off_ss = take((size_t)p->nc * R * 4);
+  p->off_logits = take(R * E * 4);
+  p->off_rstd = take(R * 4);
+  p->off_ids = take(R * 8 * 4);
+  p->off_gates = take(R * 8 * 4);
+  p->off_ngroups = take(4);
+  p->off_gexpert = take(G * 4);
+  p->off_gowner = take(G * 2);
+  p->off_gmask = take(G);
+  p->off_gslot = take(G * 8);
+  p->off_grows = take(G * 8);
+  p->off_gnrows = take(G);
+  p->off_actq = take(R * H);
+  p->off_acts = take(R * (H / 128) * 4);
+  p->off_mid = take(S * R * IM * 4);
+  p->off_midq = take(S * R * IM);
+  p->off_midqs = take(S * R * (IM / 128) * 4);
+  p->off_ybuf = take(R * 9 * H * 4);
+  p->total = o;
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+struct moe_decode_ctx {
+  moe_decode_config cfg;
+  Plan plan;
+  char* ws;
+  Ws view;
+  hipEvent_t events[MOE_DECODE_N_KERNELS + 1];
+  bool timing;
+};
+
+extern "C" {
+
+size_t moe_decode_workspace_size(const moe_decode_config* cfg) {
+  Plan p;
+  if (plan_config(cfg, &p) != MOE_OK) return 0;
+  return p.total;
+}
+
+moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t ws_bytes,
+                           hipStream_t stream, moe_decode_ctx** out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  Plan p;
+  moe_status st = plan_config(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (!workspace || ((uintptr_t)workspace & 255u)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < p.total) return MOE_ERR_WORKSPACE;
+  moe_decode_ctx* c = new (std::nothrow) moe_decode_ctx();
+  if (!c) return MOE_ERR_DEVICE;
+  c->cfg = *cfg;
+  c->plan = p;
+  c->ws = static_cast<char*>(workspace);
+  c->timing = false;
+  char* b = c->ws;
+  Ws& v = c->view;
+  v.ctrl_router = reinterpret_cast<uint32_t*>(b + p.off_ctrl_router);
+  v.ctrl_upgate = reinterpret_cast<uint32_t*>(b + p.off_ctrl_upgate);
+  v.ctrl_down = reinterpret_cast<uint32_t*>(b + p.off_ctrl_down);
+  v.part = reinterpret_cast<float*>(b + p.off_part);
+  v.ss_part = reinterpret_cast<float*>(b + p.off_ss);
+  v.logits = reinterpret_cast<float*>(b + p.off_logits);
+  v.rstd = reinterpret_cast<float*>(b + p.off_rstd);
+  v.ids = reinterpret_cast<int32_t*>(b + p.off_ids);
+  v.gates = reinterpret_cast<float*>(b + p.off_gates);
+  v.n_groups = reinterpret_cast<int32_t*>(b + p.off_ngroups);
+  v.grp_expert = reinterpret_cast<int32_t*>(b + p.off_gexpert);
+  v.grp_owner = reinterpret_cast<uint8_t*>(b + p.off_gowner);
+  v.grp_mask = reinterpret_cast<uint8_t*>(b + p.off_gmask);
+  v.grp_slot = reinterpret_cast<uint8_t*>(b + p.off_gslot);
+  v.grp_rows = reinterpret_cast<uint8_t*>(b + p.off_grows);
+  v.grp_nrows = reinterpret_cast<uint8_t*>(b + p.off_gnrows);
+  v.act_q = reinterpret_cast<uint8_t*>(b + p.off_actq);
+  v.act_s = reinterpret_cast<float*>(b + p.off_acts);
+  v.mid = reinterpret_cast<float*>(b + p.off_mid);
+  v.midq = reinterpret_cast<uint8_t*>(b + p.off_midq);
+  v.midqs = reinterpret_cast<float*>(b + p.off_midqs);
+  v.ybuf = reinterpret_cast<float*>(b + p.off_ybuf);
+  // clear the whole workspace once (counters must start at zero; the rest
+  // keeps stale debug views well defined)
+  const size_t words = p.total / 4;
+  hipLaunchKernelGGL(moe_fill_u32_kernel, dim3(256), dim3(256), 0, stream,
+                     reinterpret_cast<uint32_t*>(c->ws), words, 0u);
+  if (hipGetLastError() != hipSuccess) {
+    delete c;
+    return MOE_ERR_DEVICE;
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
+                           const moe_decode_weights* w, uint16_t* out, hipStream_t stream) {
+  if (!ctx) return MOE_ERR_INVALID_ARG;
+  const Plan& p = ctx->plan;
+  if (rows < 0 || rows > p.R) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!x || !w || !out || !aligned16(x) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)rows * p.H * 2;
+  const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out;
+  if (xa < oa + bytes && oa < xa + bytes) return MOE_ERR_INVALID_ARG;
+  const void* need[] = {w->rms_gamma, w->router_w, w->gate.codes, w->gate.scales, w->up.codes,
+                        w->up.scales, w->down.codes, w->down.scales};
+  for (const void* q : need)
+    if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (p.Is > 0) {
+    const void* sh[] = {w->sh_gate.codes, w->sh_gate.scales, w->sh_up.codes,
+                        w->sh_up.scales, w->sh_down.codes, w->sh_down.scales};
+    for (const void* q : sh)
+      if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  }
+
+  Weights wt;
+  wt.gamma = w->rms_gamma;
+  wt.router = w->router_w;
+  wt.gate_c = static_cast<const uint8_t*>(w->gate.codes);
+  wt.up_c = static_cast<const uint8_t*>(w->up.codes);
+  wt.down_c = static_cast<const uint8_t*>(w->down.codes);
+  wt.gate_s = w->gate.scales;
+  wt.up_s = w->up.scales;
+  wt.down_s = w->down.scales;
+  wt.sg_c = static_cast<const uint8_t*>(w->sh_gate.codes);
+  wt.su_c = static_cast<const uint8_t*>(w->sh_up.codes);
+  wt.sd_c = static_cast<const uint8_t*>(w->sh_down.codes);
+  wt.sg_s = static_cast<const float*>(w->sh_gate.scales);
+  wt.su_s = static_cast<const float*>(w->sh_up.scales);
+  wt.sd_s = static_cast<const float*>(w->sh_down.scales);
+
+  Dims d;
+  d.H = p.H;
+  d.I = p.I;
+  d.E = p.E;
+  d.Is = p.Is;
+  d.rows = rows;
+  d.max_rows = p.R;
+  d.imax = p.imax;
+  d.nc = p.nc;
+  d.chunk = p.chunk;
+  d.no_dedup = (ctx->cfg.flags & MOE_F_NO_DEDUP) ? 1 : 0;
+  d.eps = ctx->cfg.rms_eps;
+
+  // groups this step can produce: at most 8 * rows (and E with dedup)
+  const int picks = 8 * rows;
+  const int groups = d.no_dedup ? picks : (picks < p.E ? picks : p.E);
+  hipEvent_t* ev = ctx->timing ? ctx->events : nullptr;
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (launch_router(x, wt, ctx->view, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (launch_upgate(p.ks, ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream) != hipSuccess)
+    return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (launch_down(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, out, stream) != hipSuccess)
+    return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  return MOE_OK;
+}
+
+moe_status moe_decode_debug_view(const moe_decode_ctx* ctx, moe_decode_debug* v) {
+  if (!ctx || !v) return MOE_ERR_INVALID_ARG;
+  const Ws& w = ctx->view;
+  v->logits = w.logits;
+  v->rstd = w.rstd;
+  v->ids = w.ids;
+  v->gates = w.gates;
+  v->n_groups = w.n_groups;
+  v->grp_expert = w.grp_expert;
+  v->grp_owner = w.grp_owner;
+  v->grp_mask = w.grp_mask;
+  v->grp_slot = w.grp_slot;
+  v->act_q = w.act_q;
+  v->act_s = w.act_s;
+  v->mid = w.mid;
+  v->midq = w.midq;
+  v->midqs = w.midqs;
+  v->max_groups = ctx->plan.groups;
+  v->mid_stride = ctx->plan.imax;
+  return MOE_OK;
+}
+
+moe_status moe_decode_set_timing(moe_decode_ctx* ctx, hipEvent_t* events) {
+  if (!ctx) return MOE_ERR_INVALID_ARG;
+  if (!events) {
+    ctx->timing = false;
+    return MOE_OK;
+  }
+  for (int i = 0; i <= MOE_DECODE_N_KERNELS; i++) {
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+    ctx->events[i] = events[i];
+  }
+  ctx->timing = true;
+  return MOE_OK;
+}
+
+void moe_decode_destroy(moe_decode_ctx* ctx) { delete ctx; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_DEVICE: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+moe_status lowbit_gemv(const lowbit_matrix* w, const uint16_t* x, int32_t rows, uint16_t* y,
+                       hipStream_t stream) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (w->fmt != MOE_FMT_Q1_G128) return MOE_ERR_UNSUPPORTED;
+  if (w->n < 0 || w->k <= 0) return MOE_ERR_INVALID_ARG;
+  if (w->k % 128 || w->k > 16384) return MOE_ERR_UNSUPPORTED;
+  if (rows < 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0 || w->n == 0) return MOE_OK;
+  if (rows > 1) return MOE_ERR_UNSUPPORTED;
+  if (!w->codes || !x || !y || !aligned16(w->codes) || !aligned16(x) || !aligned16(y))
+    return MOE_ERR_INVALID_ARG;
+  const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
+  if (xa < ya + (size_t)w->n * 2 && ya < xa + (size_t)w->k * 2) return MOE_ERR_INVALID_ARG;
+  if (launch_lowbit_q1(static_cast<const uint8_t*>(w->codes), x, y, w->n, w->k, stream) !=
+      hipSuccess)
+    return MOE_ERR_DEVICE;
+  return MOE_OK;
+}
+
+}  // extern "C"

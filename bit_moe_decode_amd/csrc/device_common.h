@@ -1,0 +1,121 @@
+// device_common.h -- shared device helpers and the workspace view for the
+// gfx950 MoE decode kernels (router.hip, upgate.hip, down.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxRows = 8;
+
+enum : int { kFmtFp8 = 1, kFmtMxfp4 = 2 };
+
+// Everything a step keeps in the caller's workspace (device pointers).
+struct Ws {
+  uint32_t* ctrl_router;  // [1] arrival counter of the router blocks
+  uint32_t* ctrl_upgate;  // [slots][imax/128] arrivals per mid quantisation block
+  uint32_t* ctrl_down;    // [H/64] arrivals per output tile
+  float* part;            // [nc][max_rows][E] router partial dots per K chunk
+  float* ss_part;         // [nc][max_rows] partial sums of x^2
+  float* logits;          // [max_rows][E]
+  float* rstd;            // [max_rows]
+  int32_t* ids;           // [max_rows][8]
+  float* gates;           // [max_rows][8]
+  int32_t* n_groups;      // [1]
+  int32_t* grp_expert;    // [G]
+  uint8_t* grp_owner;     // [G][2]
+  uint8_t* grp_mask;      // [G]
+  uint8_t* grp_slot;      // [G][8]
+  uint8_t* grp_rows;      // [G][8] using rows, ascending
+  uint8_t* grp_nrows;     // [G]
+  uint8_t* act_q;         // [max_rows][H]
+  float* act_s;           // [max_rows][H/128]
+  float* mid;             // [slots][max_rows][imax]
+  uint8_t* midq;          // [slots][max_rows][imax]
+  float* midqs;           // [slots][max_rows][imax/128]
+  float* ybuf;            // [max_rows][9][H]
+};
+
+// Shapes of the step (all multiples as validated on the host).
+struct Dims {
+  int H, I, E, Is;     // hidden, routed inter, experts, shared inter (0: none)
+  int rows, max_rows;  // this step's rows, the context's maximum
+  int imax;            // max(I, Is)
+  int nc, chunk;       // router K chunks and their width (multiple of 128)
+  int no_dedup;        // 1: one group per (row, pick)
+  float eps;
+};
+
+struct Weights {
+  const uint16_t* gamma;
+  const uint16_t* router;
+  const uint8_t *gate_c, *up_c, *down_c;  // routed codes
+  const void *gate_s, *up_s, *down_s;     // routed scales (fp32 or E8M0 bytes)
+  const uint8_t *sg_c, *su_c, *sd_c;      // shared codes (FP8)
+  const float *sg_s, *su_s, *sd_s;        // shared scales
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x7FFFFFu)) return (uint16_t)((b >> 16) | 0x40);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+// Two fp32 -> two E4M3FN bytes (hardware conversion: round to nearest even,
+// OCP E4M3FN as on gfx950), returned in the low 16 bits.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// 16x16x128 FP8 x FP8 -> fp32 MFMA, unit scales.  A: lane l holds row l%16,
+// K bytes 32*(l/16)..+32; B: lane l holds column l%16, same K bytes;
+// D: lane l holds rows 4*(l/16)+v (v=0..3) of column l%16.
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
+  v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Nontemporal 16-byte load for weights read once per step.
+__device__ __forceinline__ u32x4 ld_nt16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ v8i cat8(const u32x4& lo, const u32x4& hi) {
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+}  // namespace moe

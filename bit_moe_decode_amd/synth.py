@@ -137,10 +137,13 @@ def _stack(fmt, n_exp, n, k, gen, device):
     return torch.stack(codes), torch.stack(scales)
 
 
-def make_layer(shape: str = "tiny", routed_fmt: int = FMT_FP8, seed: int = 1000,
+def make_layer(shape="tiny", routed_fmt: int = FMT_FP8, seed: int = 1000,
                device="cpu") -> Layer:
-    """One MoE layer of the named shape, drawn from ``seed`` on ``device``."""
-    p = SHAPES[shape]
+    """One MoE layer of the named shape (or a dict with the same keys as
+    SHAPES' entries), drawn from ``seed`` on ``device``."""
+    p = SHAPES[shape] if isinstance(shape, str) else dict(shape)
+    if not isinstance(shape, str):
+        shape = "custom"
     H, I, E, Is = p["hidden"], p["inter"], p["n_experts"], p["shared_inter"]
     gen = _gen(seed, device)
     gamma = (torch.rand(H, generator=gen, device=device) * 0.4 + 0.8).to(torch.bfloat16)

@@ -1,0 +1,192 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) small-row MoE decode library.
+ *
+ * One call runs the decode / verify step of a top-8 routed mixture-of-experts
+ * layer for 1..8 token rows, entirely in hand-written HIP kernels on the
+ * caller's stream:
+ *   RMSNorm folded into the router logits -> top-8 (ties to the lower expert
+ *   ID) -> softmax gates -> expert dedup table -> FP8 activation blocks ->
+ *   up/gate GEMV over low-bit weights -> SiLU * gate, mid re-quantised to FP8
+ *   per 1x128 block -> down GEMV -> gate-weighted combine with a shared expert.
+ * A second entry point, lowbit_gemv, is a dense decode GEMV over 1-bit
+ * group-128 weights.
+ *
+ * Sources.  The operations follow the body of sgl-amd-mono PR #85 ("...MoE
+ * expert dedup and weight loads, kernarg reload, LM-head loads"), quoted on the
+ * GitHub page of sglang PR #47324 (cited below as "#85", with "Mod. row N" for
+ * row N of its Modifications table), the README page "SGLang 1-Bit Turbo"
+ * (section "PrismML 1-Bit GGUF Model Support (Q1_0_G128)"), and the page of
+ * sglang PR #31683 "[ROCm][MI35X] Enable GLM-5.2-MXFP4 MTP speculative
+ * decoding" for MXFP4 experts.
+ *
+ * Conventions for every function below:
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or copies device memory on its own; all scratch
+ *    lives in the caller's workspace.  Host objects (the context) are the only
+ *    allocations it makes.
+ *  - Layouts are row-major; "[N, K]" is N rows of K contiguous elements.
+ *    Every pointer must be 16-byte aligned.
+ *  - bf16 values are passed as uint16_t bit patterns.
+ *  - Validation is synchronous and happens before anything is enqueued; on an
+ *    error nothing is launched.  Device faults surface at the caller's next
+ *    synchronisation of the stream.  No C++ exception crosses the ABI.
+ *  - Work is enqueued on `stream` in stream order; the functions do not
+ *    synchronise.  One context per stream: two steps that overlap on one
+ *    workspace race.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null / misaligned pointer, rows out of range, aliasing */
+  MOE_ERR_UNSUPPORTED = 2, /* shape or format outside what the kernels implement */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than moe_decode_workspace_size */
+  MOE_ERR_DEVICE = 4       /* a HIP launch error (hipGetLastError) */
+} moe_status;
+
+/* Weight formats. */
+typedef enum {
+  /* FP8 E4M3 (OCP E4M3FN, largest finite 448) codes uint8 [N, K] with one fp32
+   * scale per 128x128 block, scales float [N/128, K/128] (#85 Mod. rows 18, 21:
+   * FP8 expert weights). */
+  MOE_FMT_FP8_E4M3_B128 = 1,
+  /* MXFP4: E2M1 codes packed two per byte, element 2i in the low nibble,
+   * uint8 [N, K/2], with one E8M0 exponent per 32 elements along K, uint8
+   * [N, K/32] (MXFP4 page; #85 Mod. row 1: MXFP4 experts).  Routed experts
+   * only; their mid is kept in fp32 (not re-quantised). */
+  MOE_FMT_MXFP4 = 2,
+  /* 1-bit group-128: [N, K/128] blocks of 18 bytes, an fp16 scale d
+   * (little-endian) then 16 bytes of sign bits; bit i of byte b is element
+   * 8b+i; bit 1 means -d, bit 0 means +d (1-Bit Turbo, Q1_0_G128).
+   * lowbit_gemv only. */
+  MOE_FMT_Q1_G128 = 3
+} moe_wfmt;
+
+/* flags */
+enum {
+  /* Skip the dedup: every (row, pick) streams its expert separately.  For the
+   * bitwise A/B check that dedup changes no output bit (#85 Mod. row 16: each
+   * row's output is summed in the one-row order). */
+  MOE_F_NO_DEDUP = 1u << 1
+};
+
+typedef struct {
+  int32_t hidden;       /* H: multiple of 128, at most 16384 */
+  int32_t inter;        /* I of a routed expert: multiple of 128, at most 16384 */
+  int32_t n_experts;    /* E: multiple of 16, 16..1024 */
+  int32_t top_k;        /* must be 8 */
+  int32_t shared_inter; /* I of the shared expert, 0 for none; multiple of 128 */
+  int32_t max_rows;     /* 1..8: the widest step this context will run */
+  float rms_eps;        /* RMSNorm epsilon */
+  int32_t routed_fmt;   /* MOE_FMT_FP8_E4M3_B128 or MOE_FMT_MXFP4 */
+  int32_t shared_fmt;   /* MOE_FMT_FP8_E4M3_B128 */
+  uint32_t flags;       /* MOE_F_* */
+} moe_decode_config;
+
+/* One stored matrix: codes and scales in the layout its format fixes. */
+typedef struct {
+  const void* codes;
+  const void* scales;
+} moe_tensor;
+
+typedef struct {
+  const uint16_t* rms_gamma; /* bf16 [H] */
+  const uint16_t* router_w;  /* bf16 [E, H] */
+  moe_tensor gate, up;       /* routed, expert-major stacks of [I, H] */
+  moe_tensor down;           /* routed, expert-major stack of [H, I] */
+  moe_tensor sh_gate, sh_up; /* shared expert [Is, H] (unused when Is == 0) */
+  moe_tensor sh_down;        /* shared expert [H, Is] */
+} moe_decode_weights;
+
+typedef struct moe_decode_ctx moe_decode_ctx;
+
+/* Bytes of device workspace a context with this config needs, or 0 when the
+ * config is not supported. */
+size_t moe_decode_workspace_size(const moe_decode_config* cfg);
+
+/* Validate cfg, bind the caller's workspace (device, >= the size above) and
+ * create a context.  Enqueues one small kernel on `stream` that clears the
+ * workspace's counters; later steps on the same stream are ordered after it.
+ * Returns MOE_ERR_UNSUPPORTED for configs the kernels do not implement,
+ * MOE_ERR_WORKSPACE for a missing or short workspace. */
+moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t ws_bytes,
+                           hipStream_t stream, moe_decode_ctx** out);
+
+/* One decode step (#85: the MoE part of a decoder-layer launch).
+ *  x    bf16 [rows, H] token rows (device)
+ *  rows 0..max_rows; 0 enqueues nothing and returns MOE_OK (zero-work
+ *       launches are skipped)
+ *  w    weights; every pointer it holds is a device pointer
+ *  out  bf16 [rows, H] (device); must not overlap x
+ * The output is the MoE branch only: sum_j g_j * expert_{e_j}(x) + shared(x),
+ * with no residual.  Selection, gates, dedup table, activation blocks and mid
+ * of the last step stay readable through moe_decode_debug_view until the next
+ * step on this context. */
+moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
+                           const moe_decode_weights* w, uint16_t* out, hipStream_t stream);
+
+/* Device pointers into the workspace holding the last step's intermediates. */
+typedef struct {
+  const float* logits;       /* [max_rows, E]: the fp32 values the top-8 compared */
+  const float* rstd;         /* [max_rows] */
+  const int32_t* ids;        /* [max_rows, 8] picks in top-8 order */
+  const float* gates;        /* [max_rows, 8] softmax of the 8 picked logits */
+  const int32_t* n_groups;   /* [1] D, the number of distinct routed experts */
+  const int32_t* grp_expert; /* [max_groups] expert of group g (slot-major first use) */
+  const uint8_t* grp_owner;  /* [max_groups, 2] (slot, row) of the group's first use */
+  const uint8_t* grp_mask;   /* [max_groups] bit r set when row r uses the group */
+  const uint8_t* grp_slot;   /* [max_groups, 8] slot where row r picked it, 0xFF if none */
+  const uint8_t* act_q;      /* [max_rows, H] FP8 activation codes */
+  const float* act_s;        /* [max_rows, H/128] their block scales */
+  /* mid, per expert slot s = 0 (shared expert) or 1 + g (routed group g),
+   * per row, with row stride mid_stride elements: */
+  const float* mid;          /* [1 + max_groups, max_rows, mid_stride] fp32, before quantisation */
+  const uint8_t* midq;       /* [1 + max_groups, max_rows, mid_stride] FP8 codes */
+  const float* midqs;        /* [1 + max_groups, max_rows, mid_stride/128] block scales */
+  int32_t max_groups;        /* min(8 * max_rows, E), or 8 * max_rows with MOE_F_NO_DEDUP */
+  int32_t mid_stride;        /* max(I, Is) */
+} moe_decode_debug;
+
+moe_status moe_decode_debug_view(const moe_decode_ctx* ctx, moe_decode_debug* view);
+
+/* Optional per-kernel timing: when `events` is non-null, every later step
+ * records events[0] before its first kernel and events[i+1] after kernel i
+ * (MOE_DECODE_N_KERNELS kernels), on the step's stream.  The caller owns the
+ * events (hipEventCreate) and must keep them alive; pass NULL to stop. */
+#define MOE_DECODE_N_KERNELS 3
+moe_status moe_decode_set_timing(moe_decode_ctx* ctx, hipEvent_t* events);
+
+void moe_decode_destroy(moe_decode_ctx* ctx);
+
+const char* moe_status_string(moe_status s);
+
+/* Dense decode GEMV over 1-bit group-128 weights (1-Bit Turbo, Q1_0_G128):
+ *   y[n] = bf16( sum_g d[n,g] * sum_{k in g} sign[n,k] * x[k] ),
+ * x used as bf16 directly, fp32 accumulation.
+ *  w->fmt must be MOE_FMT_Q1_G128; w->k a multiple of 128; w->codes points to
+ *  the [N, K/128, 18] blocks (device); w->scales is unused (the scales are in
+ *  the blocks).  rows must be 1 (the reference path is batch 1); 0 is a no-op.
+ *  x bf16 [K], y bf16 [N] (device, no overlap). */
+typedef struct {
+  int32_t fmt, n, k;
+  const void* codes;
+  const void* scales;
+} lowbit_matrix;
+
+moe_status lowbit_gemv(const lowbit_matrix* w, const uint16_t* x, int32_t rows, uint16_t* y,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_DECODE_H */

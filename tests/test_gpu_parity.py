@@ -1,0 +1,161 @@
+"""GPU parity: the HIP library's decode step, called through the C ABI,
+against the fp64 oracle on the same seeded inputs.
+
+Checks per step (see tests/parity.py): bit-exact top-8 judged on the GPU's own
+fp32 logits, bit-exact dedup table, bit-exact activation scales and codes,
+mid codes bit-exact when the oracle's quantiser is applied to the GPU's fp32
+mid and at most one code apart end to end, and the bf16 output within
+2e-2 * max|ref|.  Invariants: dedup on/off and run-to-run bitwise equality,
+row permutation.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from bit_moe_decode_amd import binding as B
+from bit_moe_decode_amd import synth as S
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return S.make_layer("tiny", seed=1000, device="cuda")
+
+
+@pytest.fixture(scope="module")
+def glm():
+    _say("generating the GLM-scale layer on the device")
+    layer = S.make_layer("glm", seed=1001, device="cuda")
+    torch.cuda.synchronize()
+    return layer
+
+
+def _run(layer, x, max_rows=None, flags=0, cache=None, check_mid_codes=True):
+    rows = x.shape[0]
+    runner = B.LayerRunner(layer, max_rows or rows, flags=flags)
+    xd = x.to("cuda")
+    out = runner.run(xd)
+    torch.cuda.synchronize()
+    gpu = runner.debug(rows)
+    ref_out, ref = P.oracle_for(layer, x, gpu["logits"], nthreads=NTHREADS, host_cache=cache)
+    rep = P.compare(layer, x, gpu, out, ref_out, ref, check_mid_codes=check_mid_codes)
+    return runner, out, gpu, rep
+
+
+@pytest.mark.parametrize("rows", [1, 2, 4, 8])
+@pytest.mark.parametrize("mode", ["indep", "corr"])
+def test_tiny_parity(tiny, rows, mode):
+    _say(f"tiny rows={rows} mode={mode}")
+    x = S.make_x(rows, tiny.hidden, seed=2000 + rows, mode=mode)
+    _, _, _, rep = _run(tiny, x)
+    _say(rep)
+
+
+def test_tiny_rows_below_max_rows(tiny):
+    """A context sized for 8 rows running 3-row and 1-row steps."""
+    runner = B.LayerRunner(tiny, 8)
+    for rows in (3, 1, 8):
+        x = S.make_x(rows, tiny.hidden, seed=2100 + rows)
+        out = runner.run(x.cuda())
+        gpu = runner.debug(rows)
+        ref_out, ref = P.oracle_for(tiny, x, gpu["logits"])
+        P.compare(tiny, x, gpu, out, ref_out, ref)
+
+
+def test_tiny_dedup_off_is_bitwise_equal(tiny):
+    for mode in ("indep", "corr"):
+        x = S.make_x(8, tiny.hidden, seed=2200, mode=mode).cuda()
+        on = B.LayerRunner(tiny, 8).run(x)
+        r_off = B.LayerRunner(tiny, 8, flags=B.F_NO_DEDUP)
+        off = r_off.run(x)
+        torch.cuda.synchronize()
+        assert torch.equal(on.view(torch.int16), off.view(torch.int16))
+        d = r_off.debug(8)
+        assert d["n_groups"] == 64 and (d["grp_mask"] != 0).all()
+
+
+def test_tiny_deterministic_and_permutation(tiny):
+    x = S.make_x(8, tiny.hidden, seed=2300, mode="corr").cuda()
+    r = B.LayerRunner(tiny, 8)
+    a = r.run(x).clone()
+    b = r.run(x).clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    perm = torch.tensor([5, 2, 7, 0, 1, 6, 3, 4], device="cuda")
+    c = r.run(x[perm].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), a[perm].view(torch.int16))
+
+
+def test_tiny_max_experts():
+    """E = 1024 (the largest the router handles), 8 rows."""
+    shape = dict(hidden=256, inter=128, n_experts=1024, shared_inter=128, router_std=0.02)
+    layer = S.make_layer(shape, seed=1003, device="cuda")
+    x = S.make_x(8, 256, seed=2400)
+    _run(layer, x)
+
+
+def test_tiny_tied_logits_go_to_lower_id():
+    """Duplicate router rows give exactly equal logits: the lower ID must win."""
+    layer = S.make_layer("tiny", seed=1004, device="cuda")
+    w = layer.router_w
+    for a, b in ((3, 17), (5, 6), (20, 31), (0, 9)):
+        w[b] = w[a]
+    x = S.make_x(4, 256, seed=2500)
+    _, _, gpu, _ = _run(layer, x)
+    for r in range(4):
+        ids = list(gpu["ids"][r])
+        for a, b in ((3, 17), (5, 6), (20, 31), (0, 9)):
+            if a in ids and b in ids:
+                assert ids.index(a) < ids.index(b)
+
+
+def test_zero_rows_is_a_noop(tiny):
+    r = B.LayerRunner(tiny, 4)
+    x = S.make_x(1, 256, seed=1).cuda()
+    out = torch.full((1, 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    assert r.ctx.step_status(x, 0, r.weights, out) == B.MOE_OK
+    torch.cuda.synchronize()
+    assert (out.float() == 7.0).all()
+
+
+def test_step_argument_errors(tiny):
+    r = B.LayerRunner(tiny, 4)
+    x = S.make_x(4, 256, seed=1).cuda()
+    out = torch.empty(4, 256, dtype=torch.bfloat16, device="cuda")
+    assert r.ctx.step_status(x, 5, r.weights, out) == B.MOE_ERR_INVALID_ARG
+    assert r.ctx.step_status(x, -1, r.weights, out) == B.MOE_ERR_INVALID_ARG
+    assert r.ctx.step_status(x, 4, r.weights, x) == B.MOE_ERR_INVALID_ARG      # out aliases x
+    assert r.ctx.step_status(None, 4, r.weights, out) == B.MOE_ERR_INVALID_ARG
+    mis = torch.empty(4 * 256 + 8, dtype=torch.bfloat16, device="cuda")[8:].view(4, 256)
+    assert r.ctx.step_status(x, 4, r.weights, mis) == B.MOE_ERR_INVALID_ARG  # not 16-B aligned
+    w = B.LayerRunner.weights_for(tiny)
+    w.router_w = None
+    assert r.ctx.step_status(x, 4, w, out) == B.MOE_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------- GLM scale
+@pytest.mark.parametrize("rows,mode", [(1, "indep"), (4, "indep"), (4, "corr"),
+                                       (8, "indep"), (8, "corr")])
+def test_glm_parity(glm, rows, mode):
+    _say(f"glm rows={rows} mode={mode}")
+    x = S.make_x(rows, glm.hidden, seed=3000 + 10 * rows + (mode == "corr"), mode=mode)
+    _, _, gpu, rep = _run(glm, x, cache=glm.extra.setdefault("host", {}))
+    _say(rep)
+
+
+def test_glm_dedup_off_is_bitwise_equal(glm):
+    x = S.make_x(8, glm.hidden, seed=3100, mode="corr").cuda()
+    on = B.LayerRunner(glm, 8).run(x)
+    off = B.LayerRunner(glm, 8, flags=B.F_NO_DEDUP).run(x)
+    torch.cuda.synchronize()
+    assert torch.equal(on.view(torch.int16), off.view(torch.int16))
