@@ -243,17 +243,18 @@ void orc_quant_blocks(const float* v, int n, uint8_t* q, float* s) {
  * element: FP8 code * fp32 block scale (per 128x128), or E2M1 * 2^(E8M0-127)
  * (per 32 along K, low nibble = even element). */
 static void orc_gemv(int fmt, const orc_mat* w, int n_out, int k_in, const double* h, double* y,
-                     int nthreads) {
+                     double* yabs, int nthreads) {
   const uint8_t* codes = w->codes;
 #pragma omp parallel for num_threads(nthreads) schedule(static)
   for (int n = 0; n < n_out; n++) {
-    double acc = 0.0;
+    double acc = 0.0, aabs = 0.0;
     if (fmt == ORC_FMT_FP8) {
       const float* sc = (const float*)w->scales;
       for (int k = 0; k < k_in; k++) {
         double wv = lut_e4m3[codes[(size_t)n * k_in + k]] *
                     (double)sc[(size_t)(n / 128) * (k_in / 128) + k / 128];
         acc += wv * h[k];
+        aabs += fabs(wv * h[k]);
       }
     } else {
       const uint8_t* sc = (const uint8_t*)w->scales;
@@ -262,9 +263,11 @@ static void orc_gemv(int fmt, const orc_mat* w, int n_out, int k_in, const doubl
         uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 15);
         double wv = lut_e2m1[nib] * lut_e8m0[sc[(size_t)n * (k_in / 32) + k / 32]];
         acc += wv * h[k];
+        aabs += fabs(wv * h[k]);
       }
     }
     y[n] = acc;
+    if (yabs) yabs[n] = aabs; /* sum of |terms|: sizes rounding-error bounds */
   }
 }
 
@@ -276,12 +279,11 @@ static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
  * row 1: "MXFP4 experts keep their path", which read mid as f32). */
 static void orc_expert(int fmt, const orc_mat* wg, const orc_mat* wu, const orc_mat* wd, int h_dim,
                        int i_dim, const double* hin, int nthreads, double* mid_out,
-                       uint8_t* midq_out, float* midqs_out, double* y) {
-  double* gate = (double*)malloc(sizeof(double) * i_dim);
-  double* upv = (double*)malloc(sizeof(double) * i_dim);
+                       uint8_t* midq_out, float* midqs_out, double* y, double* gate,
+                       double* upv, double* gate_abs, double* up_abs) {
   double* mhat = (double*)malloc(sizeof(double) * i_dim);
-  orc_gemv(fmt, wg, i_dim, h_dim, hin, gate, nthreads);
-  orc_gemv(fmt, wu, i_dim, h_dim, hin, upv, nthreads);
+  orc_gemv(fmt, wg, i_dim, h_dim, hin, gate, gate_abs, nthreads);
+  orc_gemv(fmt, wu, i_dim, h_dim, hin, upv, up_abs, nthreads);
   for (int n = 0; n < i_dim; n++) mid_out[n] = orc_silu(gate[n]) * upv[n];
   if (fmt == ORC_FMT_FP8) {
     float* mf = (float*)malloc(sizeof(float) * i_dim);
@@ -292,9 +294,7 @@ static void orc_expert(int fmt, const orc_mat* wg, const orc_mat* wu, const orc_
   } else {
     for (int n = 0; n < i_dim; n++) mhat[n] = mid_out[n];
   }
-  orc_gemv(fmt, wd, h_dim, i_dim, mhat, y, nthreads);
-  free(gate);
-  free(upv);
+  orc_gemv(fmt, wd, h_dim, i_dim, mhat, y, NULL, nthreads);
   free(mhat);
 }
 
@@ -380,6 +380,10 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
   float* as = (float*)malloc(sizeof(float) * (H / 128));
   double* ys = (double*)malloc(sizeof(double) * 9 * H);
   double* midv = (double*)malloc(sizeof(double) * Imax);
+  double* gv = (double*)malloc(sizeof(double) * Imax);
+  double* uv = (double*)malloc(sizeof(double) * Imax);
+  double* ga = (double*)malloc(sizeof(double) * Imax);
+  double* ua = (double*)malloc(sizeof(double) * Imax);
   uint8_t* mq = (uint8_t*)malloc(Imax);
   float* ms = (float*)malloc(sizeof(float) * (Imax / 128));
   int rc = ORC_OK;
@@ -432,10 +436,16 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
       }
       memset(mq, 0, Imax);
       for (int b = 0; b < Imax / 128; b++) ms[b] = 0.0f;
-      orc_expert(fmt, wg, wu, wd, H, idim, hin, nt, midv, mq, ms, ys + (size_t)j * H);
+      orc_expert(fmt, wg, wu, wd, H, idim, hin, nt, midv, mq, ms, ys + (size_t)j * H, gv, uv, ga,
+                 ua);
       size_t base = ((size_t)r * 9 + j) * Imax;
-      if (dbg->mid)
-        for (int n = 0; n < idim; n++) dbg->mid[base + n] = midv[n];
+      for (int n = 0; n < idim; n++) {
+        if (dbg->mid) dbg->mid[base + n] = midv[n];
+        if (dbg->gate) dbg->gate[base + n] = gv[n];
+        if (dbg->up) dbg->up[base + n] = uv[n];
+        if (dbg->gate_abs) dbg->gate_abs[base + n] = ga[n];
+        if (dbg->up_abs) dbg->up_abs[base + n] = ua[n];
+      }
       if (dbg->midq) memcpy(dbg->midq + base, mq, idim);
       if (dbg->midqs)
         for (int b = 0; b < idim / 128; b++) dbg->midqs[((size_t)r * 9 + j) * (Imax / 128) + b] = ms[b];
@@ -465,6 +475,10 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
   free(as);
   free(ys);
   free(midv);
+  free(gv);
+  free(uv);
+  free(ga);
+  free(ua);
   free(mq);
   free(ms);
   return rc;

@@ -84,6 +84,10 @@ typedef struct {
   float* midqs;     /* [R][9][Imax/128] */
   double* y;        /* [R][9][H] per-slot down outputs */
   double* out_f64;  /* [R][H] combine before the bf16 rounding */
+  double* gate;     /* [R][9][Imax] gate = W_gate . h (h includes rstd) */
+  double* up;       /* [R][9][Imax] */
+  double* gate_abs; /* [R][9][Imax] sum_k |W_gate[n,k] h_k|: sizes rounding bounds */
+  double* up_abs;   /* [R][9][Imax] */
 } orc_debug;
 
 int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,

@@ -36,7 +36,7 @@ class OrcCfg(ctypes.Structure):
 class OrcDebug(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "z", "rstd", "u", "ids", "gates", "act_q", "act_s", "mid", "midq", "midqs",
-        "y", "out_f64")]
+        "y", "out_f64", "gate", "up", "gate_abs", "up_abs")]
 
 
 def lib():
@@ -225,7 +225,8 @@ def moe_step(cfg, x, gamma, router_w, experts, shared=None, anchor_z=None, nthre
         act_q=np.zeros((R, H), np.uint8), act_s=np.zeros((R, H // 128), np.float32),
         mid=np.zeros((R, 9, Imax)), midq=np.zeros((R, 9, Imax), np.uint8),
         midqs=np.zeros((R, 9, Imax // 128), np.float32), y=np.zeros((R, 9, H)),
-        out_f64=np.zeros((R, H)))
+        out_f64=np.zeros((R, H)), gate=np.zeros((R, 9, Imax)), up=np.zeros((R, 9, Imax)),
+        gate_abs=np.zeros((R, 9, Imax)), up_abs=np.zeros((R, 9, Imax)))
     d = OrcDebug(**{k: v.ctypes.data for k, v in dbg.items()})
     rc = lib().orc_moe_step(ctypes.byref(c), _p(x), _p(gamma), _p(router_w), G, U, D,
                             psg, psu, psd, _p(az), _p(out), ctypes.byref(d))

@@ -136,7 +136,7 @@ def test_step_argument_errors(tiny):
     assert r.ctx.step_status(x, -1, r.weights, out) == B.MOE_ERR_INVALID_ARG
     assert r.ctx.step_status(x, 4, r.weights, x) == B.MOE_ERR_INVALID_ARG      # out aliases x
     assert r.ctx.step_status(None, 4, r.weights, out) == B.MOE_ERR_INVALID_ARG
-    mis = torch.empty(4 * 256 + 8, dtype=torch.bfloat16, device="cuda")[8:].view(4, 256)
+    mis = torch.empty(4 * 256 + 4, dtype=torch.bfloat16, device="cuda")[4:].view(4, 256)
     assert r.ctx.step_status(x, 4, r.weights, mis) == B.MOE_ERR_INVALID_ARG  # not 16-B aligned
     w = B.LayerRunner.weights_for(tiny)
     w.router_w = None

@@ -124,6 +124,13 @@ def test_hand_worked_layer_fp8():
         assert np.allclose(d["y"][0, j], np.repeat(y, 128), rtol=1e-13, atol=0)
     mid, sm, y = cf["ysh"]
     assert np.allclose(d["y"][0, 8], np.repeat(y, 128), rtol=1e-13, atol=0)
+    # sums of |terms| of gate / up (used for rounding bounds): 128 A rstd (|S0| + 2|S1|)
+    a, b, _, _, _, _ = _hand_scales()
+    A = 448.0 * cf["s0"]
+    for j, e in enumerate(cf["ids"]):
+        for mats, key in ((a, "gate_abs"), (b, "up_abs")):
+            blk = 128 * A * cf["rstd"] * (np.abs(mats[e][:, 0]) + 2 * np.abs(mats[e][:, 1]))
+            assert np.allclose(d[key][0, j, :I], np.repeat(blk, 128), rtol=1e-13, atol=0)
     assert np.allclose(d["out_f64"][0], cf["out"], rtol=1e-13, atol=0)
     assert np.array_equal(out[0], O.round_bf16_n(d["out_f64"][0]))
 
