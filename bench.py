@@ -10,12 +10,14 @@ copies of the layer's weights are rotated step by step so that no step finds
 another step's weights in the 256 MB MALL or the L2s; a pool of 16 token rows
 varies the routing.
 
-One step = one moe_decode_step call (router + up/gate + down kernels).  Value =
+One step = one moe_decode_step call (router, up/gate, mid quantiser, down +
+combine kernels).  Value =
 algorithmic bytes of the step (each distinct expert counted once, read from
 the step's own dedup table, plus the shared expert, router, gamma, x and out)
-divided by the step time.  The dominant kernel (up/gate) is also timed on its
-own with HIP events recorded by the library around each kernel, on the step's
-stream.  The fp64 CPU oracle is timed on the host for a bounded sample of the
+divided by the step time, timed over back-to-back steps.  A second pass over
+the same steps has the library record HIP events around each kernel on the
+step's stream; the dominant kernel's (up/gate) average duration gives the
+roofline figure.  The fp64 CPU oracle is timed on the host for a bounded sample of the
 1-row workload.
 
 Prints one JSON line on stdout; progress goes to stderr.
@@ -70,18 +72,27 @@ def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base):
     for i in range(warmup):
         runner.ctx.step(pool[i % POOL], rows, weights[i % len(weights)], out, stream)
     nk = B.N_KERNELS
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    # (a) the step as a caller runs it: back-to-back steps, no events between kernels
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(steps):
-        runner.ctx.set_timing(evs[i])
         runner.ctx.step(pool[i % POOL], rows, weights[i % len(weights)], out, stream)
     t1.record(stream)
     torch.cuda.synchronize()
-    runner.ctx.set_timing(None)
     ms = t0.elapsed_time(t1) / steps
+    # (b) the same steps with the library's per-kernel events, for kernel durations
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+    for row in evs:  # torch creates the HIP event on its first record
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        runner.ctx.set_timing(evs[i])
+        runner.ctx.step(pool[i % POOL], rows, weights[i % len(weights)], out, stream)
+    torch.cuda.synchronize()
+    runner.ctx.set_timing(None)
     kern = [sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(steps)) / steps
             for k in range(nk)]
     d_mean = sum(dvals[i % POOL] for i in range(steps)) / steps
@@ -90,8 +101,9 @@ def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base):
     gbs = nbytes / (ms * 1e-3) / 1e9
     ug_gbs = ug_bytes / (kern[1] * 1e-3) / 1e9
     return dict(rows=rows, us_per_step=ms * 1e3, gbs=gbs, frac=gbs / PEAK_GBS, d_mean=d_mean,
-                bytes_per_step=nbytes, kernel_us=dict(router=kern[0] * 1e3, upgate=kern[1] * 1e3,
-                                                      down=kern[2] * 1e3),
+                bytes_per_step=nbytes,
+                kernel_us=dict(router=kern[0] * 1e3, upgate=kern[1] * 1e3, midq=kern[2] * 1e3,
+                               down=kern[3] * 1e3),
                 upgate_gbs=ug_gbs, upgate_bytes=ug_bytes, runner=runner, pool=pool,
                 weights=weights, dvals=dvals)
 

@@ -17,7 +17,7 @@ FMT_FP8 = 1
 FMT_MXFP4 = 2
 FMT_Q1 = 3
 F_NO_DEDUP = 1 << 1
-N_KERNELS = 3
+N_KERNELS = 4
 
 
 class MoeError(RuntimeError):

@@ -12,8 +12,10 @@ hipError_t launch_router(const uint16_t* x, const Weights& w, const Ws& ws, cons
                          hipStream_t stream);
 hipError_t launch_upgate(int ks, int rfmt, int max_groups, const Weights& w, const Ws& ws,
                          const Dims& d, hipStream_t stream);
-hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws, const Dims& d,
-                       uint16_t* out, hipStream_t stream);
+hipError_t launch_midq(int rfmt, int max_groups, const Ws& ws, const Dims& d,
+                       hipStream_t stream);
+hipError_t launch_down(int rfmt, const Weights& w, const Ws& ws, const Dims& d, uint16_t* out,
+                       hipStream_t stream);
 int upgate_block_rows(int ks);
 hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
                             hipStream_t stream);
@@ -35,10 +37,10 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
   int H, I, E, Is, R, imax, groups, slots, nc, chunk, ks;
-  size_t off_ctrl_router, off_ctrl_upgate, off_ctrl_down, ctrl_words;
+  size_t off_ctrl_router, ctrl_words;
   size_t off_part, off_ss, off_logits, off_rstd, off_ids, off_gates, off_ngroups, off_gexpert,
       off_gowner, off_gmask, off_gslot, off_grows, off_gnrows, off_actq, off_acts, off_mid,
-      off_midq, off_midqs, off_ybuf, total;
+      off_midq, off_midqs, total;
 };
 
 bool is_mult(int v, int m) { return v > 0 && v % m == 0; }
@@ -48,8 +50,8 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   if (c->top_k != 8) return MOE_ERR_UNSUPPORTED;
   if (!is_mult(c->hidden, 128) || c->hidden > 16384) return MOE_ERR_UNSUPPORTED;
   if (!is_mult(c->inter, 128) || c->inter > 16384) return MOE_ERR_UNSUPPORTED;
-  if (c->shared_inter < 0 || c->shared_inter % 128 || c->shared_inter > 16384)
-    return MOE_ERR_UNSUPPORTED;
+  // the shared expert, when present, has the routed experts' intermediate size
+  if (c->shared_inter != 0 && c->shared_inter != c->inter) return MOE_ERR_UNSUPPORTED;
   if (!is_mult(c->n_experts, 16) || c->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
   if (c->max_rows < 1 || c->max_rows > 8) return MOE_ERR_INVALID_ARG;
   if (c->routed_fmt != MOE_FMT_FP8_E4M3_B128) return MOE_ERR_UNSUPPORTED;
@@ -86,10 +88,8 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
     return at;
   };
   const size_t R = p->R, E = p->E, H = p->H, G = p->groups, S = p->slots, IM = p->imax;
-  p->ctrl_words = 1 + S * (IM / 128) + H / 64;
+  p->ctrl_words = 1;
   p->off_ctrl_router = take(p->ctrl_words * 4);
-  p->off_ctrl_upgate = p->off_ctrl_router + 4;
-  p->off_ctrl_down = p->off_ctrl_upgate + S * (IM / 128) * 4;
   p->off_part = take((size_t)p->nc * R * E * 4);
   p->off_ss = take((size_t)p->nc * R * 4);
   p->off_logits = take(R * E * 4);
@@ -108,7 +108,6 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   p->off_mid = take(S * R * IM * 4);
   p->off_midq = take(S * R * IM);
   p->off_midqs = take(S * R * (IM / 128) * 4);
-  p->off_ybuf = take(R * 9 * H * 4);
   p->total = o;
   return MOE_OK;
 }
@@ -152,8 +151,6 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
   char* b = c->ws;
   Ws& v = c->view;
   v.ctrl_router = reinterpret_cast<uint32_t*>(b + p.off_ctrl_router);
-  v.ctrl_upgate = reinterpret_cast<uint32_t*>(b + p.off_ctrl_upgate);
-  v.ctrl_down = reinterpret_cast<uint32_t*>(b + p.off_ctrl_down);
   v.part = reinterpret_cast<float*>(b + p.off_part);
   v.ss_part = reinterpret_cast<float*>(b + p.off_ss);
   v.logits = reinterpret_cast<float*>(b + p.off_logits);
@@ -172,7 +169,6 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
   v.mid = reinterpret_cast<float*>(b + p.off_mid);
   v.midq = reinterpret_cast<uint8_t*>(b + p.off_midq);
   v.midqs = reinterpret_cast<float*>(b + p.off_midqs);
-  v.ybuf = reinterpret_cast<float*>(b + p.off_ybuf);
   // clear the whole workspace once (counters must start at zero; the rest
   // keeps stale debug views well defined)
   const size_t words = p.total / 4;
@@ -246,9 +242,12 @@ moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
   if (launch_upgate(p.ks, ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream) != hipSuccess)
     return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (launch_down(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, out, stream) != hipSuccess)
+  if (launch_midq(ctx->cfg.routed_fmt, groups, ctx->view, d, stream) != hipSuccess)
     return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (launch_down(ctx->cfg.routed_fmt, wt, ctx->view, d, out, stream) != hipSuccess)
+    return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return MOE_ERR_DEVICE;
   return MOE_OK;
 }
 

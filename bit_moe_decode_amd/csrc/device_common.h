@@ -20,8 +20,6 @@ enum : int { kFmtFp8 = 1, kFmtMxfp4 = 2 };
 // Everything a step keeps in the caller's workspace (device pointers).
 struct Ws {
   uint32_t* ctrl_router;  // [1] arrival counter of the router blocks
-  uint32_t* ctrl_upgate;  // [slots][imax/128] arrivals per mid quantisation block
-  uint32_t* ctrl_down;    // [H/64] arrivals per output tile
   float* part;            // [nc][max_rows][E] router partial dots per K chunk
   float* ss_part;         // [nc][max_rows] partial sums of x^2
   float* logits;          // [max_rows][E]
@@ -40,7 +38,6 @@ struct Ws {
   float* mid;             // [slots][max_rows][imax]
   uint8_t* midq;          // [slots][max_rows][imax]
   float* midqs;           // [slots][max_rows][imax/128]
-  float* ybuf;            // [max_rows][9][H]
 };
 
 // Shapes of the step (all multiples as validated on the host).
@@ -88,6 +85,24 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
 }
 
+// Pins a value in registers at this point of the program.  Results of MFMA
+// chains must be pinned before any lane-divergent branch that consumes them:
+// otherwise the compiler may sink the last MFMA into that branch, where it
+// would run under a partial EXEC mask and read the masked lanes' operands as
+// missing (the 16 rows and columns of an MFMA come from all 64 lanes).
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin4(float* a) {
+  pin(a[0]);
+  pin(a[1]);
+  pin(a[2]);
+  pin(a[3]);
+}
+__device__ __forceinline__ void pin4(v4f& a) {
+  float t[4] = {a[0], a[1], a[2], a[3]};
+  pin4(t);
+  a = v4f{t[0], t[1], t[2], t[3]};
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
@@ -109,6 +124,28 @@ __device__ __forceinline__ u32x4 ld_nt16(const void* p) {
 }
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Row-contiguous weight tile -> MFMA operand order, through a per-wave LDS
+// tile of 16 rows x 128 bytes (row stride 144 B so that the 16 rows of a
+// column read fall on different banks).  `lo`/`hi` were loaded by lane l from
+// rows (l/8) and 8 + (l/8), 16-byte chunk (l%8) of one 128-wide K block; the
+// result is lane l's A operand: row l%16, bytes 32*(l/16) .. +32.  Only this
+// wave touches `tile`, and LDS operations of one wave complete in order.
+constexpr int kTileStride = 144;
+constexpr int kTileBytes = 16 * kTileStride;
+__device__ __forceinline__ void tile_put(uint8_t* tile, int lane, const u32x4& lo, const u32x4& hi) {
+  *reinterpret_cast<u32x4*>(tile + (lane >> 3) * kTileStride + (lane & 7) * 16) = lo;
+  *reinterpret_cast<u32x4*>(tile + (8 + (lane >> 3)) * kTileStride + (lane & 7) * 16) = hi;
+}
+__device__ __forceinline__ v8i tile_get(const uint8_t* tile, int lane) {
+  const uint8_t* p = tile + (lane & 15) * kTileStride + (lane >> 4) * 32;
+  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
+  v8i r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
 }
 
 __device__ __forceinline__ v8i cat8(const u32x4& lo, const u32x4& hi) {

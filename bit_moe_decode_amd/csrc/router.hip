@@ -53,6 +53,7 @@ struct RouterSmem {
   int last;
 };
 
+template <int CB>  // K blocks of 128 per chunk
 __global__ __launch_bounds__(256) void moe_router_kernel(const uint16_t* __restrict__ x,
                                                          Weights w, Ws ws, Dims d) {
   __shared__ RouterSmem sm;
@@ -106,28 +107,25 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const uint16_t* __restr
   }
 
   // -- 3. router partial dots: 16 experts per wave x token-row columns
-  const int e0 = eg * 64 + wv * 16;
+  // first expert of this wave (wave-uniform: the branch below never splits a wave)
+  const int e0 = __builtin_amdgcn_readfirstlane(eg * 64 + wv * 16);
   if (e0 < E) {
     const int col = lane & 15, kq = (lane >> 4) * 8;
     const uint16_t* wr = w.router + (size_t)(e0 + col) * H + k0 + kq;
-    const int nks = chunk / 32;
+    constexpr int NKS = CB * 4;  // 32-wide K steps of the chunk
+    u32x4 a[NKS];
+#pragma unroll
+    for (int i = 0; i < NKS; i++) a[i] = ld16(wr + i * 32);
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    constexpr int kBatch = 8;
-    for (int ks0 = 0; ks0 < nks; ks0 += kBatch) {
-      u32x4 a[kBatch];
+    // columns past the step's rows read row 0 of the staged u and are never stored
+    const int brow = col < R ? col : 0;
 #pragma unroll
-      for (int i = 0; i < kBatch; i++)
-        if (ks0 + i < nks) a[i] = ld16(wr + (ks0 + i) * 32);
-#pragma unroll
-      for (int i = 0; i < kBatch; i++) {
-        if (ks0 + i < nks) {
-          u32x4 b = {0u, 0u, 0u, 0u};
-          if (col < R) b = *reinterpret_cast<const u32x4*>(&sm.u[col][(ks0 + i) * 32 + kq]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[i]),
-                                                        __builtin_bit_cast(v8bf, b), acc, 0, 0, 0);
-        }
-      }
+    for (int i = 0; i < NKS; i++) {
+      const u32x4 b = *reinterpret_cast<const u32x4*>(&sm.u[brow][i * 32 + kq]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[i]),
+                                                    __builtin_bit_cast(v8bf, b), acc, 0, 0, 0);
     }
+    pin4(acc);  // the MFMA chain runs with every lane, before the row-dependent store
     if (col < R) {
       float* dst = ws.part + ((size_t)c * d.max_rows + col) * E + e0 + 4 * (lane >> 4);
 #pragma unroll
@@ -143,9 +141,20 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const uint16_t* __restr
   if (!sm.last) return;
   __threadfence();
 
+  // sums over the K chunks, in chunk order; each thread issues all of its
+  // loads before adding (a dependent chain of misses would serialise)
+  constexpr int kNcBatch = 16;
   if (tid < R) {
     float s = 0.f;
-    for (int cc = 0; cc < d.nc; cc++) s += ws.ss_part[cc * d.max_rows + tid];
+    for (int c0 = 0; c0 < d.nc; c0 += kNcBatch) {
+      float v[kNcBatch];
+#pragma unroll
+      for (int q = 0; q < kNcBatch; q++)
+        v[q] = (c0 + q < d.nc) ? ws.ss_part[(c0 + q) * d.max_rows + tid] : 0.f;
+#pragma unroll
+      for (int q = 0; q < kNcBatch; q++)
+        if (c0 + q < d.nc) s += v[q];
+    }
     const float rs = 1.0f / sqrtf(s / (float)H + d.eps);
     sm.rstd[tid] = rs;
     ws.rstd[tid] = rs;
@@ -154,7 +163,15 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const uint16_t* __restr
   for (int i = tid; i < R * E; i += 256) {
     const int r = i / E, e = i - r * E;
     float s = 0.f;
-    for (int cc = 0; cc < d.nc; cc++) s += ws.part[((size_t)cc * d.max_rows + r) * E + e];
+    for (int c0 = 0; c0 < d.nc; c0 += kNcBatch) {
+      float v[kNcBatch];
+#pragma unroll
+      for (int q = 0; q < kNcBatch; q++)
+        v[q] = (c0 + q < d.nc) ? ws.part[((size_t)(c0 + q) * d.max_rows + r) * E + e] : 0.f;
+#pragma unroll
+      for (int q = 0; q < kNcBatch; q++)
+        if (c0 + q < d.nc) s += v[q];
+    }
     const float z = sm.rstd[r] * s;
     sm.z[i] = z;
     ws.logits[(size_t)r * E + e] = z;
@@ -260,7 +277,17 @@ namespace moe {
 hipError_t launch_router(const uint16_t* x, const Weights& w, const Ws& ws, const Dims& d,
                          hipStream_t stream) {
   dim3 grid(d.nc, (d.E + 63) / 64);
-  hipLaunchKernelGGL(moe_router_kernel, grid, dim3(256), 0, stream, x, w, ws, d);
+  switch (d.chunk / 128) {
+    case 1: hipLaunchKernelGGL(moe_router_kernel<1>, grid, dim3(256), 0, stream, x, w, ws, d); break;
+    case 2: hipLaunchKernelGGL(moe_router_kernel<2>, grid, dim3(256), 0, stream, x, w, ws, d); break;
+    case 3: hipLaunchKernelGGL(moe_router_kernel<3>, grid, dim3(256), 0, stream, x, w, ws, d); break;
+    case 4: hipLaunchKernelGGL(moe_router_kernel<4>, grid, dim3(256), 0, stream, x, w, ws, d); break;
+    case 5: hipLaunchKernelGGL(moe_router_kernel<5>, grid, dim3(256), 0, stream, x, w, ws, d); break;
+    case 6: hipLaunchKernelGGL(moe_router_kernel<6>, grid, dim3(256), 0, stream, x, w, ws, d); break;
+    case 7: hipLaunchKernelGGL(moe_router_kernel<7>, grid, dim3(256), 0, stream, x, w, ws, d); break;
+    case 8: hipLaunchKernelGGL(moe_router_kernel<8>, grid, dim3(256), 0, stream, x, w, ws, d); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 }  // namespace moe

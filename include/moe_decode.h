@@ -85,7 +85,7 @@ typedef struct {
   int32_t inter;        /* I of a routed expert: multiple of 128, at most 16384 */
   int32_t n_experts;    /* E: multiple of 16, 16..1024 */
   int32_t top_k;        /* must be 8 */
-  int32_t shared_inter; /* I of the shared expert, 0 for none; multiple of 128 */
+  int32_t shared_inter; /* I of the shared expert: 0 for none, else equal to inter */
   int32_t max_rows;     /* 1..8: the widest step this context will run */
   float rms_eps;        /* RMSNorm epsilon */
   int32_t routed_fmt;   /* MOE_FMT_FP8_E4M3_B128 or MOE_FMT_MXFP4 */
@@ -163,7 +163,7 @@ moe_status moe_decode_debug_view(const moe_decode_ctx* ctx, moe_decode_debug* vi
  * records events[0] before its first kernel and events[i+1] after kernel i
  * (MOE_DECODE_N_KERNELS kernels), on the step's stream.  The caller owns the
  * events (hipEventCreate) and must keep them alive; pass NULL to stop. */
-#define MOE_DECODE_N_KERNELS 3
+#define MOE_DECODE_N_KERNELS 4 /* router, up/gate, mid quantiser, down + combine */
 moe_status moe_decode_set_timing(moe_decode_ctx* ctx, hipEvent_t* events);
 
 void moe_decode_destroy(moe_decode_ctx* ctx);
