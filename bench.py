@@ -57,6 +57,22 @@ def upgate_bytes(layer, rows, d):
             + rows * H + rows * (H // 128) * 4)
 
 
+def measured_traffic():
+    """HBM bytes per up/gate launch at one row from the committed counter
+    record, or None when the kernel source changed since it was taken."""
+    import hashlib
+    rec = os.path.join(ROOT, "profiles", "moe_upgate_glm_rows1_traffic.json")
+    if not os.path.exists(rec):
+        return None
+    with open(rec) as f:
+        r = json.load(f)
+    h = hashlib.sha256()
+    for name in ("upgate.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "bit_moe_decode_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return int(r["traffic_bytes"]) if h.hexdigest() == r["source_sha256"] else None
+
+
 def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base):
     stream = torch.cuda.current_stream()
     runner = B.LayerRunner(layer, rows, stream=stream)
@@ -217,7 +233,8 @@ def main():
                      "achieved": round(m["upgate_gbs"], 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(m["upgate_gbs"] / PEAK_GBS, 4),
                      "bytes_per_launch": int(m["upgate_bytes"]),
-                     "us_per_launch": round(m["kernel_us"]["upgate"], 2), "traffic": None},
+                     "us_per_launch": round(m["kernel_us"]["upgate"], 2),
+                     "traffic": measured_traffic() if main_rows == 1 else None},
         "cpu_baseline": cpu,
         "oracle_check_out_err_rel_max": err,
         "by_rows": {str(r): {"us_per_step": round(v["us_per_step"], 2), "gbs": round(v["gbs"], 1),
