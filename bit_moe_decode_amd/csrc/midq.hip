@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void moe_midq_kernel(Ws ws, Dims d, int routed
     for (int i = 0; i < kPer; i++) {
       if (b0 + i >= nb) break;
       const int b = b0 + i;
-      const float amax = wave_max(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])));
+      const float amax = wave_max_nonneg(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])));
       const float s = amax / 448.0f;
       const uint32_t q = (s > 0.f) ? f32x2_to_e4m3(v[i][0] / s, v[i][1] / s) : 0u;
       *reinterpret_cast<uint16_t*>(ws.midq + base + b * 128 + 2 * lane) = (uint16_t)q;

@@ -23,17 +23,12 @@ constexpr int kEMax = 1024;
 
 typedef short v8s __attribute__((ext_vector_type(8)));
 
-// Order key: larger logit first, -0 == +0, NaN below every number; equal
-// values fall to the lower expert ID because its complement is larger.
-__device__ __forceinline__ uint64_t topk_key(float z, int e) {
-  uint32_t k;
-  if (z != z) {
-    k = 0;
-  } else {
-    uint32_t b = (z == 0.0f) ? 0u : __float_as_uint(z);
-    k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  }
-  return ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+// Order key of a logit: unsigned compare = float order, -0 == +0, NaN (1)
+// below every number (-inf maps to 0x007FFFFF), 0 = already picked.
+__device__ __forceinline__ uint32_t topk_vkey(float z) {
+  if (z != z) return 1u;
+  const uint32_t b = (z == 0.0f) ? 0u : __float_as_uint(z);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
 struct RouterSmem {
@@ -59,8 +54,21 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const uint16_t* __restr
   __shared__ RouterSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = blockIdx.x, eg = blockIdx.y;
-  const int H = d.H, R = d.rows, E = d.E, chunk = d.chunk;
+  const int H = d.H, R = d.rows, E = d.E;
+  constexpr int chunk = CB * 128;
   const int k0 = c * chunk;
+
+  // the router weights of this wave's 16 experts over the chunk: issued first,
+  // they do not depend on the staged activations
+  constexpr int NKS = CB * 4;  // 32-wide K steps of the chunk
+  const int e0 = __builtin_amdgcn_readfirstlane(eg * 64 + wv * 16);  // wave-uniform
+  const int col = lane & 15, kq = (lane >> 4) * 8;
+  u32x4 a[NKS];
+  if (e0 < E) {
+    const uint16_t* wr = w.router + (size_t)(e0 + col) * H + k0 + kq;
+#pragma unroll
+    for (int i = 0; i < NKS; i++) a[i] = ld16(wr + i * 32);
+  }
 
   // -- 1. stage u = bf16(x * gamma) for the chunk and the x^2 partial sums
   float ss[kMaxRows];
@@ -97,7 +105,7 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const uint16_t* __restr
       const int r = p / nkc, kb = p % nkc;
       const float u0 = bf16_to_f32(sm.u[r][kb * 128 + 2 * lane]);
       const float u1 = bf16_to_f32(sm.u[r][kb * 128 + 2 * lane + 1]);
-      const float amax = wave_max(fmaxf(fabsf(u0), fabsf(u1)));
+      const float amax = wave_max_nonneg(fmaxf(fabsf(u0), fabsf(u1)));
       const float s = amax / 448.0f;
       const uint32_t q = (s > 0.f) ? f32x2_to_e4m3(u0 / s, u1 / s) : 0u;
       *reinterpret_cast<uint16_t*>(ws.act_q + (size_t)r * H + k0 + kb * 128 + 2 * lane) =
@@ -107,15 +115,7 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const uint16_t* __restr
   }
 
   // -- 3. router partial dots: 16 experts per wave x token-row columns
-  // first expert of this wave (wave-uniform: the branch below never splits a wave)
-  const int e0 = __builtin_amdgcn_readfirstlane(eg * 64 + wv * 16);
   if (e0 < E) {
-    const int col = lane & 15, kq = (lane >> 4) * 8;
-    const uint16_t* wr = w.router + (size_t)(e0 + col) * H + k0 + kq;
-    constexpr int NKS = CB * 4;  // 32-wide K steps of the chunk
-    u32x4 a[NKS];
-#pragma unroll
-    for (int i = 0; i < NKS; i++) a[i] = ld16(wr + i * 32);
     v4f acc = {0.f, 0.f, 0.f, 0.f};
     // columns past the step's rows read row 0 of the staged u and are never stored
     const int brow = col < R ? col : 0;
@@ -133,84 +133,57 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const uint16_t* __restr
     }
   }
 
-  // -- 4. arrival; the last block finishes the routing
-  __threadfence();
+  // -- 4. arrival; the last block finishes the routing.  Producers release
+  // (L2 write-back), only the last block acquires (L2 invalidate).
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (tid == 0) sm.last = (atomicAdd(ws.ctrl_router, 1u) == gridDim.x * gridDim.y - 1);
   __syncthreads();
   if (!sm.last) return;
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-  // sums over the K chunks, in chunk order; each thread issues all of its
-  // loads before adding (a dependent chain of misses would serialise)
-  constexpr int kNcBatch = 16;
+  // sums over the K chunks, in chunk order; every thread issues all of its
+  // loads (float4 over 4 experts, all chunks, two groups) before adding
+  constexpr int kNcMax = 16;
   if (tid < R) {
+    float v[kNcMax];
+#pragma unroll
+    for (int q = 0; q < kNcMax; q++) v[q] = q < d.nc ? ws.ss_part[q * d.max_rows + tid] : 0.f;
     float s = 0.f;
-    for (int c0 = 0; c0 < d.nc; c0 += kNcBatch) {
-      float v[kNcBatch];
 #pragma unroll
-      for (int q = 0; q < kNcBatch; q++)
-        v[q] = (c0 + q < d.nc) ? ws.ss_part[(c0 + q) * d.max_rows + tid] : 0.f;
-#pragma unroll
-      for (int q = 0; q < kNcBatch; q++)
-        if (c0 + q < d.nc) s += v[q];
-    }
+    for (int q = 0; q < kNcMax; q++)
+      if (q < d.nc) s += v[q];
     const float rs = 1.0f / sqrtf(s / (float)H + d.eps);
     sm.rstd[tid] = rs;
     ws.rstd[tid] = rs;
   }
   __syncthreads();
-  for (int i = tid; i < R * E; i += 256) {
-    const int r = i / E, e = i - r * E;
-    float s = 0.f;
-    for (int c0 = 0; c0 < d.nc; c0 += kNcBatch) {
-      float v[kNcBatch];
+  {
+    const int n4 = R * E / 4;  // groups of 4 (row, expert) logits
+    for (int i0 = tid; i0 < n4; i0 += 512) {
+      v4f v[2][kNcMax];
 #pragma unroll
-      for (int q = 0; q < kNcBatch; q++)
-        v[q] = (c0 + q < d.nc) ? ws.part[((size_t)(c0 + q) * d.max_rows + r) * E + e] : 0.f;
+      for (int h = 0; h < 2; h++) {
+        const int i = i0 + 256 * h < n4 ? i0 + 256 * h : i0;
+        const int r = (4 * i) / E, e = 4 * i - r * E;
 #pragma unroll
-      for (int q = 0; q < kNcBatch; q++)
-        if (c0 + q < d.nc) s += v[q];
-    }
-    const float z = sm.rstd[r] * s;
-    sm.z[i] = z;
-    ws.logits[(size_t)r * E + e] = z;
-  }
-  __syncthreads();
-
-  // top-8 per row, one wave a row; lane l holds experts l, l+64, ...
-  for (int r = wv; r < R; r += 4) {
-    uint64_t key[kEMax / kWave];
-#pragma unroll
-    for (int i = 0; i < kEMax / kWave; i++) {
-      const int e = lane + kWave * i;
-      key[i] = (e < E) ? topk_key(sm.z[r * E + e], e) : 0ull;
-    }
-    for (int j = 0; j < 8; j++) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int i = 0; i < kEMax / kWave; i++) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64(best);
-      const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-#pragma unroll
-      for (int i = 0; i < kEMax / kWave; i++)
-        if (lane + kWave * i == e) key[i] = 0ull;
-      if (lane == 0) {
-        sm.ids[r][j] = e;
-        sm.zsel[r][j] = sm.z[r * E + e];
+        for (int q = 0; q < kNcMax; q++)
+          if (q < d.nc)
+            v[h][q] = *reinterpret_cast<const v4f*>(&ws.part[((size_t)q * d.max_rows + r) * E + e]);
       }
-    }
-    if (lane == 0) {
-      float m = sm.zsel[r][0];
-      for (int j = 1; j < 8; j++) m = fmaxf(m, sm.zsel[r][j]);
-      float g[8], sum = 0.f;
-      for (int j = 0; j < 8; j++) {
-        g[j] = expf(sm.zsel[r][j] - m);
-        sum += g[j];
-      }
-      for (int j = 0; j < 8; j++) {
-        ws.gates[r * 8 + j] = g[j] / sum;
-        ws.ids[r * 8 + j] = sm.ids[r][j];
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int i = i0 + 256 * h;
+        if (i >= n4) break;
+        const int r = (4 * i) / E, e = 4 * i - r * E;
+        v4f acc = v[h][0];
+#pragma unroll
+        for (int q = 1; q < kNcMax; q++)
+          if (q < d.nc) acc += v[h][q];
+        const float rs = sm.rstd[r];
+        v4f z = {rs * acc[0], rs * acc[1], rs * acc[2], rs * acc[3]};
+        *reinterpret_cast<v4f*>(&sm.z[r * E + e]) = z;
+        *reinterpret_cast<v4f*>(&ws.logits[(size_t)r * E + e]) = z;
       }
     }
   }
@@ -221,25 +194,84 @@ __global__ __launch_bounds__(256) void moe_router_kernel(const uint16_t* __restr
   }
   __syncthreads();
 
-  // dedup table: lane p holds pick p in slot-major order (p = j*R + r)
+  // top-8 per row, one wave a row; lane l holds experts l, l+64, ...  A round
+  // takes the largest value key across the wave (DPP max); when one lane holds
+  // it (ballot) that lane's expert is the pick, and only an exact tie runs the
+  // expert-ID reduction (#85 Mod. row 9).  Within a lane, scanning experts in
+  // increasing order with a strict compare keeps the lowest ID among equals.
+  for (int r = wv; r < R; r += 4) {
+    uint32_t key[kEMax / kWave];
+#pragma unroll
+    for (int i = 0; i < kEMax / kWave; i++) {
+      const int e = lane + kWave * i;
+      key[i] = (e < E) ? topk_vkey(sm.z[r * E + e]) : 0u;
+    }
+    for (int j = 0; j < 8; j++) {
+      uint32_t best = 0, bid = 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < kEMax / kWave; i++)
+        if (key[i] > best) {
+          best = key[i];
+          bid = lane + kWave * i;
+        }
+      const uint32_t m = dpp_umax(best);
+      const uint64_t holders = __ballot(best == m);
+      uint32_t e;
+      if (__popcll(holders) == 1)
+        e = __builtin_amdgcn_readlane(bid, __ffsll((unsigned long long)holders) - 1);
+      else
+        e = dpp_umin(best == m ? bid : 0xFFFFFFFFu);
+#pragma unroll
+      for (int i = 0; i < kEMax / kWave; i++)
+        if (lane + kWave * i == (int)e) key[i] = 0u;
+      if (lane == 0) {
+        sm.ids[r][j] = (int)e;
+        sm.zsel[r][j] = sm.z[r * E + e];
+      }
+    }
+    if (lane == 0) {
+      float mz = sm.zsel[r][0];
+      for (int j = 1; j < 8; j++) mz = fmaxf(mz, sm.zsel[r][j]);
+      float g[8], sum = 0.f;
+      for (int j = 0; j < 8; j++) {
+        g[j] = expf(sm.zsel[r][j] - mz);
+        sum += g[j];
+      }
+      for (int j = 0; j < 8; j++) {
+        ws.gates[r * 8 + j] = g[j] / sum;
+        ws.ids[r * 8 + j] = sm.ids[r][j];
+      }
+    }
+  }
+  __syncthreads();
+
+  // dedup table: lane p holds pick p in slot-major order (p = j*R + r).  The
+  // lanes holding the same expert are found with one ballot per ID bit; the
+  // lowest of them owns the group (first use), and a group's index is the
+  // number of first uses before its owner.
   if (wv == 0) {
     const int P = 8 * R;
-    int ep = -1, jp = 0, rp = 0;
-    if (lane < P) {
+    const bool valid = lane < P;
+    int ep = 0, jp = 0, rp = 0;
+    if (valid) {
       jp = lane / R;
       rp = lane - jp * R;
       ep = sm.ids[rp][jp];
     }
-    int owner = lane;
-    if (!d.no_dedup) {
-      for (int q = 0; q < P; q++) {
-        const int eq = __shfl(ep, q, kWave);
-        if (eq == ep && q < owner) owner = q;
+    uint64_t same = __ballot(valid);
+    if (d.no_dedup) {
+      same = 1ull << lane;
+    } else {
+#pragma unroll
+      for (int b = 0; b < 10; b++) {  // expert IDs < 1024
+        const uint64_t bb = __ballot(valid && ((ep >> b) & 1));
+        same &= ((ep >> b) & 1) ? bb : ~bb;
       }
     }
-    const uint64_t first = __ballot(lane < P && owner == lane);
+    const int owner = valid ? __ffsll((unsigned long long)same) - 1 : lane;
+    const uint64_t first = __ballot(valid && owner == lane);
     const int gidx = __popcll(first & ((1ull << owner) - 1ull));
-    if (lane < P) {
+    if (valid) {
       atomicOr(&sm.g_mask[gidx], 1u << rp);
       sm.g_slot[gidx][rp] = (uint8_t)jp;
       if (owner == lane) {
