@@ -115,11 +115,11 @@ def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base):
     nbytes = sum(step_bytes(layer, rows, dvals[i % POOL]) for i in range(steps)) / steps
     ug_bytes = sum(upgate_bytes(layer, rows, dvals[i % POOL]) for i in range(steps)) / steps
     gbs = nbytes / (ms * 1e-3) / 1e9
-    ug_gbs = ug_bytes / (kern[1] * 1e-3) / 1e9
+    kernel_us = {name: kern[k] * 1e3 for k, name in enumerate(B.KERNEL_NAMES)}
+    ug_gbs = ug_bytes / (kernel_us["upgate"] * 1e-6) / 1e9
     return dict(rows=rows, us_per_step=ms * 1e3, gbs=gbs, frac=gbs / PEAK_GBS, d_mean=d_mean,
                 bytes_per_step=nbytes,
-                kernel_us=dict(router=kern[0] * 1e3, upgate=kern[1] * 1e3, midq=kern[2] * 1e3,
-                               down=kern[3] * 1e3),
+                kernel_us=kernel_us,
                 upgate_gbs=ug_gbs, upgate_bytes=ug_bytes, runner=runner, pool=pool,
                 weights=weights, dvals=dvals)
 

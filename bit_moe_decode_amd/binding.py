@@ -17,7 +17,8 @@ FMT_FP8 = 1
 FMT_MXFP4 = 2
 FMT_Q1 = 3
 F_NO_DEDUP = 1 << 1
-N_KERNELS = 4
+N_KERNELS = 5
+KERNEL_NAMES = ("router", "route", "upgate", "midq", "down")  # launch order of a step
 
 
 class MoeError(RuntimeError):
@@ -255,7 +256,7 @@ class LayerRunner:
         """Host copies (numpy) of the last step's intermediates."""
         import torch
         v = self.ctx.debug_view()
-        L, R, G, S = self.layer, self.cfg.max_rows, v.max_groups, 1 + v.max_groups
+        L, R, G = self.layer, self.cfg.max_rows, v.max_groups
         E, H, st = L.n_experts, L.hidden, v.mid_stride
         f32, i32, u8 = torch.float32, torch.int32, torch.uint8
         torch.cuda.synchronize()
@@ -272,9 +273,9 @@ class LayerRunner:
             grp_slot=g(v.grp_slot, 8 * G, u8).reshape(G, 8),
             act_q=g(v.act_q, R * H, u8).reshape(R, H)[:rows],
             act_s=g(v.act_s, R * (H // 128), f32).reshape(R, H // 128)[:rows],
-            mid=g(v.mid, S * R * st, f32).reshape(S, R, st),
-            midq=g(v.midq, S * R * st, u8).reshape(S, R, st),
-            midqs=g(v.midqs, S * R * (st // 128), f32).reshape(S, R, st // 128),
+            mid=g(v.mid, R * 9 * st, f32).reshape(R, 9, st)[:rows],
+            midq=g(v.midq, R * 9 * st, u8).reshape(R, 9, st)[:rows],
+            midqs=g(v.midqs, R * 9 * (st // 128), f32).reshape(R, 9, st // 128)[:rows],
         )
         n = d["n_groups"]
         for k in ("grp_expert", "grp_owner", "grp_mask", "grp_slot"):

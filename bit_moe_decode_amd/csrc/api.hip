@@ -10,13 +10,13 @@
 namespace moe {
 hipError_t launch_router(const uint16_t* x, const Weights& w, const Ws& ws, const Dims& d,
                          hipStream_t stream);
-hipError_t launch_upgate(int ks, int rfmt, int max_groups, const Weights& w, const Ws& ws,
+hipError_t launch_route(const Ws& ws, const Dims& d, hipStream_t stream);
+hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& ws,
                          const Dims& d, hipStream_t stream);
-hipError_t launch_midq(int rfmt, int max_groups, const Ws& ws, const Dims& d,
-                       hipStream_t stream);
+hipError_t launch_midq(int rfmt, const Ws& ws, const Dims& d, hipStream_t stream);
 hipError_t launch_down(int rfmt, const Weights& w, const Ws& ws, const Dims& d, uint16_t* out,
                        hipStream_t stream);
-int upgate_block_rows(int ks);
+int upgate_k_parts(int hidden, int inter);
 hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
                             hipStream_t stream);
 
@@ -36,11 +36,10 @@ constexpr uint32_t kKnownFlags = MOE_F_NO_DEDUP;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
-  int H, I, E, Is, R, imax, groups, slots, nc, chunk, ks;
-  size_t off_ctrl_router, ctrl_words;
-  size_t off_part, off_ss, off_logits, off_rstd, off_ids, off_gates, off_ngroups, off_gexpert,
-      off_gowner, off_gmask, off_gslot, off_grows, off_gnrows, off_actq, off_acts, off_mid,
-      off_midq, off_midqs, total;
+  int H, I, E, Is, R, imax, groups, ks;
+  size_t off_logits, off_rstd, off_ids, off_gates, off_ngroups, off_gexpert,
+      off_gowner, off_gmask, off_gslot, off_grows, off_gnrows, off_actq, off_acts, off_gpart,
+      off_upart, off_mid, off_midq, off_midqs, off_pad, total;
 };
 
 bool is_mult(int v, int m) { return v > 0 && v % m == 0; }
@@ -67,19 +66,7 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   p->imax = p->I > p->Is ? p->I : p->Is;
   const int picks = 8 * p->R;
   p->groups = (c->flags & MOE_F_NO_DEDUP) ? picks : (picks < p->E ? picks : p->E);
-  p->slots = 1 + p->groups;
-  // router K chunks: about 16 chunks of a multiple of 128, at most 1024 wide
-  const int nkb = p->H / 128;
-  int cb = nkb / 16 > 0 ? nkb / 16 : 1;
-  while (nkb % cb) cb--;
-  while (cb * 128 > 1024) {
-    cb--;
-    while (nkb % cb) cb--;
-  }
-  p->chunk = cb * 128;
-  p->nc = p->H / p->chunk;
-  // up/gate K split: halves when the K blocks split evenly
-  p->ks = (nkb % 2 == 0) ? 2 : 1;
+  p->ks = upgate_k_parts(p->H, p->I);
 
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -87,11 +74,7 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
     o = align_up(o + bytes, 256);
     return at;
   };
-  const size_t R = p->R, E = p->E, H = p->H, G = p->groups, S = p->slots, IM = p->imax;
-  p->ctrl_words = 1;
-  p->off_ctrl_router = take(p->ctrl_words * 4);
-  p->off_part = take((size_t)p->nc * R * E * 4);
-  p->off_ss = take((size_t)p->nc * R * 4);
+  const size_t R = p->R, E = p->E, H = p->H, G = p->groups, IM = p->imax;
   p->off_logits = take(R * E * 4);
   p->off_rstd = take(R * 4);
   p->off_ids = take(R * 8 * 4);
@@ -105,9 +88,13 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   p->off_gnrows = take(G);
   p->off_actq = take(R * H);
   p->off_acts = take(R * (H / 128) * 4);
-  p->off_mid = take(S * R * IM * 4);
-  p->off_midq = take(S * R * IM);
-  p->off_midqs = take(S * R * (IM / 128) * 4);
+  const size_t U = R * 9;  // (row, pick) pairs, pick 8 = the shared expert
+  p->off_gpart = take(U * p->ks * IM * 4);
+  p->off_upart = take(U * p->ks * IM * 4);
+  p->off_mid = take(U * IM * 4);
+  p->off_midq = take(U * IM);
+  p->off_midqs = take(U * (IM / 128) * 4);
+  p->off_pad = take(2048);  // zero from init on, never written
   p->total = o;
   return MOE_OK;
 }
@@ -150,9 +137,6 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
   c->timing = false;
   char* b = c->ws;
   Ws& v = c->view;
-  v.ctrl_router = reinterpret_cast<uint32_t*>(b + p.off_ctrl_router);
-  v.part = reinterpret_cast<float*>(b + p.off_part);
-  v.ss_part = reinterpret_cast<float*>(b + p.off_ss);
   v.logits = reinterpret_cast<float*>(b + p.off_logits);
   v.rstd = reinterpret_cast<float*>(b + p.off_rstd);
   v.ids = reinterpret_cast<int32_t*>(b + p.off_ids);
@@ -166,11 +150,14 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
   v.grp_nrows = reinterpret_cast<uint8_t*>(b + p.off_gnrows);
   v.act_q = reinterpret_cast<uint8_t*>(b + p.off_actq);
   v.act_s = reinterpret_cast<float*>(b + p.off_acts);
+  v.gpart = reinterpret_cast<float*>(b + p.off_gpart);
+  v.upart = reinterpret_cast<float*>(b + p.off_upart);
   v.mid = reinterpret_cast<float*>(b + p.off_mid);
   v.midq = reinterpret_cast<uint8_t*>(b + p.off_midq);
   v.midqs = reinterpret_cast<float*>(b + p.off_midqs);
-  // clear the whole workspace once (counters must start at zero; the rest
-  // keeps stale debug views well defined)
+  v.pad = reinterpret_cast<const uint8_t*>(b + p.off_pad);
+  // clear the whole workspace once, so that debug views read before the
+  // first step are well defined
   const size_t words = p.total / 4;
   hipLaunchKernelGGL(moe_fill_u32_kernel, dim3(256), dim3(256), 0, stream,
                      reinterpret_cast<uint32_t*>(c->ws), words, 0u);
@@ -227,27 +214,28 @@ moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
   d.rows = rows;
   d.max_rows = p.R;
   d.imax = p.imax;
-  d.nc = p.nc;
-  d.chunk = p.chunk;
+  d.ks = p.ks;
   d.no_dedup = (ctx->cfg.flags & MOE_F_NO_DEDUP) ? 1 : 0;
   d.eps = ctx->cfg.rms_eps;
 
-  // groups this step can produce: at most 8 * rows (and E with dedup)
-  const int picks = 8 * rows;
-  const int groups = d.no_dedup ? picks : (picks < p.E ? picks : p.E);
   hipEvent_t* ev = ctx->timing ? ctx->events : nullptr;
   if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (launch_router(x, wt, ctx->view, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (launch_upgate(p.ks, ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream) != hipSuccess)
-    return MOE_ERR_DEVICE;
+  if (launch_route(ctx->view, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (launch_midq(ctx->cfg.routed_fmt, groups, ctx->view, d, stream) != hipSuccess)
+  // groups this step can produce: at most 8 * rows (and E with dedup)
+  const int picks = 8 * rows;
+  const int groups = d.no_dedup ? picks : (picks < p.E ? picks : p.E);
+  if (launch_upgate(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream) != hipSuccess)
     return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (launch_down(ctx->cfg.routed_fmt, wt, ctx->view, d, out, stream) != hipSuccess)
+  if (launch_midq(ctx->cfg.routed_fmt, ctx->view, d, stream) != hipSuccess)
     return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (launch_down(ctx->cfg.routed_fmt, wt, ctx->view, d, out, stream) != hipSuccess)
+    return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[5], stream) != hipSuccess) return MOE_ERR_DEVICE;
   return MOE_OK;
 }
 

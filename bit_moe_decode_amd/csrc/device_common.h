@@ -1,5 +1,5 @@
 // device_common.h -- shared device helpers and the workspace view for the
-// gfx950 MoE decode kernels (router.hip, upgate.hip, down.hip).
+// gfx950 MoE decode kernels (router.hip, upgate.hip, midq.hip, down.hip).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -19,9 +19,6 @@ enum : int { kFmtFp8 = 1, kFmtMxfp4 = 2 };
 
 // Everything a step keeps in the caller's workspace (device pointers).
 struct Ws {
-  uint32_t* ctrl_router;  // [1] arrival counter of the router blocks
-  float* part;            // [nc][max_rows][E] router partial dots per K chunk
-  float* ss_part;         // [nc][max_rows] partial sums of x^2
   float* logits;          // [max_rows][E]
   float* rstd;            // [max_rows]
   int32_t* ids;           // [max_rows][8]
@@ -35,9 +32,13 @@ struct Ws {
   uint8_t* grp_nrows;     // [G]
   uint8_t* act_q;         // [max_rows][H]
   float* act_s;           // [max_rows][H/128]
-  float* mid;             // [slots][max_rows][imax]
-  uint8_t* midq;          // [slots][max_rows][imax]
-  float* midqs;           // [slots][max_rows][imax/128]
+  // per (row, pick) with pick 8 = the shared expert: u = row * 9 + pick
+  float* gpart;           // [max_rows * 9][ks][imax] up/gate K-part sums of gate
+  float* upart;           // [max_rows * 9][ks][imax] ... and of up
+  float* mid;             // [max_rows * 9][imax]
+  uint8_t* midq;          // [max_rows * 9][imax]
+  float* midqs;           // [max_rows * 9][imax/128]
+  const uint8_t* pad;     // [2048] zero bytes, read in place of weights past a ring's end
 };
 
 // Shapes of the step (all multiples as validated on the host).
@@ -45,7 +46,7 @@ struct Dims {
   int H, I, E, Is;     // hidden, routed inter, experts, shared inter (0: none)
   int rows, max_rows;  // this step's rows, the context's maximum
   int imax;            // max(I, Is)
-  int nc, chunk;       // router K chunks and their width (multiple of 128)
+  int ks;              // up/gate K parts (divides H/128)
   int no_dedup;        // 1: one group per (row, pick)
   float eps;
 };
@@ -63,12 +64,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN kept quiet).
+// fp32 -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32): round to
+// nearest even, NaN stays NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x7FFFFFu)) return (uint16_t)((b >> 16) | 0x40);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // Two fp32 -> two E4M3FN bytes (hardware conversion: round to nearest even,
@@ -129,6 +128,31 @@ __device__ __forceinline__ uint32_t dpp_umin(uint32_t v) {
   v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
   v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Sum and unsigned max over each row of 16 lanes: xor 1 and xor 2 within
+// quads, then the half-row and row mirrors.  Every lane of a row ends with the
+// row's result; for the sum the association differs from lane to lane, so a
+// caller takes one fixed lane's value.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+__device__ __forceinline__ uint32_t row16_umax(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// Number of set bits of `m` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Wave max of non-negative floats (their bit patterns order as unsigned).

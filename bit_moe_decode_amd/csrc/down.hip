@@ -8,13 +8,13 @@
 // FP8 bytes and scales quantised once.  Mod. rows 18 and 21: 16-byte,
 // nontemporal weight loads.
 //
-// Block = 4 waves = HW sub-tiles of 16 output rows x KSD parts of K; the block
-// owns 16*HW output rows and walks every expert of the step (shared first,
-// then the routed groups in table order).  For each 128-wide K block of its
-// part a wave loads its 16 weight rows row-contiguously, re-lays them through
-// LDS into MFMA operand order and runs one 16x16x128 FP8 MFMA against the
-// group's midq columns (one column per using row), scaled by weight scale x
-// mid scale.  At the end of each group the wave files its partial into
+// Block = 4 waves = HW sub-tiles of 16 output rows x KSD parts of K; the
+// block owns 16*HW output rows and walks every expert of the step (shared
+// first, then the routed groups in table order).  For each 128-wide K block of
+// its part a wave loads its 16 weight rows row-contiguously, re-lays them
+// through LDS into MFMA operand order and runs one 16x16x128 FP8 MFMA against
+// the group's midq columns (one column per using row), scaled by weight scale
+// x mid scale.  At the end of each group the wave files its partial into
 // part[K part][row][pick][h] (pick 8 = shared expert): every (row, pick) has
 // exactly one group, so no two writes collide.  Finally the block combines
 //   out[r][h] = bf16( sum_{j<8} g_rj * y_rj[h] + y_r8[h] ),
@@ -82,24 +82,28 @@ __global__ __launch_bounds__(256) void moe_down_kernel(Weights w, Ws ws, Dims d,
   const int col = lane & 15;
   const int nitems = ng * nkw;  // (group, K block) pairs of this wave
   uint8_t* tile = s_tile[wv];
+  // lane l loads rows h0 + l/8 and h0 + 8 + l/8, 16-byte chunk l%8
   const size_t wrow = (size_t)(h0 + (lane >> 3)) * I + (lane & 7) * 16;
   const size_t r8 = (size_t)8 * I;
   const int hblk = h0 / 128;
 
   DnStage st[P];
   // Item i = K block (kp*nkw + i%nkw) of group i/nkw.  Items past the end
-  // reload the last one (in bounds, weight 0) so the ring has no branches.
+  // read the workspace's zero pad (cache-resident) for weights and the last
+  // item's mid (weight 0), so the ring has no branches and no extra HBM reads.
   auto issue = [&](DnStage& s, int i) {
-    i = i < nitems ? i : nitems - 1;
+    const bool pad = i >= nitems;
+    i = pad ? nitems - 1 : i;
     const int gi = i / nkw, kb = kp * nkw + (i - gi * nkw);
     const int e = s_expert[gi];
-    const int slot = gi + 1 - has_sh;
     const uint8_t* wb = e < 0 ? w.sd_c : w.down_c + (size_t)e * H * I;
     const float* sb = e < 0 ? w.sd_s
                             : reinterpret_cast<const float*>(w.down_s) + (size_t)e * (H / 128) * nkb;
-    const size_t mrow = (size_t)slot * d.max_rows + s_row[gi][col];
-    s.w0 = ld_nt16(wb + wrow + (size_t)kb * 128);
-    s.w1 = ld_nt16(wb + wrow + r8 + (size_t)kb * 128);
+    const size_t mrow = (size_t)s_row[gi][col] * 9 + s_pick[gi][col];  // (row, pick)
+    const uint8_t* p0 = pad ? ws.pad + lane * 16 : wb + wrow + (size_t)kb * 128;
+    const uint8_t* p1 = pad ? p0 + 1024 : p0 + r8;
+    s.w0 = ld_nt16(p0);
+    s.w1 = ld_nt16(p1);
     s.m0 = ld16(ws.midq + mrow * d.imax + kb * 128 + (lane >> 4) * 32);
     s.m1 = ld16(ws.midq + mrow * d.imax + kb * 128 + (lane >> 4) * 32 + 16);
     s.sm = ws.midqs[mrow * (d.imax / 128) + kb];

@@ -1,0 +1,210 @@
+// route.h -- the routing decisions of a step, computed inside one block from
+// the final router logits: top-8 per row, the softmax gates and the expert
+// dedup table, published to the workspace for the kernels that follow.
+//
+// #85 Mod. row 9: a row's picks are its 8 largest logits in decreasing order,
+// exact ties going to the lower expert ID.  Mod. rows 16 and 20: the distinct
+// experts of the step are numbered by first use in slot-major order (slot j of
+// every row before slot j + 1), the owner of a group being that first use.
+//
+// Top-8 by radix select: with lane l holding experts l, l + 64, ... as order
+// keys, the 8th largest key T is built bit by bit from the top, keeping a bit
+// when at least 8 keys are >= the candidate (one ballot per key slot); it
+// stops early once exactly 8 keys reach the candidate.  The picks are the keys
+// above T plus, when several keys equal T, the lowest IDs among them; their
+// order comes from ranking the 8 against each other.
+#pragma once
+#include "device_common.h"
+
+namespace moe {
+
+// Order key of a logit: unsigned compare = float order, -0 == +0, NaN (1)
+// below every number (-inf maps to 0x007FFFFF), 0 = no expert.
+__device__ __forceinline__ uint32_t topk_vkey(float z) {
+  if (z != z) return 1u;
+  const uint32_t b = (z == 0.0f) ? 0u : __float_as_uint(z);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+// The logit back from its key (-0 comes back as +0, NaN as a NaN).
+__device__ __forceinline__ float topk_vkey_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+struct RouteSmem {
+  uint32_t ckey[kMaxRows][8];  // a row's 8 picks, unordered
+  int cid[kMaxRows][8];
+  int ids[kMaxRows][8];        // picks in top-8 order
+  float zsel[kMaxRows][8];
+  int g_expert[64];
+  uint32_t g_mask[64];
+  uint8_t g_slot[64][8];
+  uint8_t g_owner[64][2];
+  uint8_t g_rows[64][8];
+  uint8_t g_nrows[64];
+  int n_groups;
+};
+
+// Runs with every thread of the block (it contains block barriers).  Fills
+// `rs` for rows 0..d.rows-1; when `publish`, also writes ids, gates and the
+// group table to the workspace.  KPL = key slots per lane, ceil(E / 64).
+template <int KPL>
+__device__ __forceinline__ void route_block(const Ws& ws, const Dims& d, RouteSmem& rs,
+                                            bool publish) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
+  const int R = d.rows, E = d.E;
+
+  for (int r = wv; r < R; r += nw) {
+    const float* z = ws.logits + (size_t)r * E;
+    float zv[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; i++) {
+      const int e = lane + kWave * i;
+      zv[i] = z[e < E ? e : E - 1];  // lanes past E load in bounds, key 0 below
+    }
+    uint32_t key[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; i++) key[i] = (lane + kWave * i < E) ? topk_vkey(zv[i]) : 0u;
+
+    // T: the largest t with at least 8 keys >= t (E >= 16 real keys, all >= 1)
+    uint32_t t = 0;
+    int nge = 0;
+    for (int b = 31; b >= 0; b--) {
+      const uint32_t c = t | (1u << b);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < KPL; i++) cnt += __popcll(__ballot(key[i] >= c));
+      if (cnt >= 8) {
+        t = c;
+        nge = cnt;
+        if (cnt == 8) break;
+      }
+    }
+    // picks: keys above T, then ties at T by increasing expert ID
+    int need = 8;
+    if (nge > 8) {
+      int ngt = 0;
+#pragma unroll
+      for (int i = 0; i < KPL; i++) ngt += __popcll(__ballot(key[i] > t));
+      need = 8 - ngt;
+    }
+    int ties = 0, base = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; i++) {
+      bool take;
+      if (nge == 8) {
+        take = key[i] >= t;
+      } else {
+        const uint64_t tb = __ballot(key[i] == t);
+        take = key[i] > t || (key[i] == t && ties + lanes_below(tb) < need);
+        ties += __popcll(tb);
+      }
+      const uint64_t sb = __ballot(take);
+      if (take) {
+        const int pos = base + lanes_below(sb);
+        rs.ckey[r][pos] = key[i];
+        rs.cid[r][pos] = lane + kWave * i;
+      }
+      base += __popcll(sb);
+    }
+  }
+  if (tid < 64) {
+    rs.g_mask[tid] = 0u;
+#pragma unroll
+    for (int r = 0; r < 8; r++) rs.g_slot[tid][r] = 0xFF;
+  }
+  __syncthreads();
+
+  // order the 8 picks of each row: rank = picks with a larger key, or an equal
+  // key and a lower ID
+  if (tid < 8 * R) {
+    const int r = tid >> 3, j = tid & 7;
+    const uint32_t k = rs.ckey[r][j];
+    const int id = rs.cid[r][j];
+    int rank = 0;
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+      const uint32_t km = rs.ckey[r][m];
+      rank += (km > k || (km == k && rs.cid[r][m] < id)) ? 1 : 0;
+    }
+    rs.ids[r][rank] = id;
+    rs.zsel[r][rank] = topk_vkey_value(k);
+  }
+  __syncthreads();
+
+  // gates: softmax of a row's 8 picked logits, in pick order
+  if (publish && tid < R) {
+    const int r = tid;
+    float mz = rs.zsel[r][0];
+    for (int j = 1; j < 8; j++) mz = fmaxf(mz, rs.zsel[r][j]);
+    float g[8], sum = 0.f;
+    for (int j = 0; j < 8; j++) {
+      g[j] = expf(rs.zsel[r][j] - mz);
+      sum += g[j];
+    }
+    for (int j = 0; j < 8; j++) {
+      ws.gates[r * 8 + j] = g[j] / sum;
+      ws.ids[r * 8 + j] = rs.ids[r][j];
+    }
+  }
+
+  // dedup: lane p holds pick p in slot-major order (p = j*R + r).  Lanes with
+  // the same expert are found with one ballot per ID bit; the lowest of them
+  // owns the group, and a group's index counts the first uses before it.
+  if (wv == 0) {
+    const int P = 8 * R;
+    const bool valid = lane < P;
+    int ep = 0, jp = 0, rp = 0;
+    if (valid) {
+      jp = lane / R;
+      rp = lane - jp * R;
+      ep = rs.ids[rp][jp];
+    }
+    uint64_t same = __ballot(valid);
+    if (d.no_dedup) {
+      same = 1ull << lane;
+    } else {
+#pragma unroll
+      for (int b = 0; b < 10; b++) {  // expert IDs < 1024
+        const uint64_t bb = __ballot(valid && ((ep >> b) & 1));
+        same &= ((ep >> b) & 1) ? bb : ~bb;
+      }
+    }
+    const int owner = valid ? __ffsll((unsigned long long)same) - 1 : lane;
+    const uint64_t first = __ballot(valid && owner == lane);
+    const int gidx = __popcll(first & ((1ull << owner) - 1ull));
+    if (valid) {
+      atomicOr(&rs.g_mask[gidx], 1u << rp);
+      rs.g_slot[gidx][rp] = (uint8_t)jp;
+      if (owner == lane) {
+        rs.g_expert[gidx] = ep;
+        rs.g_owner[gidx][0] = (uint8_t)jp;
+        rs.g_owner[gidx][1] = (uint8_t)rp;
+      }
+    }
+    if (lane == 0) rs.n_groups = __popcll(first);
+  }
+  __syncthreads();
+  const int D = rs.n_groups;
+  if (tid < D) {
+    const uint32_t m = rs.g_mask[tid];
+    int n = 0;
+    for (int r = 0; r < 8; r++)
+      if ((m >> r) & 1u) rs.g_rows[tid][n++] = (uint8_t)r;
+    rs.g_nrows[tid] = (uint8_t)n;
+    if (publish) {
+      ws.grp_expert[tid] = rs.g_expert[tid];
+      ws.grp_owner[2 * tid] = rs.g_owner[tid][0];
+      ws.grp_owner[2 * tid + 1] = rs.g_owner[tid][1];
+      ws.grp_mask[tid] = (uint8_t)m;
+      for (int r = 0; r < 8; r++) {
+        ws.grp_slot[tid * 8 + r] = rs.g_slot[tid][r];
+        ws.grp_rows[tid * 8 + r] = r < n ? rs.g_rows[tid][r] : (uint8_t)0;
+      }
+      ws.grp_nrows[tid] = (uint8_t)n;
+    }
+  }
+  if (publish && tid == 0) *ws.n_groups = D;
+  __syncthreads();
+}
+
+}  // namespace moe

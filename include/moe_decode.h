@@ -116,7 +116,9 @@ size_t moe_decode_workspace_size(const moe_decode_config* cfg);
 
 /* Validate cfg, bind the caller's workspace (device, >= the size above) and
  * create a context.  Enqueues one small kernel on `stream` that clears the
- * workspace's counters; later steps on the same stream are ordered after it.
+ * workspace (so debug views read before the first step are defined); later
+ * steps on the same stream are ordered after it.  The workspace must be
+ * 256-byte aligned.
  * Returns MOE_ERR_UNSUPPORTED for configs the kernels do not implement,
  * MOE_ERR_WORKSPACE for a missing or short workspace. */
 moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t ws_bytes,
@@ -148,11 +150,12 @@ typedef struct {
   const uint8_t* grp_slot;   /* [max_groups, 8] slot where row r picked it, 0xFF if none */
   const uint8_t* act_q;      /* [max_rows, H] FP8 activation codes */
   const float* act_s;        /* [max_rows, H/128] their block scales */
-  /* mid, per expert slot s = 0 (shared expert) or 1 + g (routed group g),
-   * per row, with row stride mid_stride elements: */
-  const float* mid;          /* [1 + max_groups, max_rows, mid_stride] fp32, before quantisation */
-  const uint8_t* midq;       /* [1 + max_groups, max_rows, mid_stride] FP8 codes */
-  const float* midqs;        /* [1 + max_groups, max_rows, mid_stride/128] block scales */
+  /* mid, per (row r, pick j) with j = 8 for the shared expert, at index
+   * r * 9 + j, with stride mid_stride elements (a deduplicated expert's mid
+   * appears under every (row, pick) that uses it): */
+  const float* mid;          /* [max_rows, 9, mid_stride] fp32, before quantisation */
+  const uint8_t* midq;       /* [max_rows, 9, mid_stride] FP8 codes */
+  const float* midqs;        /* [max_rows, 9, mid_stride/128] block scales */
   int32_t max_groups;        /* min(8 * max_rows, E), or 8 * max_rows with MOE_F_NO_DEDUP */
   int32_t mid_stride;        /* max(I, Is) */
 } moe_decode_debug;
@@ -163,7 +166,7 @@ moe_status moe_decode_debug_view(const moe_decode_ctx* ctx, moe_decode_debug* vi
  * records events[0] before its first kernel and events[i+1] after kernel i
  * (MOE_DECODE_N_KERNELS kernels), on the step's stream.  The caller owns the
  * events (hipEventCreate) and must keep them alive; pass NULL to stop. */
-#define MOE_DECODE_N_KERNELS 4 /* router, up/gate, mid quantiser, down + combine */
+#define MOE_DECODE_N_KERNELS 5 /* router, routing, up/gate, mid, down + combine */
 moe_status moe_decode_set_timing(moe_decode_ctx* ctx, hipEvent_t* events);
 
 void moe_decode_destroy(moe_decode_ctx* ctx);

@@ -67,8 +67,9 @@ def mid_tau(gate, up, gate_abs, up_abs, nkb):
     """Bound on |mid_gpu - mid_exact| from the kernel's arithmetic: each gate /
     up output is one 128-term FP8 MFMA per K block (products exact, sum
     bounded as fp32 with truncation, 128 * 2^-23 * sum|terms|), nkb block
-    partials scaled and accumulated in fp32, two K parts added and two scale
-    products and the rstd product rounded: (nkb + 6) * 2^-24 * sum|terms|.
+    partials scaled and summed in fp32 (within K parts, then the parts in
+    order: nkb - 1 additions in all) and two scale products and the rstd
+    product rounded: (nkb + 6) * 2^-24 * sum|terms|.
     mid = g sigma(g) u then carries |d mid/dg| dg + |d mid/du| du plus eight
     fp32 roundings of the SiLU evaluation."""
     eps = 128 * 2.0 ** -23 + (nkb + 6) * U32
@@ -139,7 +140,7 @@ def compare(layer, x, gpu, out_gpu, ref_out, ref, check_mid_codes=True):
             users = [(r, int(t["slot"][g][r])) for r in range(R) if t["slot"][g][r] != 0xFF]
             width, fp8 = layer.inter, layer.routed_fmt == O.FMT_FP8
         for r, j in users:
-            mg = gpu["mid"][slot, r, :width].astype(np.float64)
+            mg = gpu["mid"][r, j, :width].astype(np.float64)
             mo = ref["mid"][r, j, :width]
             tau = mid_tau(ref["gate"][r, j, :width], ref["up"][r, j, :width],
                           ref["gate_abs"][r, j, :width], ref["up_abs"][r, j, :width], nkb)
@@ -149,8 +150,8 @@ def compare(layer, x, gpu, out_gpu, ref_out, ref, check_mid_codes=True):
                                         float((dev / tau).max()))
             if not fp8 or not check_mid_codes:
                 continue
-            qg = gpu["midq"][slot, r, :width]
-            sg = gpu["midqs"][slot, r, :width // 128]
+            qg = gpu["midq"][r, j, :width]
+            sg = gpu["midqs"][r, j, :width // 128]
             # (i) anchored: the oracle's quantiser on the GPU's fp32 mid, bit-exact
             q, s = O.quant_blocks(mg.astype(np.float32))
             assert np.array_equal(sg, s), ("midqs anchored", slot, r)
