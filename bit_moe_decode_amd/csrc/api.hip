@@ -14,8 +14,9 @@ hipError_t launch_route(const Ws& ws, const Dims& d, hipStream_t stream);
 hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& ws,
                          const Dims& d, hipStream_t stream);
 hipError_t launch_midq(int rfmt, const Ws& ws, const Dims& d, hipStream_t stream);
-hipError_t launch_down(int rfmt, const Weights& w, const Ws& ws, const Dims& d, uint16_t* out,
+hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws, const Dims& d,
                        hipStream_t stream);
+hipError_t launch_combine(const Ws& ws, const Dims& d, uint16_t* out, hipStream_t stream);
 int upgate_k_parts(int hidden, int inter);
 hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
                             hipStream_t stream);
@@ -39,7 +40,7 @@ struct Plan {
   int H, I, E, Is, R, imax, groups, ks;
   size_t off_logits, off_rstd, off_ids, off_gates, off_ngroups, off_gexpert,
       off_gowner, off_gmask, off_gslot, off_grows, off_gnrows, off_actq, off_acts, off_gpart,
-      off_upart, off_mid, off_midq, off_midqs, off_pad, total;
+      off_upart, off_mid, off_midq, off_midqs, off_ypart, total;
 };
 
 bool is_mult(int v, int m) { return v > 0 && v % m == 0; }
@@ -94,7 +95,7 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   p->off_mid = take(U * IM * 4);
   p->off_midq = take(U * IM);
   p->off_midqs = take(U * (IM / 128) * 4);
-  p->off_pad = take(2048);  // zero from init on, never written
+  p->off_ypart = take(U * H * 4);
   p->total = o;
   return MOE_OK;
 }
@@ -155,7 +156,7 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
   v.mid = reinterpret_cast<float*>(b + p.off_mid);
   v.midq = reinterpret_cast<uint8_t*>(b + p.off_midq);
   v.midqs = reinterpret_cast<float*>(b + p.off_midqs);
-  v.pad = reinterpret_cast<const uint8_t*>(b + p.off_pad);
+  v.ypart = reinterpret_cast<float*>(b + p.off_ypart);
   // clear the whole workspace once, so that debug views read before the
   // first step are well defined
   const size_t words = p.total / 4;
@@ -233,9 +234,11 @@ moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
   if (launch_midq(ctx->cfg.routed_fmt, ctx->view, d, stream) != hipSuccess)
     return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (launch_down(ctx->cfg.routed_fmt, wt, ctx->view, d, out, stream) != hipSuccess)
+  if (launch_down(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream) != hipSuccess)
     return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[5], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (launch_combine(ctx->view, d, out, stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[6], stream) != hipSuccess) return MOE_ERR_DEVICE;
   return MOE_OK;
 }
 

@@ -38,7 +38,7 @@ struct Ws {
   float* mid;             // [max_rows * 9][imax]
   uint8_t* midq;          // [max_rows * 9][imax]
   float* midqs;           // [max_rows * 9][imax/128]
-  const uint8_t* pad;     // [2048] zero bytes, read in place of weights past a ring's end
+  float* ypart;           // [max_rows * 9][H] down output per (row, pick)
 };
 
 // Shapes of the step (all multiples as validated on the host).

@@ -1,6 +1,5 @@
 // down.hip -- down GEMV of the shared expert and of every distinct routed
-// expert from the FP8 mid, and the gate-weighted combine, in one launch with
-// no cross-block synchronisation.
+// expert from the FP8 mid, per (row, pick); then the gate-weighted combine.
 //
 // #85 Mod. row 16: down units take one expert's tile against every row that
 // uses it; a row's output is summed over its units in the one-row form's
@@ -8,18 +7,20 @@
 // FP8 bytes and scales quantised once.  Mod. rows 18 and 21: 16-byte,
 // nontemporal weight loads.
 //
-// Block = 4 waves = HW sub-tiles of 16 output rows x KSD parts of K; the
-// block owns 16*HW output rows and walks every expert of the step (shared
-// first, then the routed groups in table order).  For each 128-wide K block of
-// its part a wave loads its 16 weight rows row-contiguously, re-lays them
-// through LDS into MFMA operand order and runs one 16x16x128 FP8 MFMA against
-// the group's midq columns (one column per using row), scaled by weight scale
-// x mid scale.  At the end of each group the wave files its partial into
-// part[K part][row][pick][h] (pick 8 = shared expert): every (row, pick) has
-// exactly one group, so no two writes collide.  Finally the block combines
-//   out[r][h] = bf16( sum_{j<8} g_rj * y_rj[h] + y_r8[h] ),
-//   y_rj = ((part_0 + part_1) + ...) in part order,
-// the same arithmetic whether or not experts were deduplicated.
+// moe_down_kernel: block = 4 waves = 64 output rows of one expert (the shared
+// expert's H/64 blocks first, then H/64 for each of the step's possible routed
+// groups; blocks of groups past the step's D exit at once).  Many small
+// blocks let the hardware dispatcher even out the load per CU.  A wave owns 16
+// output rows over the whole K: for each 128-wide K block it loads its 16
+// weight rows row-contiguously, re-lays them through LDS into MFMA operand
+// order and runs one 16x16x128 FP8 MFMA against the expert's midq columns (one
+// column per using row), scaled by weight scale x mid scale and accumulated in
+// fp32.  It stores y[row, pick][h]; every (row, pick) belongs to exactly one
+// expert of the step, so no two writes collide.
+//
+// moe_combine_kernel:
+//   out[r][h] = bf16( sum_{j<8} g_rj * y_rj[h] + y_r8[h] )
+// in pick order, the same arithmetic whether or not experts were deduplicated.
 #include "device_common.h"
 
 namespace moe {
@@ -29,162 +30,138 @@ struct DnStage {
   float sd, sm;
 };
 
-constexpr int kGroupsMax = 65;  // 64 routed groups + the shared expert
-
-template <int KSD, int P>
-__global__ __launch_bounds__(256) void moe_down_kernel(Weights w, Ws ws, Dims d,
-                                                       uint16_t* __restrict__ out) {
-  constexpr int HW = 4 / KSD;   // 16-row output sub-tiles per block
-  constexpr int BH = 16 * HW;   // output rows per block
+template <int P>
+__global__ __launch_bounds__(256) void moe_down_kernel(Weights w, Ws ws, Dims d) {
   __shared__ uint8_t s_tile[4][kTileBytes];
-  __shared__ float s_part[KSD][kMaxRows][9][BH];
-  __shared__ int s_expert[kGroupsMax];
-  __shared__ uint8_t s_nrows[kGroupsMax];
-  __shared__ uint8_t s_row[kGroupsMax][16];
-  __shared__ uint8_t s_pick[kGroupsMax][16];
-
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int hs = wv % HW, kp = wv / HW;
-  const int H = d.H, I = d.I, nkb = I / 128, nkw = nkb / KSD;
-  const int hb = blockIdx.x * BH, h0 = hb + hs * 16;
-  const int has_sh = d.Is > 0;
-  const int ng = *ws.n_groups + has_sh;
-
-  // ---- the step's groups: index 0 is the shared expert when there is one.
-  // One round of independent loads copies the routed table into LDS ...
-  __shared__ uint64_t s_grows[kGroupsMax], s_gslot[kGroupsMax];
-  const int D = ng - has_sh;
-  if (tid < D) {
-    s_expert[tid + has_sh] = ws.grp_expert[tid];
-    s_nrows[tid + has_sh] = ws.grp_nrows[tid];
-    s_grows[tid] = reinterpret_cast<const uint64_t*>(ws.grp_rows)[tid];
-    s_gslot[tid] = reinterpret_cast<const uint64_t*>(ws.grp_slot)[tid];
-  }
-  if (has_sh && tid == 0) {
-    s_expert[0] = -1;
-    s_nrows[0] = (uint8_t)d.rows;
-  }
-  __syncthreads();
-  // ... and the per-column rows and picks are derived there
-  for (int idx = tid; idx < ng * 16; idx += 256) {
-    const int gi = idx >> 4, c = idx & 15, g = gi - has_sh;
-    const int nr = s_nrows[gi];
-    int r = 0, pk = 0;
-    if (c < nr) {
-      r = g < 0 ? c : (int)((s_grows[g] >> (8 * c)) & 0xFF);
-      pk = g < 0 ? 8 : (int)((s_gslot[g] >> (8 * r)) & 0xFF);
-    }
-    s_row[gi][c] = (uint8_t)r;
-    s_pick[gi][c] = (uint8_t)pk;
-  }
-  __syncthreads();
-
+  const int H = d.H, I = d.I, nkb = I / 128;
   const int col = lane & 15;
-  const int nitems = ng * nkw;  // (group, K block) pairs of this wave
-  uint8_t* tile = s_tile[wv];
-  // lane l loads rows h0 + l/8 and h0 + 8 + l/8, 16-byte chunk l%8
-  const size_t wrow = (size_t)(h0 + (lane >> 3)) * I + (lane & 7) * 16;
-  const size_t r8 = (size_t)8 * I;
-  const int hblk = h0 / 128;
 
-  DnStage st[P];
-  // Item i = K block (kp*nkw + i%nkw) of group i/nkw.  Items past the end
-  // read the workspace's zero pad (cache-resident) for weights and the last
-  // item's mid (weight 0), so the ring has no branches and no extra HBM reads.
-  auto issue = [&](DnStage& s, int i) {
-    const bool pad = i >= nitems;
-    i = pad ? nitems - 1 : i;
-    const int gi = i / nkw, kb = kp * nkw + (i - gi * nkw);
-    const int e = s_expert[gi];
-    const uint8_t* wb = e < 0 ? w.sd_c : w.down_c + (size_t)e * H * I;
-    const float* sb = e < 0 ? w.sd_s
-                            : reinterpret_cast<const float*>(w.down_s) + (size_t)e * (H / 128) * nkb;
-    const size_t mrow = (size_t)s_row[gi][col] * 9 + s_pick[gi][col];  // (row, pick)
-    const uint8_t* p0 = pad ? ws.pad + lane * 16 : wb + wrow + (size_t)kb * 128;
-    const uint8_t* p1 = pad ? p0 + 1024 : p0 + r8;
-    s.w0 = ld_nt16(p0);
-    s.w1 = ld_nt16(p1);
-    s.m0 = ld16(ws.midq + mrow * d.imax + kb * 128 + (lane >> 4) * 32);
-    s.m1 = ld16(ws.midq + mrow * d.imax + kb * 128 + (lane >> 4) * 32 + 16);
-    s.sm = ws.midqs[mrow * (d.imax / 128) + kb];
-    s.sd = sb[(size_t)hblk * nkb + kb];
+  // ---- the block's expert and rows
+  const int per = H / 64;
+  const int nb_sh = d.Is > 0 ? per : 0;
+  int b = blockIdx.x, g = -1, nrows, e;
+  uint64_t rows8 = 0, picks8 = 0;
+  if (b < nb_sh) {
+    nrows = d.rows;
+    e = -1;
+  } else {
+    b -= nb_sh;
+    g = b / per;
+    b -= g * per;
+    // one round of independent loads; the table of a group past D is stale
+    // but in bounds, and unused
+    const int D = *ws.n_groups;
+    e = ws.grp_expert[g];
+    nrows = ws.grp_nrows[g];
+    rows8 = *reinterpret_cast<const uint64_t*>(ws.grp_rows + g * 8);
+    picks8 = *reinterpret_cast<const uint64_t*>(ws.grp_slot + g * 8);
+    if (g >= D) return;
+  }
+  const int row = col < nrows ? (g < 0 ? col : (int)((rows8 >> (8 * (col & 7))) & 0xFF)) : 0;
+  const int pick = g < 0 ? 8 : (int)((picks8 >> (8 * row)) & 0xFF);
+  const int u = col < nrows ? row * 9 + pick : 0;  // (row, pick) of this column
+  const int h0 = b * 64 + wv * 16;
+
+  const uint8_t* wb = e < 0 ? w.sd_c : w.down_c + (size_t)e * H * I;
+  const float* sb =
+      e < 0 ? w.sd_s : reinterpret_cast<const float*>(w.down_s) + (size_t)e * (H / 128) * nkb;
+  // lane l loads rows h0 + l/8 and h0 + 8 + l/8, 16-byte chunk l%8
+  const uint8_t* pw = wb + (size_t)(h0 + (lane >> 3)) * I + (lane & 7) * 16;
+  const size_t r8 = (size_t)8 * I;
+  const uint8_t* pm = ws.midq + (size_t)u * d.imax + (lane >> 4) * 32;
+  const float* psd = sb + (size_t)(h0 / 128) * nkb;
+  const float* psm = ws.midqs + (size_t)u * (d.imax / 128);
+  uint8_t* tile = s_tile[wv];
+
+  auto issue = [&](DnStage& s, int k) {
+    const size_t o = (size_t)k * 128;
+    s.w0 = ld_nt16(pw + o);
+    s.w1 = ld_nt16(pw + r8 + o);
+    s.m0 = ld16(pm + o);
+    s.m1 = ld16(pm + o + 16);
+    s.sd = psd[k];
+    s.sm = psm[k];
   };
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  auto consume = [&](DnStage& s, int i) {
+  auto consume = [&](DnStage& s) {
     tile_put(tile, lane, s.w0, s.w1);
     asm volatile("" ::: "memory");
     const v4f c = mfma_fp8(tile_get(tile, lane), cat8(s.m0, s.m1));
     asm volatile("" ::: "memory");
-    const float f = i < nitems ? s.sd * s.sm : 0.f;
+    const float f = s.sd * s.sm;
 #pragma unroll
     for (int v = 0; v < 4; v++) acc[v] = fmaf(c[v], f, acc[v]);
-    if (i < nitems && (i + 1) % nkw == 0) {  // last K block of a group: file it
-      pin4(acc);
-      const int gi = i / nkw;
-      if (col < s_nrows[gi]) {
-        float* dst = &s_part[kp][s_row[gi][col]][s_pick[gi][col]][hs * 16 + 4 * (lane >> 4)];
-#pragma unroll
-        for (int v = 0; v < 4; v++) dst[v] = acc[v];
-      }
-#pragma unroll
-      for (int v = 0; v < 4; v++) acc[v] = 0.f;
-    }
   };
+  // ring of P K blocks (P divides nkb): every issued load is used
+  DnStage st[P];
 #pragma unroll
   for (int p = 0; p < P; p++) issue(st[p], p);
-  for (int i0 = 0; i0 < nitems; i0 += P) {
+  for (int k0 = 0; k0 < nkb - P; k0 += P) {
 #pragma unroll
     for (int p = 0; p < P; p++) {
-      consume(st[p], i0 + p);
-      issue(st[p], i0 + P + p);
+      consume(st[p]);
+      issue(st[p], k0 + P + p);
     }
   }
-  __syncthreads();
-
-  // ---- combine in pick order, K parts in part order
-  for (int idx = tid; idx < d.rows * BH; idx += 256) {
-    const int r = idx / BH, hh = idx - r * BH;
-    float a = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      float y = s_part[0][r][j][hh];
-#pragma unroll
-      for (int q = 1; q < KSD; q++) y += s_part[q][r][j][hh];
-      a = fmaf(ws.gates[r * 8 + j], y, a);
-    }
-    if (has_sh) {
-      float y = s_part[0][r][8][hh];
-#pragma unroll
-      for (int q = 1; q < KSD; q++) y += s_part[q][r][8][hh];
-      a += y;
-    }
-    out[(size_t)r * H + hb + hh] = f32_to_bf16(a);
-  }
+  for (int p = 0; p < P; p++) consume(st[p]);
+  pin4(acc);  // the MFMAs run with every lane, before the divergent store
+  if (col < nrows)
+    *reinterpret_cast<v4f*>(ws.ypart + (size_t)u * H + h0 + 4 * (lane >> 4)) =
+        v4f{acc[0], acc[1], acc[2], acc[3]};
 }
 
-// K parts per block for the down GEMV: the largest of 4, 2, 1 dividing the
-// expert's K blocks.
-int down_k_split(int inter) {
+// out[r][h] for 4 consecutive h per thread.
+__global__ __launch_bounds__(256) void moe_combine_kernel(Ws ws, Dims d,
+                                                          uint16_t* __restrict__ out) {
+  const int r = blockIdx.y, h = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (h >= d.H) return;
+  const size_t H = d.H;
+  v4f y[9];
+#pragma unroll
+  for (int j = 0; j < 9; j++)
+    y[j] = (j < 8 || d.Is > 0) ? *reinterpret_cast<const v4f*>(ws.ypart + (r * 9 + j) * H + h)
+                               : v4f{0.f, 0.f, 0.f, 0.f};
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const float gj = ws.gates[r * 8 + j];
+#pragma unroll
+    for (int v = 0; v < 4; v++) a[v] = fmaf(gj, y[j][v], a[v]);
+  }
+  if (d.Is > 0) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) a[v] += y[8][v];
+  }
+  uint2 pk;
+  pk.x = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
+  pk.y = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
+  *reinterpret_cast<uint2*>(out + (size_t)r * H + h) = pk;
+}
+
+// K blocks in flight per wave: the largest of 8, 4, 2, 1 dividing I/128.
+static int down_ring(int inter) {
   const int nkb = inter / 128;
-  return nkb % 4 == 0 ? 4 : (nkb % 2 == 0 ? 2 : 1);
+  return nkb % 8 == 0 ? 8 : (nkb % 4 == 0 ? 4 : (nkb % 2 == 0 ? 2 : 1));
 }
 
-template <int KSD>
-static void launch_ksd(dim3 grid, const Weights& w, const Ws& ws, const Dims& d, uint16_t* out,
-                       hipStream_t stream) {
-  hipLaunchKernelGGL((moe_down_kernel<KSD, 8>), grid, dim3(256), 0, stream, w, ws, d, out);
-}
-
-hipError_t launch_down(int rfmt, const Weights& w, const Ws& ws, const Dims& d, uint16_t* out,
+hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws, const Dims& d,
                        hipStream_t stream) {
   if (rfmt != kFmtFp8) return hipErrorInvalidValue;
-  const int ksd = down_k_split(d.I);
-  dim3 grid(d.H / (16 * (4 / ksd)));
-  switch (ksd) {
-    case 4: launch_ksd<4>(grid, w, ws, d, out, stream); break;
-    case 2: launch_ksd<2>(grid, w, ws, d, out, stream); break;
-    default: launch_ksd<1>(grid, w, ws, d, out, stream); break;
+  const dim3 grid((d.H / 64) * ((d.Is > 0 ? 1 : 0) + max_groups));
+  switch (down_ring(d.I)) {
+    case 8: hipLaunchKernelGGL((moe_down_kernel<8>), grid, dim3(256), 0, stream, w, ws, d); break;
+    case 4: hipLaunchKernelGGL((moe_down_kernel<4>), grid, dim3(256), 0, stream, w, ws, d); break;
+    case 2: hipLaunchKernelGGL((moe_down_kernel<2>), grid, dim3(256), 0, stream, w, ws, d); break;
+    default: hipLaunchKernelGGL((moe_down_kernel<1>), grid, dim3(256), 0, stream, w, ws, d); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Ws& ws, const Dims& d, uint16_t* out, hipStream_t stream) {
+  const dim3 grid((d.H / 4 + 255) / 256, d.rows);
+  hipLaunchKernelGGL(moe_combine_kernel, grid, dim3(256), 0, stream, ws, d, out);
   return hipGetLastError();
 }
 
