@@ -10,7 +10,7 @@ copies of the layer's weights are rotated step by step so that no step finds
 another step's weights in the 256 MB MALL or the L2s; a pool of 16 token rows
 varies the routing.
 
-One step = one moe_decode_step call (router, up/gate, mid quantiser, down +
+One step = one moe_decode_step call (router, routing, up/gate, mid, down and
 combine kernels).  Value =
 algorithmic bytes of the step (each distinct expert counted once, read from
 the step's own dedup table, plus the shared expert, router, gamma, x and out)
