@@ -124,6 +124,39 @@ def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base):
                 weights=weights, dvals=dvals)
 
 
+LOWBIT_SHAPES = (("mlp_up_gate", 9728, 2560), ("mlp_down", 2560, 9728), ("lm_head", 151936, 2560))
+
+
+def lowbit_bytes(n, k):
+    return n * (k // 128) * 18 + k * 2 + n * 2
+
+
+def time_lowbit(torch, B, S, n, k, steps):
+    """lowbit_gemv at batch 1: back-to-back launches over enough weight copies
+    (>= 512 MB in all) that no launch finds its matrix in the MALL."""
+    size = n * (k // 128) * 18
+    ncopy = max(2, -(-512 * 2 ** 20 // size))
+    base = S.make_q1(n, k, seed=77, device="cuda")
+    mats = [base] + [base.clone() for _ in range(ncopy - 1)]
+    x = S.make_x(1, k, seed=78, device="cuda")[0]
+    y = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    for i in range(10):
+        B.lowbit_gemv(mats[i % ncopy], x, y, n, k)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        B.lowbit_gemv(mats[i % ncopy], x, y, n, k)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / steps
+    gbs = lowbit_bytes(n, k) / (us * 1e-6) / 1e9
+    del mats
+    return dict(n=n, k=k, us=round(us, 2), gbs=round(gbs, 1), frac=round(gbs / PEAK_GBS, 4),
+                bytes=lowbit_bytes(n, k), copies=ncopy)
+
+
 def cpu_baseline(torch, layer, res, seconds):
     from oracle import oracle as O
     from tests import parity as P
@@ -165,6 +198,7 @@ def main():
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-lowbit", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the decode step has no multi-GPU path in this "
@@ -202,6 +236,14 @@ def main():
         r = results[rows]
         log(f"rows={rows}: {r['us_per_step']:.1f} us/step, {r['gbs']:.0f} GB/s "
             f"({100 * r['frac']:.1f}% of peak), D={r['d_mean']:.1f}, kernels {r['kernel_us']}")
+
+    lowbit = None
+    if not args.no_lowbit:
+        lowbit = {}
+        for name, n, k in LOWBIT_SHAPES:
+            log(f"timing lowbit_gemv {name} [{n}, {k}]")
+            lowbit[name] = time_lowbit(torch, B, S, n, k, steps=max(args.steps, 50))
+            log(f"  {lowbit[name]}")
 
     main_rows = 1 if 1 in results else min(results)
     m = results[main_rows]
@@ -243,6 +285,7 @@ def main():
                              "kernel_us": {k: round(t, 2) for k, t in v["kernel_us"].items()},
                              "upgate_gbs": round(v["upgate_gbs"], 1)}
                     for r, v in results.items()},
+        "lowbit_gemv": lowbit,
     }
     print(json.dumps(line), flush=True)
 
