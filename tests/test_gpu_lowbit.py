@@ -82,3 +82,10 @@ def test_lowbit_zero_rows_and_zero_n():
     torch.cuda.synchronize()
     assert (y.float() == 7.0).all()
     assert B.lowbit_gemv_status(blk, x, y, 4, k, rows=2) == B.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("n,k", [(16384, 256), (16385, 768), (20000, 5632)])
+def test_lowbit_table_form_edges(n, k):
+    """The table form's limits: its smallest row count, a ragged last block,
+    and a K where only 64 rows fit the staging area."""
+    _check(n, k, seed=n + k)
