@@ -17,7 +17,7 @@ hipError_t launch_midq(int rfmt, const Ws& ws, const Dims& d, hipStream_t stream
 hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws, const Dims& d,
                        hipStream_t stream);
 hipError_t launch_combine(const Ws& ws, const Dims& d, uint16_t* out, hipStream_t stream);
-int upgate_k_parts(int hidden, int inter);
+int upgate_k_parts(int hidden, int routed_fmt);
 hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
                             hipStream_t stream);
 
@@ -54,7 +54,10 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   if (c->shared_inter != 0 && c->shared_inter != c->inter) return MOE_ERR_UNSUPPORTED;
   if (!is_mult(c->n_experts, 16) || c->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
   if (c->max_rows < 1 || c->max_rows > 8) return MOE_ERR_INVALID_ARG;
-  if (c->routed_fmt != MOE_FMT_FP8_E4M3_B128) return MOE_ERR_UNSUPPORTED;
+  if (c->routed_fmt != MOE_FMT_FP8_E4M3_B128 && c->routed_fmt != MOE_FMT_MXFP4)
+    return MOE_ERR_UNSUPPORTED;
+  // MXFP4 up/gate items are two K blocks wide
+  if (c->routed_fmt == MOE_FMT_MXFP4 && c->hidden % 256) return MOE_ERR_UNSUPPORTED;
   if (c->shared_inter > 0 && c->shared_fmt != MOE_FMT_FP8_E4M3_B128) return MOE_ERR_UNSUPPORTED;
   if (c->flags & ~kKnownFlags) return MOE_ERR_UNSUPPORTED;
   if (!(c->rms_eps >= 0.0f) || c->rms_eps > 1.0f) return MOE_ERR_INVALID_ARG;
@@ -67,7 +70,7 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   p->imax = p->I > p->Is ? p->I : p->Is;
   const int picks = 8 * p->R;
   p->groups = (c->flags & MOE_F_NO_DEDUP) ? picks : (picks < p->E ? picks : p->E);
-  p->ks = upgate_k_parts(p->H, p->I);
+  p->ks = upgate_k_parts(p->H, c->routed_fmt);
 
   size_t o = 0;
   auto take = [&](size_t bytes) {

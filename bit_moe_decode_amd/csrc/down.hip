@@ -18,6 +18,13 @@
 // fp32.  It stores y[row, pick][h]; every (row, pick) belongs to exactly one
 // expert of the step, so no two writes collide.
 //
+// MXFP4 routed experts (mid kept in fp32, as the oracle does): a VALU path in
+// the same blocks, one mid column at a time.  Per K chunk of 512 the block
+// stages the column's fp32 mid in LDS (4 pad floats per 32, so the 4 lanes of
+// a row read disjoint banks); each 16-byte run of weights -- 32 inputs, one
+// E8M0 block -- is decoded with the hardware FP4 -> fp32 conversion scaled by
+// 2^(E8M0-127) and multiplied into an fp32 sum.
+//
 // moe_combine_kernel:
 //   out[r][h] = bf16( sum_{j<8} g_rj * y_rj[h] + y_r8[h] )
 // in pick order, the same arithmetic whether or not experts were deduplicated.
@@ -30,9 +37,94 @@ struct DnStage {
   float sd, sm;
 };
 
-template <int P>
+constexpr int kDnChunk = 512;                  // K inputs per staged mid chunk (MXFP4)
+constexpr int kDnMidStride = kDnChunk + kDnChunk / 8;  // 4 pad floats per 32
+
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+
+// 2^(e-127) as fp32 for an E8M0 code (0xFF, NaN, is not produced by the
+// generator; it decodes to a NaN here as well).
+__device__ __forceinline__ float e8m0_scale(uint32_t e) {
+  uint32_t b = e << 23;
+  b = e == 0 ? 0x00400000u : b;
+  b = e == 255 ? 0x7FC00000u : b;
+  return __uint_as_float(b);
+}
+
+// The MXFP4 down GEMV of one block: 64 output rows of routed expert e against
+// its nrows mid columns u_c (fp32, unquantised), one column at a time.  Lane l
+// takes row hb + 16*wave + l/4 and, of each staged K chunk, the 16-byte runs
+// 16(l%4) + 64i (32 inputs, one E8M0 block each); the 4 lanes of a row are
+// summed at the end.
+__device__ __forceinline__ void down_fp4_block(const Weights& w, const Ws& ws, const Dims& d,
+                                               int e, int nrows, const int* ucol, int hb,
+                                               float* s_mid) {
+  constexpr int R = kDnChunk / 128;  // runs of a lane per chunk
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int H = d.H, I = d.I;
+  const size_t rbytes = I / 2;
+  const int h = hb + wv * 16 + (lane >> 2), q = lane & 3;
+  const uint8_t* wrow = w.down_c + ((size_t)e * H + h) * rbytes;
+  const uint8_t* erow = reinterpret_cast<const uint8_t*>(w.down_s) + ((size_t)e * H + h) * (I / 32);
+#pragma unroll 1
+  for (int c = 0; c < nrows; c++) {
+    const float* mcol = ws.mid + (size_t)ucol[c] * d.imax;
+    float a = 0.f;
+#pragma unroll 1
+    for (int k0 = 0; k0 < I; k0 += kDnChunk) {
+      const int kc = I - k0 < kDnChunk ? I - k0 : kDnChunk;  // a multiple of 128
+      const int nrun = kc / 128;
+      u32x4 wq[R];
+      uint32_t ev[R];
+#pragma unroll
+      for (int i = 0; i < R; i++)
+        if (i < nrun) {
+          const int byte = k0 / 2 + 64 * i + 16 * q;
+          wq[i] = ld_nt16(wrow + byte);
+          ev[i] = erow[byte / 16];
+        }
+      __syncthreads();  // the previous chunk's readers are done
+      for (int f4 = tid; f4 < kc / 4; f4 += 256)
+        *reinterpret_cast<v4f*>(s_mid + 4 * f4 + (f4 / 8) * 4) =
+            *reinterpret_cast<const v4f*>(mcol + k0 + 4 * f4);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < R; i++) {
+        if (i >= nrun) break;
+        const float sc = e8m0_scale(ev[i]);
+        const int kl = 128 * i + 32 * q;  // first input of the run within the chunk
+        const float* mp = s_mid + kl + (kl / 32) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {  // 8 inputs per dword of codes
+          const v2f_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wq[i][j], sc, 0);
+          const v2f_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wq[i][j], sc, 1);
+          const v2f_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wq[i][j], sc, 2);
+          const v2f_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wq[i][j], sc, 3);
+          const v4f m0 = *reinterpret_cast<const v4f*>(mp + 8 * j);
+          const v4f m1 = *reinterpret_cast<const v4f*>(mp + 8 * j + 4);
+          a = fmaf(p0[0], m0[0], a);
+          a = fmaf(p0[1], m0[1], a);
+          a = fmaf(p1[0], m0[2], a);
+          a = fmaf(p1[1], m0[3], a);
+          a = fmaf(p2[0], m1[0], a);
+          a = fmaf(p2[1], m1[1], a);
+          a = fmaf(p3[0], m1[2], a);
+          a = fmaf(p3[1], m1[3], a);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one run decoded at a time
+      }
+    }
+    // sum over the 4 lanes of the row (xor 1, xor 2 within quads)
+    a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xF, 0xF, false));
+    a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF, false));
+    if (q == 0) ws.ypart[(size_t)ucol[c] * H + h] = a;
+  }
+}
+
+template <int RF, int P>
 __global__ __launch_bounds__(256) void moe_down_kernel(Weights w, Ws ws, Dims d) {
   __shared__ uint8_t s_tile[4][kTileBytes];
+  __shared__ float s_mid[RF == kFmtMxfp4 ? kDnMidStride : 1];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = d.H, I = d.I, nkb = I / 128;
   const int col = lane & 15;
@@ -57,6 +149,16 @@ __global__ __launch_bounds__(256) void moe_down_kernel(Weights w, Ws ws, Dims d)
     rows8 = *reinterpret_cast<const uint64_t*>(ws.grp_rows + g * 8);
     picks8 = *reinterpret_cast<const uint64_t*>(ws.grp_slot + g * 8);
     if (g >= D) return;
+  }
+  if (RF == kFmtMxfp4 && g >= 0) {
+    int ucol[kMaxRows];
+#pragma unroll
+    for (int c = 0; c < kMaxRows; c++) {
+      const int r = (int)((rows8 >> (8 * c)) & 0xFF);
+      ucol[c] = c < nrows ? r * 9 + (int)((picks8 >> (8 * r)) & 0xFF) : 0;
+    }
+    down_fp4_block(w, ws, d, e, nrows, ucol, b * 64, s_mid);
+    return;
   }
   const int row = col < nrows ? (g < 0 ? col : (int)((rows8 >> (8 * (col & 7))) & 0xFF)) : 0;
   const int pick = g < 0 ? 8 : (int)((picks8 >> (8 * row)) & 0xFF);
@@ -146,16 +248,26 @@ static int down_ring(int inter) {
   return nkb % 8 == 0 ? 8 : (nkb % 4 == 0 ? 4 : (nkb % 2 == 0 ? 2 : 1));
 }
 
+template <int RF>
+static void launch_rf(dim3 grid, const Weights& w, const Ws& ws, const Dims& d,
+                      hipStream_t stream) {
+  switch (down_ring(d.I)) {
+    case 8: hipLaunchKernelGGL((moe_down_kernel<RF, 8>), grid, dim3(256), 0, stream, w, ws, d); break;
+    case 4: hipLaunchKernelGGL((moe_down_kernel<RF, 4>), grid, dim3(256), 0, stream, w, ws, d); break;
+    case 2: hipLaunchKernelGGL((moe_down_kernel<RF, 2>), grid, dim3(256), 0, stream, w, ws, d); break;
+    default: hipLaunchKernelGGL((moe_down_kernel<RF, 1>), grid, dim3(256), 0, stream, w, ws, d); break;
+  }
+}
+
 hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws, const Dims& d,
                        hipStream_t stream) {
-  if (rfmt != kFmtFp8) return hipErrorInvalidValue;
   const dim3 grid((d.H / 64) * ((d.Is > 0 ? 1 : 0) + max_groups));
-  switch (down_ring(d.I)) {
-    case 8: hipLaunchKernelGGL((moe_down_kernel<8>), grid, dim3(256), 0, stream, w, ws, d); break;
-    case 4: hipLaunchKernelGGL((moe_down_kernel<4>), grid, dim3(256), 0, stream, w, ws, d); break;
-    case 2: hipLaunchKernelGGL((moe_down_kernel<2>), grid, dim3(256), 0, stream, w, ws, d); break;
-    default: hipLaunchKernelGGL((moe_down_kernel<1>), grid, dim3(256), 0, stream, w, ws, d); break;
-  }
+  if (rfmt == kFmtFp8)
+    launch_rf<kFmtFp8>(grid, w, ws, d, stream);
+  else if (rfmt == kFmtMxfp4)
+    launch_rf<kFmtMxfp4>(grid, w, ws, d, stream);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

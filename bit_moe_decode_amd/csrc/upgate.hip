@@ -6,79 +6,91 @@
 // distinct expert, with every row that uses the expert as an MFMA column, so
 // an expert's weights stream once however many rows picked it.  Mod. rows 18
 // and 21: weights load 16 bytes a lane and, being read once, nontemporal.
+// Mod. row 1 and the MXFP4 page: routed experts may instead hold MXFP4
+// weights (E2M1 pairs, one E8M0 exponent per 32 inputs); the shared expert
+// stays FP8.
 //
 // Block = 4 waves = 4/ks slabs of 16 intermediate rows x ks parts of K; the
 // grid lists the shared expert's slabs, then I/16 slabs for each of the step's
 // possible routed groups (blocks of groups past the step's D exit at once).
 // Many small blocks let the hardware dispatcher even out the load per CU.
-// Per K block a wave loads its 16 weight rows of gate and of up
-// row-contiguously (8 lanes read one row's 128-byte line), re-lays them through
-// LDS into MFMA operand order and runs one 16x16x128 FP8 MFMA for each, whose
-// 16 columns are the expert's using rows; the result is scaled by weight scale
-// x activation scale and accumulated in fp32.  The wave then stores its K-part
+// A wave loads its 16 weight rows of gate and of up row-contiguously (8 lanes
+// read one row's 128-byte line), re-lays them through LDS into MFMA operand
+// order and runs 16x16x128 MFMAs whose 16 columns are the expert's using rows;
+// the fp32 results are scaled and accumulated.  The wave then stores its K-part
 // sums per (row, pick).  No block waits for another, and no wave for another.
+//
+//  FP8 item = one 128-wide K block: one FP8 x FP8 MFMA per matrix, scaled by
+//    weight block scale x activation block scale.
+//  MXFP4 item = two 128-wide K blocks (a 128-byte line per row): per K block
+//    one scaled FP4 x FP8 MFMA per matrix, the E8M0 exponents entering as the
+//    MFMA's A scales, then the activation block scale.  Operand layout of that
+//    MFMA on gfx950 (established by a device probe): A lane l holds row l%16
+//    and the 32 inputs 32*(l/16) .. +32 of the K block as 16 bytes, low nibble
+//    first, with the E8M0 of those 32 as its scale; B lane l holds column l%16
+//    and the FP8 inputs 16*(l/16) .. +16 and 64 + 16*(l/16) .. +16.
 #include "device_common.h"
 
 namespace moe {
 
-// One K block of one wave: gate and up weight rows (row-contiguous), the
-// using rows' activation codes in operand order and the three scales.  Every
-// lane loads (columns past the expert's rows read row 0; their results are
-// never stored), so the ring carries no per-lane condition.
+// One K item of one wave: gate and up weight rows (row-contiguous), the using
+// rows' activation codes in operand order and the scales.  Every lane loads
+// (columns past the expert's rows read row 0; their results are never
+// stored), so the ring carries no per-lane condition.
 struct UgStage {
   u32x4 g0, g1, u0, u1, a0, a1;
   float sg, su, sa;
 };
+struct UgStage4 {
+  u32x4 g0, g1, u0, u1, a0, a1, a2, a3;  // a0,a1: K block 0; a2,a3: K block 1
+  uint32_t eg0, eg1, eu0, eu1;           // E8M0 of the lane's row, K blocks 0 and 1
+  float sa0, sa1;
+};
 
+// Operand of the scaled MFMA for FP4 A: 16 bytes in the low half.
+__device__ __forceinline__ v8i fp4_operand(const u32x4& v) {
+  v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
+  r[0] = v[0];
+  r[1] = v[1];
+  r[2] = v[2];
+  r[3] = v[3];
+  return r;
+}
+// Row l%16, bytes 64h + 16(l/16) .. +16 of the tile (K block h of the item).
+__device__ __forceinline__ u32x4 tile_get_fp4(const uint8_t* tile, int lane, int h) {
+  return *reinterpret_cast<const u32x4*>(tile + (lane & 15) * kTileStride + 64 * h +
+                                         (lane >> 4) * 16);
+}
+__device__ __forceinline__ v4f mfma_fp4_fp8(const v8i& a, const v8i& b, int scale_a) {
+  v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 4, 0, 0, scale_a, 0, 127);
+}
+
+struct UgJob {
+  int e, row, n0;  // expert (-1: shared), activation row of the lane's column, first row
+};
+
+// FP8 weights: K blocks kb0 .. kb0 + nk of the slab.
 template <int P>
-__global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims d) {
-  __shared__ uint8_t s_tile[4][2][kTileBytes];  // per wave: gate and up weight tiles
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int H = d.H, nkbh = H / 128, KS = d.ks, nk = nkbh / KS;
-  const int spb = 4 / KS;  // slabs per block
-  const int col = lane & 15;
-
-  // ---- the block's expert and slab
-  const int nb_sh = d.Is / (16 * spb);
-  int b = blockIdx.x, g = -1, nrows, row, e;
-  uint64_t picks8 = 0;  // pick of each row in the group (routed)
-  if (b < nb_sh) {
-    nrows = d.rows;
-    row = col < nrows ? col : 0;
-    e = -1;
-  } else {
-    b -= nb_sh;
-    const int per = d.I / (16 * spb);
-    g = b / per;
-    b -= g * per;
-    // one round of independent loads; the table of a group past D is stale
-    // but in bounds, and unused
-    const int D = *ws.n_groups;
-    e = ws.grp_expert[g];
-    nrows = ws.grp_nrows[g];
-    const uint64_t rows8 = *reinterpret_cast<const uint64_t*>(ws.grp_rows + g * 8);
-    picks8 = *reinterpret_cast<const uint64_t*>(ws.grp_slot + g * 8);
-    if (g >= D) return;
-    row = col < nrows ? (int)((rows8 >> (8 * (col & 7))) & 0xFF) : 0;
-  }
-  const int slab = b * spb + wv / KS, kp = wv % KS;
-  const int n0 = slab * 16, kb0 = kp * nk;
+__device__ __forceinline__ void ug_fp8(const Weights& w, const Ws& ws, const Dims& d, UgJob j,
+                                       int kb0, int nk, uint8_t* tg, uint8_t* tu, int lane,
+                                       float* accg, float* accu) {
+  const int H = d.H, nkbh = H / 128;
   const size_t ebytes = (size_t)d.I * H;
   const size_t escl = (size_t)(d.I / 128) * nkbh;  // scales per routed expert
-  const uint8_t* bg = e < 0 ? w.sg_c : w.gate_c + (size_t)e * ebytes;
-  const uint8_t* bu = e < 0 ? w.su_c : w.up_c + (size_t)e * ebytes;
-  const float* sg = e < 0 ? w.sg_s : reinterpret_cast<const float*>(w.gate_s) + (size_t)e * escl;
-  const float* su = e < 0 ? w.su_s : reinterpret_cast<const float*>(w.up_s) + (size_t)e * escl;
+  const uint8_t* bg = j.e < 0 ? w.sg_c : w.gate_c + (size_t)j.e * ebytes;
+  const uint8_t* bu = j.e < 0 ? w.su_c : w.up_c + (size_t)j.e * ebytes;
+  const float* sg =
+      j.e < 0 ? w.sg_s : reinterpret_cast<const float*>(w.gate_s) + (size_t)j.e * escl;
+  const float* su = j.e < 0 ? w.su_s : reinterpret_cast<const float*>(w.up_s) + (size_t)j.e * escl;
   // lane l loads rows n0 + l/8 and n0 + 8 + l/8, 16-byte chunk l%8
-  const uint8_t* pg = bg + (size_t)(n0 + (lane >> 3)) * H + (lane & 7) * 16 + (size_t)kb0 * 128;
+  const uint8_t* pg = bg + (size_t)(j.n0 + (lane >> 3)) * H + (lane & 7) * 16 + (size_t)kb0 * 128;
   const uint8_t* pu = bu + (pg - bg);
   const size_t r8 = (size_t)8 * H;
-  const uint8_t* pa = ws.act_q + (size_t)row * H + (lane >> 4) * 32 + (size_t)kb0 * 128;
-  const float* psg = sg + (size_t)(n0 / 128) * nkbh + kb0;
-  const float* psu = su + (size_t)(n0 / 128) * nkbh + kb0;
-  const float* psa = ws.act_s + (size_t)row * nkbh + kb0;
-  uint8_t* tg = s_tile[wv][0];
-  uint8_t* tu = s_tile[wv][1];
+  const uint8_t* pa = ws.act_q + (size_t)j.row * H + (lane >> 4) * 32 + (size_t)kb0 * 128;
+  const float* psg = sg + (size_t)(j.n0 / 128) * nkbh + kb0;
+  const float* psu = su + (size_t)(j.n0 / 128) * nkbh + kb0;
+  const float* psa = ws.act_s + (size_t)j.row * nkbh + kb0;
 
   auto issue = [&](UgStage& st, int k) {
     const size_t o = (size_t)k * 128;
@@ -92,7 +104,6 @@ __global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims 
     st.su = psu[k];
     st.sa = psa[k];
   };
-  float accg[4] = {0.f, 0.f, 0.f, 0.f}, accu[4] = {0.f, 0.f, 0.f, 0.f};
   auto consume = [&](UgStage& st) {
     tile_put(tg, lane, st.g0, st.g1);
     tile_put(tu, lane, st.u0, st.u1);
@@ -121,36 +132,175 @@ __global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims 
   }
 #pragma unroll
   for (int p = 0; p < P; p++) consume(st[p]);
+}
+
+// MXFP4 weights: items (pairs of K blocks) it0 .. it0 + ni of the slab.
+template <int P>
+__device__ __forceinline__ void ug_fp4(const Weights& w, const Ws& ws, const Dims& d, UgJob j,
+                                       int it0, int ni, uint8_t* tg, uint8_t* tu, int lane,
+                                       float* accg, float* accu) {
+  const int H = d.H, nkbh = H / 128;
+  const size_t rbytes = H / 2;  // one row of codes
+  const size_t ebytes = (size_t)d.I * rbytes, escl = (size_t)d.I * (H / 32);
+  const uint8_t* bg = w.gate_c + (size_t)j.e * ebytes;
+  const uint8_t* bu = w.up_c + (size_t)j.e * ebytes;
+  const uint8_t* eg = reinterpret_cast<const uint8_t*>(w.gate_s) + (size_t)j.e * escl;
+  const uint8_t* eu = reinterpret_cast<const uint8_t*>(w.up_s) + (size_t)j.e * escl;
+  // lane l loads rows n0 + l/8 and n0 + 8 + l/8, 16-byte chunk l%8 of the
+  // item's 128 bytes, and the E8M0 of its MFMA row n0 + l%16 (4 per K block)
+  const uint8_t* pg =
+      bg + (size_t)(j.n0 + (lane >> 3)) * rbytes + (lane & 7) * 16 + (size_t)it0 * 128;
+  const uint8_t* pu = bu + (pg - bg);
+  const size_t r8 = 8 * rbytes;
+  const uint8_t* peg = eg + (size_t)(j.n0 + (lane & 15)) * (H / 32) + (size_t)it0 * 8;
+  const uint8_t* peu = eu + (peg - eg);
+  // activation of K block 2i + h: bytes 16(l/16) .. +16 and 64 + 16(l/16) .. +16
+  const uint8_t* pa = ws.act_q + (size_t)j.row * H + (lane >> 4) * 16 + (size_t)it0 * 256;
+  const float* psa = ws.act_s + (size_t)j.row * nkbh + 2 * it0;
+  const int sh = 8 * (lane >> 4);  // the lane's byte of each E8M0 word
+
+  auto issue = [&](UgStage4& st, int k) {
+    const size_t o = (size_t)k * 128;
+    st.g0 = ld_nt16(pg + o);
+    st.g1 = ld_nt16(pg + r8 + o);
+    st.u0 = ld_nt16(pu + o);
+    st.u1 = ld_nt16(pu + r8 + o);
+    const size_t oa = (size_t)k * 256;
+    st.a0 = ld16(pa + oa);
+    st.a1 = ld16(pa + oa + 64);
+    st.a2 = ld16(pa + oa + 128);
+    st.a3 = ld16(pa + oa + 192);
+    st.eg0 = *reinterpret_cast<const uint32_t*>(peg + 8 * k);
+    st.eg1 = *reinterpret_cast<const uint32_t*>(peg + 8 * k + 4);
+    st.eu0 = *reinterpret_cast<const uint32_t*>(peu + 8 * k);
+    st.eu1 = *reinterpret_cast<const uint32_t*>(peu + 8 * k + 4);
+    st.sa0 = psa[2 * k];
+    st.sa1 = psa[2 * k + 1];
+  };
+  auto consume = [&](UgStage4& st) {
+    tile_put(tg, lane, st.g0, st.g1);
+    tile_put(tu, lane, st.u0, st.u1);
+    asm volatile("" ::: "memory");
+    const v8i b0 = cat8(st.a0, st.a1), b1 = cat8(st.a2, st.a3);
+    const v4f cg0 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tg, lane, 0)), b0, (st.eg0 >> sh) & 0xFF);
+    const v4f cu0 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tu, lane, 0)), b0, (st.eu0 >> sh) & 0xFF);
+    const v4f cg1 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tg, lane, 1)), b1, (st.eg1 >> sh) & 0xFF);
+    const v4f cu1 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tu, lane, 1)), b1, (st.eu1 >> sh) & 0xFF);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      accg[v] = fmaf(cg1[v], st.sa1, fmaf(cg0[v], st.sa0, accg[v]));
+      accu[v] = fmaf(cu1[v], st.sa1, fmaf(cu0[v], st.sa0, accu[v]));
+    }
+  };
+  // ring of P items (P divides ni)
+  UgStage4 st[P];
+#pragma unroll
+  for (int p = 0; p < P; p++) issue(st[p], p);
+  for (int k0 = 0; k0 < ni - P; k0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+      consume(st[p]);
+      issue(st[p], k0 + P + p);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; p++) consume(st[p]);
+}
+
+template <int RF, int P, int P4>
+__global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims d) {
+  __shared__ uint8_t s_tile[4][2][kTileBytes];  // per wave: gate and up weight tiles
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int KS = d.ks;
+  const int spb = 4 / KS;  // slabs per block
+  const int col = lane & 15;
+
+  // ---- the block's expert and slab
+  const int nb_sh = d.Is / (16 * spb);
+  int b = blockIdx.x, g = -1, nrows, row, e;
+  uint64_t picks8 = 0;  // pick of each row in the group (routed)
+  if (b < nb_sh) {
+    nrows = d.rows;
+    row = col < nrows ? col : 0;
+    e = -1;
+  } else {
+    b -= nb_sh;
+    const int per = d.I / (16 * spb);
+    g = b / per;
+    b -= g * per;
+    // one round of independent loads; the table of a group past D is stale
+    // but in bounds, and unused
+    const int D = *ws.n_groups;
+    e = ws.grp_expert[g];
+    nrows = ws.grp_nrows[g];
+    const uint64_t rows8 = *reinterpret_cast<const uint64_t*>(ws.grp_rows + g * 8);
+    picks8 = *reinterpret_cast<const uint64_t*>(ws.grp_slot + g * 8);
+    if (g >= D) return;
+    row = col < nrows ? (int)((rows8 >> (8 * (col & 7))) & 0xFF) : 0;
+  }
+  const int slab = b * spb + wv / KS, kp = wv % KS;
+  const UgJob j{e, row, slab * 16};
+  float accg[4] = {0.f, 0.f, 0.f, 0.f}, accu[4] = {0.f, 0.f, 0.f, 0.f};
+  if (RF == kFmtMxfp4 && e >= 0) {
+    const int ni = d.H / 256 / KS;  // items of two K blocks per part
+    ug_fp4<P4>(w, ws, d, j, kp * ni, ni, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
+  } else {
+    const int nk = d.H / 128 / KS;
+    ug_fp8<P>(w, ws, d, j, kp * nk, nk, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
+  }
   pin4(accg);  // the MFMAs run with every lane, before the divergent store
   pin4(accu);
   if (col < nrows) {
     const int pick = g < 0 ? 8 : (int)((picks8 >> (8 * row)) & 0xFF);
-    const size_t o = ((size_t)(row * 9 + pick) * KS + kp) * d.imax + n0 + 4 * (lane >> 4);
+    const size_t o = ((size_t)(row * 9 + pick) * KS + kp) * d.imax + j.n0 + 4 * (lane >> 4);
     *reinterpret_cast<v4f*>(ws.gpart + o) = v4f{accg[0], accg[1], accg[2], accg[3]};
     *reinterpret_cast<v4f*>(ws.upart + o) = v4f{accu[0], accu[1], accu[2], accu[3]};
   }
 }
 
-// K blocks in flight per wave: the largest of 4, 2, 1 dividing the wave's
-// K blocks.
+// Items in flight per wave: the largest of 4, 2, 1 (3, 2, 1 for MXFP4 items)
+// that divides the wave's items.
 static int ring_depth(int nk) { return nk % 4 == 0 ? 4 : (nk % 2 == 0 ? 2 : 1); }
+static int ring_depth4(int ni) { return ni % 3 == 0 ? 3 : (ni % 2 == 0 ? 2 : 1); }
 
-// K parts of the up/gate slabs: the largest of 4, 2, 1 dividing H/128.
-int upgate_k_parts(int hidden, int inter) {
-  (void)inter;
-  const int nkb = hidden / 128;
-  return nkb % 4 == 0 ? 4 : (nkb % 2 == 0 ? 2 : 1);
+// K parts of the up/gate slabs: the largest of 4, 2, 1 dividing H/128, or
+// H/256 when routed experts are MXFP4 (their items are two K blocks).
+int upgate_k_parts(int hidden, int routed_fmt) {
+  const int n = routed_fmt == kFmtMxfp4 ? hidden / 256 : hidden / 128;
+  return n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1);
+}
+
+template <int RF, int P>
+static void launch_p4(int p4, dim3 grid, const Weights& w, const Ws& ws, const Dims& d,
+                      hipStream_t stream) {
+  switch (p4) {
+    case 3: hipLaunchKernelGGL((moe_upgate_kernel<RF, P, 3>), grid, dim3(256), 0, stream, w, ws, d); break;
+    case 2: hipLaunchKernelGGL((moe_upgate_kernel<RF, P, 2>), grid, dim3(256), 0, stream, w, ws, d); break;
+    default: hipLaunchKernelGGL((moe_upgate_kernel<RF, P, 1>), grid, dim3(256), 0, stream, w, ws, d); break;
+  }
 }
 
 hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& ws,
                          const Dims& d, hipStream_t stream) {
-  if (rfmt != kFmtFp8) return hipErrorInvalidValue;
   const int br = 16 * (4 / d.ks);
   const dim3 grid(d.Is / br + max_groups * (d.I / br));
-  switch (ring_depth(d.H / 128 / d.ks)) {
-    case 4: hipLaunchKernelGGL((moe_upgate_kernel<4>), grid, dim3(256), 0, stream, w, ws, d); break;
-    case 2: hipLaunchKernelGGL((moe_upgate_kernel<2>), grid, dim3(256), 0, stream, w, ws, d); break;
-    default: hipLaunchKernelGGL((moe_upgate_kernel<1>), grid, dim3(256), 0, stream, w, ws, d); break;
+  const int p = ring_depth(d.H / 128 / d.ks);
+  if (rfmt == kFmtFp8) {
+    switch (p) {
+      case 4: hipLaunchKernelGGL((moe_upgate_kernel<kFmtFp8, 4, 1>), grid, dim3(256), 0, stream, w, ws, d); break;
+      case 2: hipLaunchKernelGGL((moe_upgate_kernel<kFmtFp8, 2, 1>), grid, dim3(256), 0, stream, w, ws, d); break;
+      default: hipLaunchKernelGGL((moe_upgate_kernel<kFmtFp8, 1, 1>), grid, dim3(256), 0, stream, w, ws, d); break;
+    }
+  } else if (rfmt == kFmtMxfp4) {
+    const int p4 = ring_depth4(d.H / 256 / d.ks);
+    switch (p) {
+      case 4: launch_p4<kFmtMxfp4, 4>(p4, grid, w, ws, d, stream); break;
+      case 2: launch_p4<kFmtMxfp4, 2>(p4, grid, w, ws, d, stream); break;
+      default: launch_p4<kFmtMxfp4, 1>(p4, grid, w, ws, d, stream); break;
+    }
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
