@@ -44,17 +44,40 @@ def fp8_matrix_bytes(n, k):
     return n * k + (n // 128) * (k // 128) * 4
 
 
+def mxfp4_matrix_bytes(n, k):
+    return n * k // 2 + n * (k // 32)
+
+
+def routed_matrix_bytes(layer, n, k):
+    return mxfp4_matrix_bytes(n, k) if layer.routed_fmt == 2 else fp8_matrix_bytes(n, k)
+
+
 def step_bytes(layer, rows, d):
     H, I, E, Is = layer.hidden, layer.inter, layer.n_experts, layer.shared_inter
-    expert = 2 * fp8_matrix_bytes(I, H) + fp8_matrix_bytes(H, I)
+    expert = 2 * routed_matrix_bytes(layer, I, H) + routed_matrix_bytes(layer, H, I)
     shared = (2 * fp8_matrix_bytes(Is, H) + fp8_matrix_bytes(H, Is)) if Is else 0
     return d * expert + shared + E * H * 2 + H * 2 + 2 * rows * H * 2
 
 
 def upgate_bytes(layer, rows, d):
     H, I, Is = layer.hidden, layer.inter, layer.shared_inter
-    return (d * 2 * fp8_matrix_bytes(I, H) + (2 * fp8_matrix_bytes(Is, H) if Is else 0)
+    return (d * 2 * routed_matrix_bytes(layer, I, H) + (2 * fp8_matrix_bytes(Is, H) if Is else 0)
             + rows * H + rows * (H // 128) * 4)
+
+
+def layer_copies(S, base, n):
+    copies = [base]
+    for _ in range(n - 1):
+        copies.append(S.Layer(base.shape, base.hidden, base.inter, base.n_experts,
+                              base.shared_inter, base.rms_eps, base.gamma.clone(),
+                              base.router_w.clone(),
+                              S.ExpertWeights(base.routed.fmt, *[tuple(t.clone() for t in m) for m in
+                                                                 (base.routed.gate, base.routed.up,
+                                                                  base.routed.down)]),
+                              S.ExpertWeights(base.shared.fmt, *[tuple(t.clone() for t in m) for m in
+                                                                 (base.shared.gate, base.shared.up,
+                                                                  base.shared.down)])))
+    return copies
 
 
 def measured_traffic():
@@ -165,8 +188,8 @@ def cpu_baseline(torch, layer, res, seconds):
     cache = {}
     done, t_used, nbytes, errs = 0, 0.0, 0.0, []
     out = torch.empty(1, layer.hidden, dtype=torch.bfloat16, device="cuda")
-    while done < POOL and (done == 0 or t_used < seconds):
-        x = pool[done]
+    while done < 64 * POOL and (done == 0 or t_used < seconds):
+        x = pool[done % POOL]
         runner.ctx.step(x, 1, res["weights"][0], out)
         torch.cuda.synchronize()
         gpu = runner.debug(1)
@@ -185,7 +208,8 @@ def cpu_baseline(torch, layer, res, seconds):
     gbs = nbytes / t_used / 1e9
     return dict(value=gbs, unit="GB/s", cores=cores, kind="oracle",
                 sample=f"{done} full 1-row GLM-scale steps (router, 8 routed + shared expert, "
-                       f"combine) in {t_used:.1f} s; fp64, {cores} OpenMP threads",
+                       f"combine; the {POOL} token rows of the timed pool, cycled) in "
+                       f"{t_used:.1f} s; fp64, {cores} OpenMP threads",
                 ms_per_step=t_used / done * 1e3), max(errs)
 
 
@@ -199,6 +223,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lowbit", action="store_true")
+    ap.add_argument("--no-mxfp4", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the decode step has no multi-GPU path in this "
@@ -214,19 +239,10 @@ def main():
     torch.cuda.set_device(0)
     log("generating GLM-scale layer")
     base = S.make_layer("glm", seed=1001, device="cuda")
-    copies = [base]
-    for _ in range(args.copies - 1):
-        c = S.Layer(base.shape, base.hidden, base.inter, base.n_experts, base.shared_inter,
-                    base.rms_eps, base.gamma.clone(), base.router_w.clone(),
-                    S.ExpertWeights(base.routed.fmt, *[tuple(t.clone() for t in m) for m in
-                                                       (base.routed.gate, base.routed.up,
-                                                        base.routed.down)]),
-                    S.ExpertWeights(base.shared.fmt, *[tuple(t.clone() for t in m) for m in
-                                                       (base.shared.gate, base.shared.up,
-                                                        base.shared.down)]))
-        copies.append(c)
+    copies = layer_copies(S, base, args.copies)
+    ncopies = len(copies)
     torch.cuda.synchronize()
-    log(f"{len(copies)} layer copies resident")
+    log(f"{ncopies} layer copies resident")
 
     results = {}
     for rows in [int(r) for r in args.rows.split(",")]:
@@ -237,6 +253,33 @@ def main():
         log(f"rows={rows}: {r['us_per_step']:.1f} us/step, {r['gbs']:.0f} GB/s "
             f"({100 * r['frac']:.1f}% of peak), D={r['d_mean']:.1f}, kernels {r['kernel_us']}")
 
+    main_rows = 1 if 1 in results else min(results)
+    m = results[main_rows]
+    cpu, err = (None, None)
+    if not args.no_cpu_baseline and main_rows == 1:
+        log("timing the oracle on the host")
+        cpu, err = cpu_baseline(torch, base, m, args.cpu_seconds)
+    mx = None
+    if not args.no_mxfp4:
+        log("generating the GLM-scale layer with MXFP4 routed experts")
+        del copies
+        torch.cuda.empty_cache()
+        mbase = S.make_layer("glm", routed_fmt=S.FMT_MXFP4, seed=1002, device="cuda")
+        mcopies = layer_copies(S, mbase, args.copies)
+        torch.cuda.synchronize()
+        mx = {}
+        for rows in (1, 8):
+            r = time_rows(torch, B, S, mbase, mcopies, rows, args.steps, args.warmup,
+                          seed_base=6000 + 100 * rows)
+            log(f"mxfp4 rows={rows}: {r['us_per_step']:.1f} us/step, {r['gbs']:.0f} GB/s "
+                f"({100 * r['frac']:.1f}% of peak), D={r['d_mean']:.1f}, kernels {r['kernel_us']}")
+            mx[str(rows)] = {"us_per_step": round(r["us_per_step"], 2), "gbs": round(r["gbs"], 1),
+                             "frac_of_peak": round(r["frac"], 4), "distinct_experts": r["d_mean"],
+                             "bytes_per_step": int(r["bytes_per_step"]),
+                             "kernel_us": {k: round(t, 2) for k, t in r["kernel_us"].items()}}
+        del mcopies, mbase
+        torch.cuda.empty_cache()
+
     lowbit = None
     if not args.no_lowbit:
         lowbit = {}
@@ -245,12 +288,6 @@ def main():
             lowbit[name] = time_lowbit(torch, B, S, n, k, steps=max(args.steps, 50))
             log(f"  {lowbit[name]}")
 
-    main_rows = 1 if 1 in results else min(results)
-    m = results[main_rows]
-    cpu, err = (None, None)
-    if not args.no_cpu_baseline and main_rows == 1:
-        log("timing the oracle on the host")
-        cpu, err = cpu_baseline(torch, base, m, args.cpu_seconds)
     line = {
         "metric": METRIC,
         "value": round(m["gbs"], 1),
@@ -270,7 +307,7 @@ def main():
                                "256 routed experts (top-8) of intermediate 2048 + 1 shared "
                                "expert of 2048, FP8 E4M3 weights with 128x128 fp32 scales, "
                                "FP8 activations and mid, bf16 in/out",
-                   "rows": main_rows, "layer_copies": len(copies), "x_pool": POOL},
+                   "rows": main_rows, "layer_copies": ncopies, "x_pool": POOL},
         "roofline": {"bound": "hbm", "kernel": "moe_upgate_kernel",
                      "achieved": round(m["upgate_gbs"], 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(m["upgate_gbs"] / PEAK_GBS, 4),
@@ -285,6 +322,7 @@ def main():
                              "kernel_us": {k: round(t, 2) for k, t in v["kernel_us"].items()},
                              "upgate_gbs": round(v["upgate_gbs"], 1)}
                     for r, v in results.items()},
+        "mxfp4_routed": mx,
         "lowbit_gemv": lowbit,
     }
     print(json.dumps(line), flush=True)
