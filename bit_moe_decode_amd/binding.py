@@ -17,8 +17,8 @@ FMT_FP8 = 1
 FMT_MXFP4 = 2
 FMT_Q1 = 3
 F_NO_DEDUP = 1 << 1
-N_KERNELS = 6
-KERNEL_NAMES = ("router", "route", "upgate", "midq", "down", "combine")  # launch order
+N_KERNELS = 5
+KERNEL_NAMES = ("router", "route", "upgate", "down", "combine")  # launch order
 
 
 class MoeError(RuntimeError):

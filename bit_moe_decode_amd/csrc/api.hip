@@ -13,7 +13,6 @@ hipError_t launch_router(const uint16_t* x, const Weights& w, const Ws& ws, cons
 hipError_t launch_route(const Ws& ws, const Dims& d, hipStream_t stream);
 hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& ws,
                          const Dims& d, hipStream_t stream);
-hipError_t launch_midq(int rfmt, const Ws& ws, const Dims& d, hipStream_t stream);
 hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws, const Dims& d,
                        hipStream_t stream);
 hipError_t launch_combine(const Ws& ws, const Dims& d, uint16_t* out, hipStream_t stream);
@@ -39,8 +38,8 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct Plan {
   int H, I, E, Is, R, imax, groups, ks;
   size_t off_logits, off_rstd, off_ids, off_gates, off_ngroups, off_gexpert,
-      off_gowner, off_gmask, off_gslot, off_grows, off_gnrows, off_actq, off_acts, off_gpart,
-      off_upart, off_mid, off_midq, off_midqs, off_ypart, total;
+      off_gowner, off_gmask, off_gslot, off_grows, off_gnrows, off_actq, off_acts, off_mid,
+      off_midq, off_midqs, off_ypart, total;
 };
 
 bool is_mult(int v, int m) { return v > 0 && v % m == 0; }
@@ -93,8 +92,6 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   p->off_actq = take(R * H);
   p->off_acts = take(R * (H / 128) * 4);
   const size_t U = R * 9;  // (row, pick) pairs, pick 8 = the shared expert
-  p->off_gpart = take(U * p->ks * IM * 4);
-  p->off_upart = take(U * p->ks * IM * 4);
   p->off_mid = take(U * IM * 4);
   p->off_midq = take(U * IM);
   p->off_midqs = take(U * (IM / 128) * 4);
@@ -154,8 +151,6 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
   v.grp_nrows = reinterpret_cast<uint8_t*>(b + p.off_gnrows);
   v.act_q = reinterpret_cast<uint8_t*>(b + p.off_actq);
   v.act_s = reinterpret_cast<float*>(b + p.off_acts);
-  v.gpart = reinterpret_cast<float*>(b + p.off_gpart);
-  v.upart = reinterpret_cast<float*>(b + p.off_upart);
   v.mid = reinterpret_cast<float*>(b + p.off_mid);
   v.midq = reinterpret_cast<uint8_t*>(b + p.off_midq);
   v.midqs = reinterpret_cast<float*>(b + p.off_midqs);
@@ -234,14 +229,11 @@ moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
   if (launch_upgate(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream) != hipSuccess)
     return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (launch_midq(ctx->cfg.routed_fmt, ctx->view, d, stream) != hipSuccess)
-    return MOE_ERR_DEVICE;
-  if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (launch_down(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream) != hipSuccess)
     return MOE_ERR_DEVICE;
-  if (ev && hipEventRecord(ev[5], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (launch_combine(ctx->view, d, out, stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (ev && hipEventRecord(ev[6], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[5], stream) != hipSuccess) return MOE_ERR_DEVICE;
   return MOE_OK;
 }
 

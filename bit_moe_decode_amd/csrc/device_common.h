@@ -1,5 +1,5 @@
 // device_common.h -- shared device helpers and the workspace view for the
-// gfx950 MoE decode kernels (router.hip, upgate.hip, midq.hip, down.hip).
+// gfx950 MoE decode kernels (router.hip, upgate.hip, down.hip).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,8 +33,6 @@ struct Ws {
   uint8_t* act_q;         // [max_rows][H]
   float* act_s;           // [max_rows][H/128]
   // per (row, pick) with pick 8 = the shared expert: u = row * 9 + pick
-  float* gpart;           // [max_rows * 9][ks][imax] up/gate K-part sums of gate
-  float* upart;           // [max_rows * 9][ks][imax] ... and of up
   float* mid;             // [max_rows * 9][imax]
   uint8_t* midq;          // [max_rows * 9][imax]
   float* midqs;           // [max_rows * 9][imax/128]

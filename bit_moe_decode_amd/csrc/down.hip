@@ -1,22 +1,30 @@
 // down.hip -- down GEMV of the shared expert and of every distinct routed
-// expert from the FP8 mid, per (row, pick); then the gate-weighted combine.
+// expert from mid, per (row, pick); then the gate-weighted combine.
 //
 // #85 Mod. row 16: down units take one expert's tile against every row that
 // uses it; a row's output is summed over its units in the one-row form's
-// order, so dedup changes no output bit.  Mod. row 1: down reads mid as the
-// FP8 bytes and scales quantised once.  Mod. rows 18 and 21: 16-byte,
-// nontemporal weight loads.
+// order, so dedup changes no output bit.  Mod. row 1: down reads mid as FP8
+// bytes with one fp32 scale per 1x128 block, quantised once per (row, pick)
+// and expert.  Mod. rows 18 and 21: 16-byte, nontemporal weight loads.
 //
 // moe_down_kernel: block = 4 waves = 64 output rows of one expert (the shared
 // expert's H/64 blocks first, then H/64 for each of the step's possible routed
 // groups; blocks of groups past the step's D exit at once).  Many small
-// blocks let the hardware dispatcher even out the load per CU.  A wave owns 16
-// output rows over the whole K: for each 128-wide K block it loads its 16
-// weight rows row-contiguously, re-lays them through LDS into MFMA operand
-// order and runs one 16x16x128 FP8 MFMA against the expert's midq columns (one
-// column per using row), scaled by weight scale x mid scale and accumulated in
-// fp32.  It stores y[row, pick][h]; every (row, pick) belongs to exactly one
-// expert of the step, so no two writes collide.
+// blocks let the hardware dispatcher even out the load per CU.
+//
+// FP8 experts.  The block first puts the first K blocks of its weight stream
+// in flight, then quantises the fp32 mid of each of its columns (one per row
+// that uses the expert) into LDS: per 1x128 block s = amax / 448 (fp32) and
+// codes = E4M3(mid / s) by the hardware's round-to-nearest-even conversion, an
+// all-zero block giving s = 0 and zero codes.  Every block of an expert does
+// this the same way, so all use the same bytes; the first block also stores
+// them as the step's midq / midqs.  A wave then owns 16 output rows over the
+// whole K: for each 128-wide K block it loads its 16 weight rows
+// row-contiguously, re-lays them through LDS into MFMA operand order and runs
+// one 16x16x128 FP8 MFMA against the mid codes, scaled by weight scale x mid
+// scale and accumulated in fp32.  It stores y[row, pick][h]; every
+// (row, pick) belongs to exactly one expert of the step, so no two writes
+// collide.
 //
 // MXFP4 routed experts (mid kept in fp32, as the oracle does): a VALU path in
 // the same blocks, one mid column at a time.  Per K chunk of 512 the block
@@ -33,9 +41,65 @@
 namespace moe {
 
 struct DnStage {
-  u32x4 w0, w1, m0, m1;
-  float sd, sm;
+  u32x4 w0, w1;
+  float sd;
 };
+
+// Dynamic LDS of the down kernel: mid codes of each column (row stride
+// I + 16 bytes, so that the columns of one MFMA read start on different
+// banks), then their scales.
+__host__ __device__ inline int dn_code_stride(int inter) { return inter + 16; }
+__host__ __device__ inline size_t dn_lds_bytes(int rows, int inter) {
+  return (size_t)rows * dn_code_stride(inter) + (size_t)rows * (inter / 128) * 4;
+}
+
+// The (row, pick) index u = row * 9 + pick of column c of a block: the shared
+// expert's columns are the rows in order (pick 8); a routed group's are its
+// using rows (`rows8`, one byte each) with their picks (`picks8`, byte per row).
+struct DnCols {
+  int g;  // -1: shared expert
+  uint64_t rows8, picks8;
+  __device__ __forceinline__ int u(int c) const {
+    if (g < 0) return c * 9 + 8;
+    const int r = (int)((rows8 >> (8 * c)) & 0xFF);
+    return r * 9 + (int)((picks8 >> (8 * r)) & 0xFF);
+  }
+};
+
+// Four fp32 -> four E4M3FN bytes (hardware conversion, round to nearest even).
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float e) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, e, lo, true);
+}
+
+// Quantises the fp32 mid of the block's columns into LDS, per 1x128 block:
+// half-wave h of the block takes blocks h, h + 8, ..., 4 values a lane.  The
+// first block of an expert (`publish`) also stores codes and scales as the
+// step's midq / midqs.
+__device__ __forceinline__ void dn_quant_mid(const Ws& ws, const Dims& d, int nrows,
+                                             const DnCols& cols, bool publish, uint8_t* s_q,
+                                             float* s_qs) {
+  const int tid = threadIdx.x, hw = tid >> 5, l = tid & 31;
+  const int nkb = d.I / 128, cs = dn_code_stride(d.I), T = nrows * nkb;
+  for (int t = hw; t < T; t += 8) {
+    const int c = t / nkb, kb = t - c * nkb;
+    const int uc = cols.u(c);
+    const size_t src = (size_t)uc * d.imax + kb * 128 + 4 * l;
+    const v4f v = *reinterpret_cast<const v4f*>(ws.mid + src);
+    uint32_t m = max(max(__float_as_uint(fabsf(v[0])), __float_as_uint(fabsf(v[1]))),
+                     max(__float_as_uint(fabsf(v[2])), __float_as_uint(fabsf(v[3]))));
+    m = row16_umax(m);
+    m = max(m, (uint32_t)__shfl_xor((int)m, 16, kWave));
+    const float s = __uint_as_float(m) / 448.0f;
+    const uint32_t q = s > 0.f ? f32x4_to_e4m3(v[0] / s, v[1] / s, v[2] / s, v[3] / s) : 0u;
+    *reinterpret_cast<uint32_t*>(s_q + c * cs + kb * 128 + 4 * l) = q;
+    if (l == 0) s_qs[c * nkb + kb] = s;
+    if (publish) {
+      *reinterpret_cast<uint32_t*>(ws.midq + src) = q;
+      if (l == 0) ws.midqs[(size_t)uc * (d.imax / 128) + kb] = s;
+    }
+  }
+}
 
 constexpr int kDnChunk = 512;                  // K inputs per staged mid chunk (MXFP4)
 constexpr int kDnMidStride = kDnChunk + kDnChunk / 8;  // 4 pad floats per 32
@@ -57,7 +121,7 @@ __device__ __forceinline__ float e8m0_scale(uint32_t e) {
 // 16(l%4) + 64i (32 inputs, one E8M0 block each); the 4 lanes of a row are
 // summed at the end.
 __device__ __forceinline__ void down_fp4_block(const Weights& w, const Ws& ws, const Dims& d,
-                                               int e, int nrows, const int* ucol, int hb,
+                                               int e, int nrows, const DnCols& cols, int hb,
                                                float* s_mid) {
   constexpr int R = kDnChunk / 128;  // runs of a lane per chunk
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -68,7 +132,8 @@ __device__ __forceinline__ void down_fp4_block(const Weights& w, const Ws& ws, c
   const uint8_t* erow = reinterpret_cast<const uint8_t*>(w.down_s) + ((size_t)e * H + h) * (I / 32);
 #pragma unroll 1
   for (int c = 0; c < nrows; c++) {
-    const float* mcol = ws.mid + (size_t)ucol[c] * d.imax;
+    const int uc = cols.u(c);
+    const float* mcol = ws.mid + (size_t)uc * d.imax;
     float a = 0.f;
 #pragma unroll 1
     for (int k0 = 0; k0 < I; k0 += kDnChunk) {
@@ -117,7 +182,7 @@ __device__ __forceinline__ void down_fp4_block(const Weights& w, const Ws& ws, c
     // sum over the 4 lanes of the row (xor 1, xor 2 within quads)
     a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xF, 0xF, false));
     a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF, false));
-    if (q == 0) ws.ypart[(size_t)ucol[c] * H + h] = a;
+    if (q == 0) ws.ypart[(size_t)uc * H + h] = a;
   }
 }
 
@@ -125,6 +190,7 @@ template <int RF, int P>
 __global__ __launch_bounds__(256) void moe_down_kernel(Weights w, Ws ws, Dims d) {
   __shared__ uint8_t s_tile[4][kTileBytes];
   __shared__ float s_mid[RF == kFmtMxfp4 ? kDnMidStride : 1];
+  extern __shared__ __align__(16) uint8_t dyn[];  // dn_lds_bytes(rows, I)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = d.H, I = d.I, nkb = I / 128;
   const int col = lane & 15;
@@ -150,19 +216,12 @@ __global__ __launch_bounds__(256) void moe_down_kernel(Weights w, Ws ws, Dims d)
     picks8 = *reinterpret_cast<const uint64_t*>(ws.grp_slot + g * 8);
     if (g >= D) return;
   }
+  const DnCols cols{g, rows8, picks8};
   if (RF == kFmtMxfp4 && g >= 0) {
-    int ucol[kMaxRows];
-#pragma unroll
-    for (int c = 0; c < kMaxRows; c++) {
-      const int r = (int)((rows8 >> (8 * c)) & 0xFF);
-      ucol[c] = c < nrows ? r * 9 + (int)((picks8 >> (8 * r)) & 0xFF) : 0;
-    }
-    down_fp4_block(w, ws, d, e, nrows, ucol, b * 64, s_mid);
+    down_fp4_block(w, ws, d, e, nrows, cols, b * 64, s_mid);
     return;
   }
-  const int row = col < nrows ? (g < 0 ? col : (int)((rows8 >> (8 * (col & 7))) & 0xFF)) : 0;
-  const int pick = g < 0 ? 8 : (int)((picks8 >> (8 * row)) & 0xFF);
-  const int u = col < nrows ? row * 9 + pick : 0;  // (row, pick) of this column
+  const int cc = col < nrows ? col : 0;  // columns past the rows reuse column 0
   const int h0 = b * 64 + wv * 16;
 
   const uint8_t* wb = e < 0 ? w.sd_c : w.down_c + (size_t)e * H * I;
@@ -171,46 +230,49 @@ __global__ __launch_bounds__(256) void moe_down_kernel(Weights w, Ws ws, Dims d)
   // lane l loads rows h0 + l/8 and h0 + 8 + l/8, 16-byte chunk l%8
   const uint8_t* pw = wb + (size_t)(h0 + (lane >> 3)) * I + (lane & 7) * 16;
   const size_t r8 = (size_t)8 * I;
-  const uint8_t* pm = ws.midq + (size_t)u * d.imax + (lane >> 4) * 32;
   const float* psd = sb + (size_t)(h0 / 128) * nkb;
-  const float* psm = ws.midqs + (size_t)u * (d.imax / 128);
   uint8_t* tile = s_tile[wv];
+  uint8_t* s_q = dyn;
+  float* s_qs = reinterpret_cast<float*>(dyn + (size_t)d.rows * dn_code_stride(I));
+  const uint8_t* pm = s_q + cc * dn_code_stride(I) + (lane >> 4) * 32;
+  const float* psm = s_qs + cc * nkb;
 
   auto issue = [&](DnStage& s, int k) {
     const size_t o = (size_t)k * 128;
     s.w0 = ld_nt16(pw + o);
     s.w1 = ld_nt16(pw + r8 + o);
-    s.m0 = ld16(pm + o);
-    s.m1 = ld16(pm + o + 16);
     s.sd = psd[k];
-    s.sm = psm[k];
   };
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  auto consume = [&](DnStage& s) {
+  auto consume = [&](DnStage& s, int k) {
     tile_put(tile, lane, s.w0, s.w1);
     asm volatile("" ::: "memory");
-    const v4f c = mfma_fp8(tile_get(tile, lane), cat8(s.m0, s.m1));
+    const u32x4 m0 = ld16(pm + k * 128), m1 = ld16(pm + k * 128 + 16);
+    const v4f c = mfma_fp8(tile_get(tile, lane), cat8(m0, m1));
     asm volatile("" ::: "memory");
-    const float f = s.sd * s.sm;
+    const float f = s.sd * psm[k];
 #pragma unroll
     for (int v = 0; v < 4; v++) acc[v] = fmaf(c[v], f, acc[v]);
   };
-  // ring of P K blocks (P divides nkb): every issued load is used
+  // ring of P K blocks (P divides nkb): every issued load is used.  The first
+  // P are in flight while the block quantises mid.
   DnStage st[P];
 #pragma unroll
   for (int p = 0; p < P; p++) issue(st[p], p);
+  dn_quant_mid(ws, d, nrows, cols, b == 0, s_q, s_qs);
+  __syncthreads();
   for (int k0 = 0; k0 < nkb - P; k0 += P) {
 #pragma unroll
     for (int p = 0; p < P; p++) {
-      consume(st[p]);
+      consume(st[p], k0 + p);
       issue(st[p], k0 + P + p);
     }
   }
 #pragma unroll
-  for (int p = 0; p < P; p++) consume(st[p]);
+  for (int p = 0; p < P; p++) consume(st[p], nkb - P + p);
   pin4(acc);  // the MFMAs run with every lane, before the divergent store
   if (col < nrows)
-    *reinterpret_cast<v4f*>(ws.ypart + (size_t)u * H + h0 + 4 * (lane >> 4)) =
+    *reinterpret_cast<v4f*>(ws.ypart + (size_t)cols.u(col) * H + h0 + 4 * (lane >> 4)) =
         v4f{acc[0], acc[1], acc[2], acc[3]};
 }
 
@@ -248,27 +310,41 @@ static int down_ring(int inter) {
   return nkb % 8 == 0 ? 8 : (nkb % 4 == 0 ? 4 : (nkb % 2 == 0 ? 2 : 1));
 }
 
+// Launches one instantiation with `lds` bytes of dynamic LDS, raising the
+// kernel's dynamic-LDS limit first when it is above the default 64 KB.
+template <int RF, int P>
+static hipError_t launch_one(dim3 grid, size_t lds, const Weights& w, const Ws& ws,
+                             const Dims& d, hipStream_t stream) {
+  static size_t raised = 0;  // the limit already set for this instantiation
+  if (lds > 65536 && lds > raised) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&moe_down_kernel<RF, P>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    raised = lds;
+  }
+  hipLaunchKernelGGL((moe_down_kernel<RF, P>), grid, dim3(256), lds, stream, w, ws, d);
+  return hipGetLastError();
+}
+
 template <int RF>
-static void launch_rf(dim3 grid, const Weights& w, const Ws& ws, const Dims& d,
-                      hipStream_t stream) {
+static hipError_t launch_rf(dim3 grid, size_t lds, const Weights& w, const Ws& ws,
+                            const Dims& d, hipStream_t stream) {
   switch (down_ring(d.I)) {
-    case 8: hipLaunchKernelGGL((moe_down_kernel<RF, 8>), grid, dim3(256), 0, stream, w, ws, d); break;
-    case 4: hipLaunchKernelGGL((moe_down_kernel<RF, 4>), grid, dim3(256), 0, stream, w, ws, d); break;
-    case 2: hipLaunchKernelGGL((moe_down_kernel<RF, 2>), grid, dim3(256), 0, stream, w, ws, d); break;
-    default: hipLaunchKernelGGL((moe_down_kernel<RF, 1>), grid, dim3(256), 0, stream, w, ws, d); break;
+    case 8: return launch_one<RF, 8>(grid, lds, w, ws, d, stream);
+    case 4: return launch_one<RF, 4>(grid, lds, w, ws, d, stream);
+    case 2: return launch_one<RF, 2>(grid, lds, w, ws, d, stream);
+    default: return launch_one<RF, 1>(grid, lds, w, ws, d, stream);
   }
 }
 
 hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws, const Dims& d,
                        hipStream_t stream) {
   const dim3 grid((d.H / 64) * ((d.Is > 0 ? 1 : 0) + max_groups));
-  if (rfmt == kFmtFp8)
-    launch_rf<kFmtFp8>(grid, w, ws, d, stream);
-  else if (rfmt == kFmtMxfp4)
-    launch_rf<kFmtMxfp4>(grid, w, ws, d, stream);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  const size_t lds = dn_lds_bytes(d.rows, d.I);
+  if (rfmt == kFmtFp8) return launch_rf<kFmtFp8>(grid, lds, w, ws, d, stream);
+  if (rfmt == kFmtMxfp4) return launch_rf<kFmtMxfp4>(grid, lds, w, ws, d, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_combine(const Ws& ws, const Dims& d, uint16_t* out, hipStream_t stream) {

@@ -1,6 +1,5 @@
 // upgate.hip -- up/gate GEMV of the shared expert and of every distinct
-// routed expert, as K-part sums; moe_midq_kernel (midq.hip) adds the parts,
-// applies SiLU * up and quantises mid.
+// routed expert, and mid = silu(gate) * up from it.
 //
 // #85 Mod. row 16: up/gate jobs are tiles of the shared expert and of each
 // distinct expert, with every row that uses the expert as an MFMA column, so
@@ -17,8 +16,11 @@
 // A wave loads its 16 weight rows of gate and of up row-contiguously (8 lanes
 // read one row's 128-byte line), re-lays them through LDS into MFMA operand
 // order and runs 16x16x128 MFMAs whose 16 columns are the expert's using rows;
-// the fp32 results are scaled and accumulated.  The wave then stores its K-part
-// sums per (row, pick).  No block waits for another, and no wave for another.
+// the fp32 results are scaled and accumulated.  The block then adds its K-part
+// sums in part order, through LDS, and stores
+//   mid = silu(gate * rstd) * (up * rstd)          (fp32)
+// per (row, pick) of its slabs.  No block waits for another.  The FP8
+// re-quantisation of mid is done by the down kernel, which reads it.
 //
 //  FP8 item = one 128-wide K block: one FP8 x FP8 MFMA per matrix, scaled by
 //    weight block scale x activation block scale.
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims 
   // ---- the block's expert and slab
   const int nb_sh = d.Is / (16 * spb);
   int b = blockIdx.x, g = -1, nrows, row, e;
-  uint64_t picks8 = 0;  // pick of each row in the group (routed)
+  uint64_t rows8 = 0, picks8 = 0;  // using rows, and the pick of each row (routed)
   if (b < nb_sh) {
     nrows = d.rows;
     row = col < nrows ? col : 0;
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims 
     const int D = *ws.n_groups;
     e = ws.grp_expert[g];
     nrows = ws.grp_nrows[g];
-    const uint64_t rows8 = *reinterpret_cast<const uint64_t*>(ws.grp_rows + g * 8);
+    rows8 = *reinterpret_cast<const uint64_t*>(ws.grp_rows + g * 8);
     picks8 = *reinterpret_cast<const uint64_t*>(ws.grp_slot + g * 8);
     if (g >= D) return;
     row = col < nrows ? (int)((rows8 >> (8 * (col & 7))) & 0xFF) : 0;
@@ -249,13 +251,33 @@ __global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims 
     const int nk = d.H / 128 / KS;
     ug_fp8<P>(w, ws, d, j, kp * nk, nk, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
   }
-  pin4(accg);  // the MFMAs run with every lane, before the divergent store
+  pin4(accg);  // the MFMAs run with every lane, before any divergent use
   pin4(accu);
-  if (col < nrows) {
-    const int pick = g < 0 ? 8 : (int)((picks8 >> (8 * row)) & 0xFF);
-    const size_t o = ((size_t)(row * 9 + pick) * KS + kp) * d.imax + j.n0 + 4 * (lane >> 4);
-    *reinterpret_cast<v4f*>(ws.gpart + o) = v4f{accg[0], accg[1], accg[2], accg[3]};
-    *reinterpret_cast<v4f*>(ws.upart + o) = v4f{accu[0], accu[1], accu[2], accu[3]};
+
+  // ---- K parts -> mid.  Each wave parks its 16 x 16 sums of gate and of up
+  // in its own (finished) tile, column-major: element (n, c) at c*16 + n.
+  float* part = reinterpret_cast<float*>(s_tile[wv][0]);
+  *reinterpret_cast<v4f*>(part + col * 16 + 4 * (lane >> 4)) = v4f{accg[0], accg[1], accg[2], accg[3]};
+  *reinterpret_cast<v4f*>(part + 256 + col * 16 + 4 * (lane >> 4)) =
+      v4f{accu[0], accu[1], accu[2], accu[3]};
+  __syncthreads();
+  // thread t: element n = t%16 of column c = t/16, for each slab of the block
+  const int c = tid >> 4, n = tid & 15;
+  if (c >= nrows) return;
+  const int r = g < 0 ? c : (int)((rows8 >> (8 * c)) & 0xFF);
+  const int pick = g < 0 ? 8 : (int)((picks8 >> (8 * r)) & 0xFF);
+  const float rs = ws.rstd[r];
+  float* mrow = ws.mid + (size_t)(r * 9 + pick) * d.imax;
+  for (int s = 0; s < spb; s++) {
+    const float* p0 = reinterpret_cast<const float*>(s_tile[s * KS][0]);
+    float gs = p0[tid], us = p0[256 + tid];
+    for (int q = 1; q < KS; q++) {  // parts in order
+      const float* pq = reinterpret_cast<const float*>(s_tile[s * KS + q][0]);
+      gs += pq[tid];
+      us += pq[256 + tid];
+    }
+    const float gt = gs * rs, ut = us * rs;
+    mrow[(b * spb + s) * 16 + n] = gt / (1.0f + expf(-gt)) * ut;
   }
 }
 
