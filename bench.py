@@ -14,7 +14,9 @@ One step = one moe_decode_step call (router, routing, up/gate, mid, down and
 combine kernels).  Value =
 algorithmic bytes of the step (each distinct expert counted once, read from
 the step's own dedup table, plus the shared expert, router, gamma, x and out)
-divided by the step time, timed over back-to-back steps.  A second pass over
+divided by the step time, timed over back-to-back steps.  The same steps are
+also captured into a HIP graph (32 steps per graph) and replayed, for the
+graph-replayed figure.  A second pass over
 the same steps has the library record HIP events around each kernel on the
 step's stream; the dominant kernel's (up/gate) average duration gives the
 roofline figure.  The fp64 CPU oracle is timed on the host for a bounded sample of the
@@ -34,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE decode layer µs/step + weight-stream HBM GB/s (% of peak) at 1/4/8 rows"
 PEAK_GBS = 8000.0  # MI355X HBM3E, published
 POOL = 16
+GSTEPS = 2 * POOL  # steps per captured graph
 
 
 def log(*a):
@@ -134,13 +137,39 @@ def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base):
     runner.ctx.set_timing(None)
     kern = [sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(steps)) / steps
             for k in range(nk)]
+    # (c) the same kind of steps captured once into a HIP graph and replayed:
+    # GSTEPS steps per graph (every pool entry and weight copy), replayed back to back
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.graph(g, stream=cap):
+        cs = torch.cuda.current_stream()
+        for i in range(GSTEPS):
+            runner.ctx.step(pool[i % POOL], rows, weights[i % len(weights)], out, cs)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+    reps = max(1, steps // GSTEPS)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = t0.elapsed_time(t1) / (reps * GSTEPS)
+    del g
     d_mean = sum(dvals[i % POOL] for i in range(steps)) / steps
     nbytes = sum(step_bytes(layer, rows, dvals[i % POOL]) for i in range(steps)) / steps
     ug_bytes = sum(upgate_bytes(layer, rows, dvals[i % POOL]) for i in range(steps)) / steps
     gbs = nbytes / (ms * 1e-3) / 1e9
     kernel_us = {name: kern[k] * 1e3 for k, name in enumerate(B.KERNEL_NAMES)}
     ug_gbs = ug_bytes / (kernel_us["upgate"] * 1e-6) / 1e9
+    gd = sum(dvals[i % POOL] for i in range(GSTEPS)) / GSTEPS
+    gbytes = sum(step_bytes(layer, rows, dvals[i % POOL]) for i in range(GSTEPS)) / GSTEPS
+    graph = dict(us_per_step=graph_ms * 1e3, gbs=gbytes / (graph_ms * 1e-3) / 1e9,
+                 distinct_experts=gd)
     return dict(rows=rows, us_per_step=ms * 1e3, gbs=gbs, frac=gbs / PEAK_GBS, d_mean=d_mean,
+                graph=graph,
                 bytes_per_step=nbytes,
                 kernel_us=kernel_us,
                 upgate_gbs=ug_gbs, upgate_bytes=ug_bytes, runner=runner, pool=pool,
@@ -251,7 +280,8 @@ def main():
                                   seed_base=5000 + 100 * rows)
         r = results[rows]
         log(f"rows={rows}: {r['us_per_step']:.1f} us/step, {r['gbs']:.0f} GB/s "
-            f"({100 * r['frac']:.1f}% of peak), D={r['d_mean']:.1f}, kernels {r['kernel_us']}")
+            f"({100 * r['frac']:.1f}% of peak), D={r['d_mean']:.1f}, kernels {r['kernel_us']}; "
+            f"graph replay {r['graph']['us_per_step']:.1f} us/step")
 
     main_rows = 1 if 1 in results else min(results)
     m = results[main_rows]
@@ -276,7 +306,8 @@ def main():
             mx[str(rows)] = {"us_per_step": round(r["us_per_step"], 2), "gbs": round(r["gbs"], 1),
                              "frac_of_peak": round(r["frac"], 4), "distinct_experts": r["d_mean"],
                              "bytes_per_step": int(r["bytes_per_step"]),
-                             "kernel_us": {k: round(t, 2) for k, t in r["kernel_us"].items()}}
+                             "kernel_us": {k: round(t, 2) for k, t in r["kernel_us"].items()},
+                             "graph_replay": {k: round(t, 2) for k, t in r["graph"].items()}}
         del mcopies, mbase
         torch.cuda.empty_cache()
 
@@ -320,7 +351,8 @@ def main():
                              "frac_of_peak": round(v["frac"], 4), "distinct_experts": v["d_mean"],
                              "bytes_per_step": int(v["bytes_per_step"]),
                              "kernel_us": {k: round(t, 2) for k, t in v["kernel_us"].items()},
-                             "upgate_gbs": round(v["upgate_gbs"], 1)}
+                             "upgate_gbs": round(v["upgate_gbs"], 1),
+                             "graph_replay": {k: round(t, 2) for k, t in v["graph"].items()}}
                     for r, v in results.items()},
         "mxfp4_routed": mx,
         "lowbit_gemv": lowbit,
