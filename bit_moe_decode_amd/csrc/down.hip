@@ -7,10 +7,13 @@
 // bytes with one fp32 scale per 1x128 block, quantised once per (row, pick)
 // and expert.  Mod. rows 18 and 21: 16-byte, nontemporal weight loads.
 //
-// moe_down_kernel: block = 4 waves = 64 output rows of one expert (the shared
-// expert's H/64 blocks first, then H/64 for each of the step's possible routed
-// groups; blocks of groups past the step's D exit at once).  Many small
-// blocks let the hardware dispatcher even out the load per CU.
+// moe_down_kernel: block = WPB waves = 16 * WPB output rows of one expert (the
+// shared expert's blocks first, then those of each of the step's possible
+// routed groups; blocks of groups past the step's D exit at once).  Many
+// small blocks let the hardware dispatcher even out the load per CU: WPB = 2
+// for FP8 steps of one or two rows, where 64-row blocks would leave some CUs
+// with a block more than others (a CU streams at most about 1/256 of the
+// chip's bandwidth), else 4.
 //
 // FP8 experts.  The block first puts the first K blocks of its weight stream
 // in flight, then quantises the fp32 mid of each of its columns (one per row
@@ -73,15 +76,16 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, flo
 }
 
 // Quantises the fp32 mid of the block's columns into LDS, per 1x128 block:
-// half-wave h of the block takes blocks h, h + 8, ..., 4 values a lane.  The
+// half-wave h of the block's n halves takes blocks h, h + n, ..., 4 values a
+// lane.  The
 // first block of an expert (`publish`) also stores codes and scales as the
 // step's midq / midqs.
 __device__ __forceinline__ void dn_quant_mid(const Ws& ws, const Dims& d, int nrows,
                                              const DnCols& cols, bool publish, uint8_t* s_q,
                                              float* s_qs) {
-  const int tid = threadIdx.x, hw = tid >> 5, l = tid & 31;
+  const int tid = threadIdx.x, hw = tid >> 5, l = tid & 31, nhw = blockDim.x >> 5;
   const int nkb = d.I / 128, cs = dn_code_stride(d.I), T = nrows * nkb;
-  for (int t = hw; t < T; t += 8) {
+  for (int t = hw; t < T; t += nhw) {
     const int c = t / nkb, kb = t - c * nkb;
     const int uc = cols.u(c);
     const size_t src = (size_t)uc * d.imax + kb * 128 + 4 * l;
@@ -186,17 +190,18 @@ __device__ __forceinline__ void down_fp4_block(const Weights& w, const Ws& ws, c
   }
 }
 
-template <int RF, int P>
-__global__ __launch_bounds__(256) void moe_down_kernel(Weights w, Ws ws, Dims d) {
-  __shared__ uint8_t s_tile[4][kTileBytes];
-  __shared__ float s_mid[RF == kFmtMxfp4 ? kDnMidStride : 1];
+template <int RF, int P, int WPB>
+__global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Dims d) {
+  static_assert(RF != kFmtMxfp4 || WPB == 4, "the MXFP4 path takes blocks of 4 waves");
+  __shared__ __align__(16) uint8_t s_tile[WPB][kTileBytes];
+  __shared__ __align__(16) float s_mid[RF == kFmtMxfp4 ? kDnMidStride : 1];
   extern __shared__ __align__(16) uint8_t dyn[];  // dn_lds_bytes(rows, I)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = d.H, I = d.I, nkb = I / 128;
   const int col = lane & 15;
 
   // ---- the block's expert and rows
-  const int per = H / 64;
+  const int per = H / (16 * WPB);
   const int nb_sh = d.Is > 0 ? per : 0;
   int b = blockIdx.x, g = -1, nrows, e;
   uint64_t rows8 = 0, picks8 = 0;
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(256) void moe_down_kernel(Weights w, Ws ws, Dims d)
     return;
   }
   const int cc = col < nrows ? col : 0;  // columns past the rows reuse column 0
-  const int h0 = b * 64 + wv * 16;
+  const int h0 = b * 16 * WPB + wv * 16;
 
   const uint8_t* wb = e < 0 ? w.sd_c : w.down_c + (size_t)e * H * I;
   const float* sb =
@@ -312,38 +317,49 @@ static int down_ring(int inter) {
 
 // Launches one instantiation with `lds` bytes of dynamic LDS, raising the
 // kernel's dynamic-LDS limit first when it is above the default 64 KB.
-template <int RF, int P>
-static hipError_t launch_one(dim3 grid, size_t lds, const Weights& w, const Ws& ws,
+template <int RF, int P, int WPB>
+static hipError_t launch_one(int max_groups, size_t lds, const Weights& w, const Ws& ws,
                              const Dims& d, hipStream_t stream) {
   static size_t raised = 0;  // the limit already set for this instantiation
   if (lds > 65536 && lds > raised) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_down_kernel<RF, P>),
+        reinterpret_cast<const void*>(&moe_down_kernel<RF, P, WPB>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     raised = lds;
   }
-  hipLaunchKernelGGL((moe_down_kernel<RF, P>), grid, dim3(256), lds, stream, w, ws, d);
+  const dim3 grid((d.H / (16 * WPB)) * ((d.Is > 0 ? 1 : 0) + max_groups));
+  hipLaunchKernelGGL((moe_down_kernel<RF, P, WPB>), grid, dim3(64 * WPB), lds, stream, w, ws, d);
   return hipGetLastError();
 }
 
+// Blocks of 2 waves (32 output rows) for FP8 steps of one or two rows, whose
+// few experts otherwise leave some CUs a block more than others; 4 waves
+// (64 rows) otherwise.
+template <int RF, int P>
+static hipError_t launch_wpb(int max_groups, size_t lds, const Weights& w, const Ws& ws,
+                             const Dims& d, hipStream_t stream) {
+  if (RF == kFmtFp8 && d.rows <= 2)
+    return launch_one<RF, P, RF == kFmtFp8 ? 2 : 4>(max_groups, lds, w, ws, d, stream);
+  return launch_one<RF, P, 4>(max_groups, lds, w, ws, d, stream);
+}
+
 template <int RF>
-static hipError_t launch_rf(dim3 grid, size_t lds, const Weights& w, const Ws& ws,
+static hipError_t launch_rf(int max_groups, size_t lds, const Weights& w, const Ws& ws,
                             const Dims& d, hipStream_t stream) {
   switch (down_ring(d.I)) {
-    case 8: return launch_one<RF, 8>(grid, lds, w, ws, d, stream);
-    case 4: return launch_one<RF, 4>(grid, lds, w, ws, d, stream);
-    case 2: return launch_one<RF, 2>(grid, lds, w, ws, d, stream);
-    default: return launch_one<RF, 1>(grid, lds, w, ws, d, stream);
+    case 8: return launch_wpb<RF, 8>(max_groups, lds, w, ws, d, stream);
+    case 4: return launch_wpb<RF, 4>(max_groups, lds, w, ws, d, stream);
+    case 2: return launch_wpb<RF, 2>(max_groups, lds, w, ws, d, stream);
+    default: return launch_wpb<RF, 1>(max_groups, lds, w, ws, d, stream);
   }
 }
 
 hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws, const Dims& d,
                        hipStream_t stream) {
-  const dim3 grid((d.H / 64) * ((d.Is > 0 ? 1 : 0) + max_groups));
   const size_t lds = dn_lds_bytes(d.rows, d.I);
-  if (rfmt == kFmtFp8) return launch_rf<kFmtFp8>(grid, lds, w, ws, d, stream);
-  if (rfmt == kFmtMxfp4) return launch_rf<kFmtMxfp4>(grid, lds, w, ws, d, stream);
+  if (rfmt == kFmtFp8) return launch_rf<kFmtFp8>(max_groups, lds, w, ws, d, stream);
+  if (rfmt == kFmtMxfp4) return launch_rf<kFmtMxfp4>(max_groups, lds, w, ws, d, stream);
   return hipErrorInvalidValue;
 }
 

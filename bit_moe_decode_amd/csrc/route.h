@@ -44,6 +44,95 @@ struct RouteSmem {
   int n_groups;
 };
 
+// The 8 largest order keys of the logits z[0 .. E) of one row, unordered,
+// with their expert IDs: written to ckey[0 .. 8) and cid[0 .. 8) by the lanes
+// that hold them.  Runs with one full wave; lane l holds experts l, l + 64,
+// ... in KPL = ceil(E / 64) key slots (key 0, below every logit, past E).
+template <int KPL>
+__device__ __forceinline__ void select8(const float* z, int E, int lane, uint32_t* ckey,
+                                        int* cid) {
+  uint32_t key[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; i++) {
+    const int e = lane + kWave * i;
+    const float v = z[e < E ? e : E - 1];  // lanes past E load in bounds
+    key[i] = e < E ? topk_vkey(v) : 0u;
+  }
+
+  // T: the largest t with at least 8 keys >= t (E >= 16 real keys, all >= 1)
+  uint32_t t = 0;
+  int nge = 0;
+  for (int b = 31; b >= 0; b--) {
+    const uint32_t c = t | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; i++) cnt += __popcll(__ballot(key[i] >= c));
+    if (cnt >= 8) {
+      t = c;
+      nge = cnt;
+      if (cnt == 8) break;
+    }
+  }
+  // picks: keys above T, then ties at T by increasing expert ID
+  int need = 8;
+  if (nge > 8) {
+    int ngt = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; i++) ngt += __popcll(__ballot(key[i] > t));
+    need = 8 - ngt;
+  }
+  int ties = 0, base = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; i++) {
+    bool take;
+    if (nge == 8) {
+      take = key[i] >= t;
+    } else {
+      const uint64_t tb = __ballot(key[i] == t);
+      take = key[i] > t || (key[i] == t && ties + lanes_below(tb) < need);
+      ties += __popcll(tb);
+    }
+    const uint64_t sb = __ballot(take);
+    if (take) {
+      const int pos = base + lanes_below(sb);
+      ckey[pos] = key[i];
+      cid[pos] = lane + kWave * i;
+    }
+    base += __popcll(sb);
+  }
+}
+
+// Rank of pick j among a row's 8 picks (unordered keys and IDs): the picks
+// with a larger key, or an equal key and a lower ID.
+__device__ __forceinline__ int rank8(const uint32_t* ckey, const int* cid, int j) {
+  const uint32_t k = ckey[j];
+  const int id = cid[j];
+  int rank = 0;
+#pragma unroll
+  for (int m = 0; m < 8; m++) {
+    const uint32_t km = ckey[m];
+    rank += (km > k || (km == k && cid[m] < id)) ? 1 : 0;
+  }
+  return rank;
+}
+
+// Gates of row r: softmax of its 8 picked logits in pick order (zsel), one
+// thread, published with the row's IDs.
+__device__ __forceinline__ void publish_gates(const Ws& ws, int r, const float* zsel,
+                                              const int* ids) {
+  float mz = zsel[0];
+  for (int j = 1; j < 8; j++) mz = fmaxf(mz, zsel[j]);
+  float g[8], sum = 0.f;
+  for (int j = 0; j < 8; j++) {
+    g[j] = expf(zsel[j] - mz);
+    sum += g[j];
+  }
+  for (int j = 0; j < 8; j++) {
+    ws.gates[r * 8 + j] = g[j] / sum;
+    ws.ids[r * 8 + j] = ids[j];
+  }
+}
+
 // Runs with every thread of the block (it contains block barriers).  Fills
 // `rs` for rows 0..d.rows-1; when `publish`, also writes ids, gates and the
 // group table to the workspace.  KPL = key slots per lane, ceil(E / 64).
@@ -53,60 +142,8 @@ __device__ __forceinline__ void route_block(const Ws& ws, const Dims& d, RouteSm
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
   const int R = d.rows, E = d.E;
 
-  for (int r = wv; r < R; r += nw) {
-    const float* z = ws.logits + (size_t)r * E;
-    float zv[KPL];
-#pragma unroll
-    for (int i = 0; i < KPL; i++) {
-      const int e = lane + kWave * i;
-      zv[i] = z[e < E ? e : E - 1];  // lanes past E load in bounds, key 0 below
-    }
-    uint32_t key[KPL];
-#pragma unroll
-    for (int i = 0; i < KPL; i++) key[i] = (lane + kWave * i < E) ? topk_vkey(zv[i]) : 0u;
-
-    // T: the largest t with at least 8 keys >= t (E >= 16 real keys, all >= 1)
-    uint32_t t = 0;
-    int nge = 0;
-    for (int b = 31; b >= 0; b--) {
-      const uint32_t c = t | (1u << b);
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < KPL; i++) cnt += __popcll(__ballot(key[i] >= c));
-      if (cnt >= 8) {
-        t = c;
-        nge = cnt;
-        if (cnt == 8) break;
-      }
-    }
-    // picks: keys above T, then ties at T by increasing expert ID
-    int need = 8;
-    if (nge > 8) {
-      int ngt = 0;
-#pragma unroll
-      for (int i = 0; i < KPL; i++) ngt += __popcll(__ballot(key[i] > t));
-      need = 8 - ngt;
-    }
-    int ties = 0, base = 0;
-#pragma unroll
-    for (int i = 0; i < KPL; i++) {
-      bool take;
-      if (nge == 8) {
-        take = key[i] >= t;
-      } else {
-        const uint64_t tb = __ballot(key[i] == t);
-        take = key[i] > t || (key[i] == t && ties + lanes_below(tb) < need);
-        ties += __popcll(tb);
-      }
-      const uint64_t sb = __ballot(take);
-      if (take) {
-        const int pos = base + lanes_below(sb);
-        rs.ckey[r][pos] = key[i];
-        rs.cid[r][pos] = lane + kWave * i;
-      }
-      base += __popcll(sb);
-    }
-  }
+  for (int r = wv; r < R; r += nw)
+    select8<KPL>(ws.logits + (size_t)r * E, E, lane, rs.ckey[r], rs.cid[r]);
   if (tid < 64) {
     rs.g_mask[tid] = 0u;
 #pragma unroll
@@ -118,34 +155,14 @@ __device__ __forceinline__ void route_block(const Ws& ws, const Dims& d, RouteSm
   // key and a lower ID
   if (tid < 8 * R) {
     const int r = tid >> 3, j = tid & 7;
-    const uint32_t k = rs.ckey[r][j];
-    const int id = rs.cid[r][j];
-    int rank = 0;
-#pragma unroll
-    for (int m = 0; m < 8; m++) {
-      const uint32_t km = rs.ckey[r][m];
-      rank += (km > k || (km == k && rs.cid[r][m] < id)) ? 1 : 0;
-    }
-    rs.ids[r][rank] = id;
-    rs.zsel[r][rank] = topk_vkey_value(k);
+    const int rank = rank8(rs.ckey[r], rs.cid[r], j);
+    rs.ids[r][rank] = rs.cid[r][j];
+    rs.zsel[r][rank] = topk_vkey_value(rs.ckey[r][j]);
   }
   __syncthreads();
 
   // gates: softmax of a row's 8 picked logits, in pick order
-  if (publish && tid < R) {
-    const int r = tid;
-    float mz = rs.zsel[r][0];
-    for (int j = 1; j < 8; j++) mz = fmaxf(mz, rs.zsel[r][j]);
-    float g[8], sum = 0.f;
-    for (int j = 0; j < 8; j++) {
-      g[j] = expf(rs.zsel[r][j] - mz);
-      sum += g[j];
-    }
-    for (int j = 0; j < 8; j++) {
-      ws.gates[r * 8 + j] = g[j] / sum;
-      ws.ids[r * 8 + j] = rs.ids[r][j];
-    }
-  }
+  if (publish && tid < R) publish_gates(ws, tid, rs.zsel[tid], rs.ids[tid]);
 
   // dedup: lane p holds pick p in slot-major order (p = j*R + r).  Lanes with
   // the same expert are found with one ballot per ID bit; the lowest of them

@@ -212,7 +212,7 @@ __device__ __forceinline__ void ug_fp4(const Weights& w, const Ws& ws, const Dim
 
 template <int RF, int P, int P4>
 __global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims d) {
-  __shared__ uint8_t s_tile[4][2][kTileBytes];  // per wave: gate and up weight tiles
+  __shared__ __align__(16) uint8_t s_tile[4][2][kTileBytes];  // per wave: gate and up weight tiles
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int KS = d.ks;
   const int spb = 4 / KS;  // slabs per block
