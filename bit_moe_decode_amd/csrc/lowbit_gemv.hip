@@ -63,136 +63,155 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_kernel(const uint8_t* __re
   }
 }
 
-// Table-lookup form, for many rows (the LM head) and K a multiple of 256 (an
-// even number of groups: a row is a whole number of 36-byte, dword-aligned
-// pairs of groups).  Block = RW waves = 64*RW rows, one per lane.  The block's
-// rows are one contiguous run of bytes; they are staged into LDS with
-// coalesced 16-byte loads (a lane reading its own row straight from memory
-// would touch a different cache line per lane).  Then for each chunk of 256
-// inputs (two groups, 32 byte positions) the block fills an LDS table with,
-// for every byte position p and byte value v, the signed sum of its 8 inputs:
-//   T[p][v] = sum_{i<8} (bit i of v ? -x : +x)[256c + 8p + i]
-// (a thread fills one position's values for some of the top bits, from pair
-// sums), and each lane adds T[p][byte] over the 16 bytes of each group of its
-// row -- one table read per 8 weights instead of 8 masked adds -- scales by
-// the group's d and accumulates in fp32.
-constexpr int kLbLutBytes = 32 * 256 * 4;
-constexpr int kLbStageMax = 96 * 1024;
+// Nibble-table form, for K a multiple of 256 (an even number of groups: a row
+// is a whole number of 36-byte, dword-aligned pairs of groups).  Block = 256
+// threads = RB rows x KP = 256/RB parts of K.  The block's rows are one
+// contiguous run of bytes; they are staged into LDS with coalesced 16-byte
+// loads (a lane reading its own row straight from memory would touch a
+// different cache line per lane).  K is taken in chunks of 256 inputs (two
+// groups, 64 positions of 4 inputs); in each round the block fills, for KP
+// chunks at once, a table of the signed sums of every position's 4 inputs
+// for all 16 nibble values,
+//   T[p][v] = sum_{i<4} (bit i of v ? -x : +x)[256c + 4p + i],
+// and thread (row r, part q) adds T[p][nibble] over the 64 nibbles of chunk
+// c = round * KP + q of its row, scales each group's sum by its d and
+// accumulates in fp32: one table read per 4 weights.  The parts of a row are
+// added in part order at the end.  The lanes of a wave read one position's
+// 16 entries at a time (a broadcast or a distinct bank each), and the tables
+// of different parts are offset by 16 floats so that they use different banks.
+constexpr int kLbStageMax = 64 * 1024;
+constexpr int kLbTab = 64 * 16 + 16;  // floats per chunk table, padded
 
-__device__ __forceinline__ float lb_bf16(uint32_t w, int hi) {
-  return bf16_to_f32((uint16_t)(hi ? (w >> 16) : (w & 0xFFFFu)));
-}
 __device__ __forceinline__ float lb_f16(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-template <int RW>
-__global__ __launch_bounds__(64 * RW) void lowbit_gemv_q1_lut_kernel(
+template <int RB>
+__global__ __launch_bounds__(256) void lowbit_gemv_q1_nib_kernel(
     const uint8_t* __restrict__ blocks, const uint16_t* __restrict__ x,
     uint16_t* __restrict__ y, int n, int k) {
-  constexpr int NT = 64 * RW;        // threads = rows per block
-  constexpr int VPT = 256 * 32 / NT;  // table values per thread per chunk
+  constexpr int KP = 256 / RB;
   extern __shared__ __align__(16) uint8_t smem[];
-  float(*lut)[256] = reinterpret_cast<float(*)[256]>(smem);
-  uint8_t* stage = smem + kLbLutBytes;
+  float* tab = reinterpret_cast<float*>(smem);                    // [KP][kLbTab]
+  float* red = tab + KP * kLbTab;                                  // [KP][RB]
+  uint8_t* stage = reinterpret_cast<uint8_t*>(red + KP * RB);      // the block's rows
   const int tid = threadIdx.x;
   const int G = k / 128, nch = G / 2, rb = 18 * G;
-  const int r0 = blockIdx.x * NT;
-  const int nr = n - r0 < NT ? n - r0 : NT;
+  const int r0 = blockIdx.x * RB;
+  const int nr = n - r0 < RB ? n - r0 : RB;
 
   // ---- stage the block's rows: [r0 * rb, (r0 + nr) * rb), 16-byte aligned
-  // start (64 rows are 1152 * G bytes); a tail shorter than 16 bytes goes by
-  // 2-byte loads, so nothing past the matrix is read
+  // start (RB rows are a multiple of 16 bytes); a tail shorter than 16 bytes
+  // goes by 2-byte loads, so nothing past the matrix is read
   {
     const uint8_t* src = blocks + (size_t)r0 * rb;
     const int bytes = nr * rb, n16 = bytes >> 4;
-    for (int i0 = tid; i0 < n16; i0 += 8 * NT) {  // 8 loads in flight per thread
+    for (int i0 = tid; i0 < n16; i0 += 8 * 256) {  // 8 loads in flight per thread
       u32x4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; u++)
-        if (i0 + u * NT < n16) v[u] = ld_nt16(src + 16 * (i0 + u * NT));
+        if (i0 + u * 256 < n16) v[u] = ld_nt16(src + 16 * (i0 + u * 256));
 #pragma unroll
       for (int u = 0; u < 8; u++)
-        if (i0 + u * NT < n16) *reinterpret_cast<u32x4*>(stage + 16 * (i0 + u * NT)) = v[u];
+        if (i0 + u * 256 < n16) *reinterpret_cast<u32x4*>(stage + 16 * (i0 + u * 256)) = v[u];
     }
     const int tail = bytes - 16 * n16;  // even
     if (tid < (tail >> 1))
       *reinterpret_cast<uint16_t*>(stage + 16 * n16 + 2 * tid) =
           *reinterpret_cast<const uint16_t*>(src + 16 * n16 + 2 * tid);
   }
-  const int rowl = tid < nr ? tid : nr - 1;  // lanes past n decode the last row
+  const int rl = tid % RB, part = tid / RB;
+  const int rowl = rl < nr ? rl : nr - 1;  // threads past n decode the last row
   const uint32_t* myrow = reinterpret_cast<const uint32_t*>(stage + rowl * rb);
-  // table role: byte position bp, values v = vb * VPT .. + VPT
-  const int bp = tid / (256 / VPT), vb = tid % (256 / VPT);
+  const float* mytab = tab + part * kLbTab;
 
   float acc = 0.f;
-  for (int c = 0; c < nch; c++) {
-    {
-      const u32x4 xv = ld16(x + 256 * c + 8 * bp);
-      float xs[8];
+  for (int c0 = 0; c0 < nch; c0 += KP) {
+    // ---- tables of chunks c0 .. c0 + KP - 1: one position (4 inputs) a thread
+    for (int e = tid; e < KP * 64; e += 256) {
+      const int cs = e >> 6, pos = e & 63, c = c0 + cs;
+      if (c < nch) {
+        const uint2 xv = *reinterpret_cast<const uint2*>(x + 256 * c + 4 * pos);
+        const float x0 = bf16_to_f32((uint16_t)(xv.x & 0xFFFFu)), x1 = bf16_to_f32((uint16_t)(xv.x >> 16));
+        const float x2 = bf16_to_f32((uint16_t)(xv.y & 0xFFFFu)), x3 = bf16_to_f32((uint16_t)(xv.y >> 16));
+        // bits 0-1 and bits 2-3 of the nibble
+        const float a0 = x0 + x1, a1 = -x0 + x1, a2 = x0 - x1, a3 = -x0 - x1;
+        const float b0 = x2 + x3, b1 = -x2 + x3, b2 = x2 - x3, b3 = -x2 - x3;
+        float* t = tab + cs * kLbTab + pos * 16;
+        const float bv[4] = {b0, b1, b2, b3};
 #pragma unroll
-      for (int i = 0; i < 8; i++) xs[i] = lb_bf16(xv[i >> 1], i & 1);
-      // values v = vb * VPT + 16 q + m: pair sums over bits 0..3, bits 4..7 added
-      float ab[16];
-#pragma unroll
-      for (int m = 0; m < 16; m++)
-        ab[m] = ((m & 1) ? -xs[0] : xs[0]) + ((m & 2) ? -xs[1] : xs[1]) +
-                ((m & 4) ? -xs[2] : xs[2]) + ((m & 8) ? -xs[3] : xs[3]);
-      float* dst = &lut[bp][vb * VPT];
-#pragma unroll
-      for (int q = 0; q < VPT / 16; q++) {
-        const int hi = vb * VPT + 16 * q;  // bits 4..7 of v
-        float hs = 0.f;
-#pragma unroll
-        for (int i = 4; i < 8; i++) hs += ((hi >> i) & 1) ? -xs[i] : xs[i];
-#pragma unroll
-        for (int m = 0; m < 16; m += 4)
-          *reinterpret_cast<float4*>(dst + 16 * q + m) =
-              float4{ab[m] + hs, ab[m + 1] + hs, ab[m + 2] + hs, ab[m + 3] + hs};
+        for (int hb = 0; hb < 4; hb++)
+          *reinterpret_cast<float4*>(t + 4 * hb) =
+              float4{a0 + bv[hb], a1 + bv[hb], a2 + bv[hb], a3 + bv[hb]};
       }
     }
-    __syncthreads();  // (the first pass also waits for the staged rows)
-    uint32_t w[9];
+    __syncthreads();  // (the first round also waits for the staged rows)
+    const int c = c0 + part;
+    if (c < nch) {
+      uint32_t w[9];
 #pragma unroll
-    for (int i = 0; i < 9; i++) w[i] = myrow[9 * c + i];
-    float s0 = 0.f, s1 = 0.f;
+      for (int i = 0; i < 9; i++) w[i] = myrow[9 * c + i];
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const int b0 = 2 + j, b1 = 20 + j;  // bits of group 2c and of group 2c+1
-      s0 += lut[j][(w[b0 >> 2] >> (8 * (b0 & 3))) & 0xFFu];
-      s1 += lut[16 + j][(w[b1 >> 2] >> (8 * (b1 & 3))) & 0xFFu];
+      for (int j = 0; j < 16; j++) {
+        const int b0 = 2 + j, b1 = 20 + j;  // bits of group 2c and of group 2c+1
+        const uint32_t v0 = (w[b0 >> 2] >> (8 * (b0 & 3))) & 0xFFu;
+        const uint32_t v1 = (w[b1 >> 2] >> (8 * (b1 & 3))) & 0xFFu;
+        s0 += mytab[(2 * j) * 16 + (v0 & 15u)] + mytab[(2 * j + 1) * 16 + (v0 >> 4)];
+        s1 += mytab[(32 + 2 * j) * 16 + (v1 & 15u)] + mytab[(33 + 2 * j) * 16 + (v1 >> 4)];
+      }
+      acc = fmaf(lb_f16(w[0] & 0xFFFFu), s0, acc);
+      acc = fmaf(lb_f16(w[4] >> 16), s1, acc);
     }
-    acc = fmaf(lb_f16(w[0] & 0xFFFFu), s0, acc);
-    acc = fmaf(lb_f16(w[4] >> 16), s1, acc);
     __syncthreads();
   }
-  if (tid < nr) y[r0 + tid] = f32_to_bf16(acc);
+  red[part * RB + rl] = acc;
+  __syncthreads();
+  if (tid < nr) {
+    float v = red[tid];
+#pragma unroll
+    for (int q = 1; q < KP; q++) v += red[q * RB + tid];
+    y[r0 + tid] = f32_to_bf16(v);
+  }
+}
+
+static size_t lb_nib_lds(int rbk, int rb) {
+  return (size_t)(256 / rbk) * kLbTab * 4 + 256 * 4 + (size_t)rbk * rb;
+}
+
+template <int RB>
+static hipError_t lb_nib_launch(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n,
+                                int k, hipStream_t stream) {
+  const size_t sh = lb_nib_lds(RB, 18 * (k / 128));
+  static bool raised = false;
+  if (!raised) {
+    const int mx = (256 / RB) * kLbTab * 4 + 256 * 4 + kLbStageMax;  // lb_nib_lds at most
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(lowbit_gemv_q1_nib_kernel<RB>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, mx) != hipSuccess)
+      return hipErrorInvalidValue;
+    raised = true;
+  }
+  hipLaunchKernelGGL(lowbit_gemv_q1_nib_kernel<RB>, dim3((n + RB - 1) / RB), dim3(256), sh,
+                     stream, blocks, x, y, n, k);
+  return hipGetLastError();
 }
 
 hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
                             hipStream_t stream) {
-  // many rows: the table form, 128 rows a block where they fit the staging
-  // area, else 64
+  // the nibble-table form: rows per block the largest of 128, 64, 32, 16 that
+  // still gives 256 blocks (or 16), whose rows fit the staging area
   const int rb = 18 * (k / 128);
-  if (n >= 16384 && k % 256 == 0 && 64 * rb <= kLbStageMax) {
-    static const bool attrs = [] {
-      const int mx = kLbLutBytes + kLbStageMax;
-      return hipFuncSetAttribute(reinterpret_cast<const void*>(lowbit_gemv_q1_lut_kernel<2>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, mx) == hipSuccess &&
-             hipFuncSetAttribute(reinterpret_cast<const void*>(lowbit_gemv_q1_lut_kernel<1>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, mx) == hipSuccess;
-    }();
-    if (!attrs) return hipErrorInvalidValue;
-    if (128 * rb <= kLbStageMax) {
-      const size_t sh = kLbLutBytes + 128 * rb;
-      hipLaunchKernelGGL(lowbit_gemv_q1_lut_kernel<2>, dim3((n + 127) / 128), dim3(128), sh,
-                         stream, blocks, x, y, n, k);
-    } else {
-      const size_t sh = kLbLutBytes + 64 * rb;
-      hipLaunchKernelGGL(lowbit_gemv_q1_lut_kernel<1>, dim3((n + 63) / 64), dim3(64), sh, stream,
-                         blocks, x, y, n, k);
+  if (k % 256 == 0) {
+    int rbk = 128;
+    while (rbk > 16 && ((n + rbk - 1) / rbk < 256 || rbk * rb > kLbStageMax)) rbk >>= 1;
+    if (rbk * rb <= kLbStageMax) {
+      switch (rbk) {
+        case 128: return lb_nib_launch<128>(blocks, x, y, n, k, stream);
+        case 64: return lb_nib_launch<64>(blocks, x, y, n, k, stream);
+        case 32: return lb_nib_launch<32>(blocks, x, y, n, k, stream);
+        default: return lb_nib_launch<16>(blocks, x, y, n, k, stream);
+      }
     }
-    return hipGetLastError();
   }
   int rows_blocks = (n + 3) / 4;
   int grid = rows_blocks < 1024 ? rows_blocks : 1024;
