@@ -82,8 +82,75 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_kernel(const uint8_t* __re
 constexpr int kLbStageMax = 64 * 1024;
 constexpr int kLbTab = 64 * 16 + 16;  // floats per chunk table, padded
 
+// Bits o .. o+3 of v as one v_bfe_u32 (the compiler would otherwise split a
+// constant-offset field extract into a shift and a mask).
+template <int O>
+__device__ __forceinline__ uint32_t nib4_at(uint32_t v) {
+  uint32_t r;
+  asm("v_bfe_u32 %0, %1, %2, 4" : "=v"(r) : "v"(v), "n"(O));
+  return r;
+}
+__device__ __forceinline__ uint32_t nib4(uint32_t v, int o) {
+  switch (o) {
+    case 0: return nib4_at<0>(v);
+    case 4: return nib4_at<4>(v);
+    case 8: return nib4_at<8>(v);
+    case 12: return nib4_at<12>(v);
+    case 16: return nib4_at<16>(v);
+    case 20: return nib4_at<20>(v);
+    case 24: return nib4_at<24>(v);
+    default: return v >> 28;
+  }
+}
+
 __device__ __forceinline__ float lb_f16(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// One chunk (two groups) of a row: w = its 9 dwords (d of group 0, 16 bit
+// bytes, d of group 1, 16 bit bytes), tab = the chunk's 64 positions x 16
+// entries.  Returns acc + d0 * s0 + d1 * s1, s = the sum of the entries of
+// the group's 32 nibbles.
+__device__ __forceinline__ float lb_chunk(const uint32_t* wp, const float* tab, float acc) {
+  uint32_t w[9];
+#pragma unroll
+  for (int i = 0; i < 9; i++) w[i] = wp[i];
+  // the 16 bit-bytes of each group as 4 aligned dwords (group 0 starts 2
+  // bytes in)
+  uint32_t u[8];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    u[q] = __builtin_amdgcn_alignbyte(w[q + 1], w[q], 2);
+    u[4 + q] = w[5 + q];
+  }
+  // nibble t of dword q is the 4 inputs of position 8(q%4) + t of its group;
+  // its entry is float `nibble` of that position's 16
+  const float* tg[2] = {tab, tab + 32 * 16};
+  float s[2] = {0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+      const int pos = 8 * (q & 3) + t;
+      const uint32_t n0 = nib4(u[q], 4 * t), n1 = nib4(u[q], 4 * t + 4);
+      s[q >> 2] += tg[q >> 2][pos * 16 + n0] + tg[q >> 2][pos * 16 + 16 + n1];
+    }
+  }
+  acc = fmaf(lb_f16(w[0] & 0xFFFFu), s[0], acc);
+  return fmaf(lb_f16(w[4] >> 16), s[1], acc);
+}
+
+// The 16 entries of one position, t[v] = sum_{i<4} (bit i of v ? -x : +x)[i],
+// from its 4 bf16 inputs (packed in xv, input 0 in the low half of xv.x).
+__device__ __forceinline__ void lb_fill_pos(float* t, uint2 xv) {
+  const float x0 = bf16_to_f32((uint16_t)(xv.x & 0xFFFFu)), x1 = bf16_to_f32((uint16_t)(xv.x >> 16));
+  const float x2 = bf16_to_f32((uint16_t)(xv.y & 0xFFFFu)), x3 = bf16_to_f32((uint16_t)(xv.y >> 16));
+  // bits 0-1 and bits 2-3 of the nibble
+  const float a0 = x0 + x1, a1 = -x0 + x1, a2 = x0 - x1, a3 = -x0 - x1;
+  const float b[4] = {x2 + x3, -x2 + x3, x2 - x3, -x2 - x3};
+#pragma unroll
+  for (int hb = 0; hb < 4; hb++)
+    *reinterpret_cast<float4*>(t + 4 * hb) = float4{a0 + b[hb], a1 + b[hb], a2 + b[hb], a3 + b[hb]};
 }
 
 template <int RB>
@@ -125,44 +192,32 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_nib_kernel(
   const uint32_t* myrow = reinterpret_cast<const uint32_t*>(stage + rowl * rb);
   const float* mytab = tab + part * kLbTab;
 
+  // table positions of this thread in a round: e = tid + 256 j (j < NE), the
+  // inputs of each loaded one round ahead
+  constexpr int NE = KP >= 4 ? KP / 4 : 1;
+  uint2 xn[NE];
+  auto xload = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < NE; j++) {
+      const int e = tid + 256 * j;
+      if (e < KP * 64 && c0 + (e >> 6) < nch)
+        xn[j] = *reinterpret_cast<const uint2*>(x + 256 * c0 + 4 * e);
+    }
+  };
+  xload(0);
   float acc = 0.f;
   for (int c0 = 0; c0 < nch; c0 += KP) {
-    // ---- tables of chunks c0 .. c0 + KP - 1: one position (4 inputs) a thread
-    for (int e = tid; e < KP * 64; e += 256) {
-      const int cs = e >> 6, pos = e & 63, c = c0 + cs;
-      if (c < nch) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(x + 256 * c + 4 * pos);
-        const float x0 = bf16_to_f32((uint16_t)(xv.x & 0xFFFFu)), x1 = bf16_to_f32((uint16_t)(xv.x >> 16));
-        const float x2 = bf16_to_f32((uint16_t)(xv.y & 0xFFFFu)), x3 = bf16_to_f32((uint16_t)(xv.y >> 16));
-        // bits 0-1 and bits 2-3 of the nibble
-        const float a0 = x0 + x1, a1 = -x0 + x1, a2 = x0 - x1, a3 = -x0 - x1;
-        const float b0 = x2 + x3, b1 = -x2 + x3, b2 = x2 - x3, b3 = -x2 - x3;
-        float* t = tab + cs * kLbTab + pos * 16;
-        const float bv[4] = {b0, b1, b2, b3};
+    // ---- tables of chunks c0 .. c0 + KP - 1: one position (4 inputs) at a time
 #pragma unroll
-        for (int hb = 0; hb < 4; hb++)
-          *reinterpret_cast<float4*>(t + 4 * hb) =
-              float4{a0 + bv[hb], a1 + bv[hb], a2 + bv[hb], a3 + bv[hb]};
-      }
+    for (int j = 0; j < NE; j++) {
+      const int e = tid + 256 * j;
+      if (e < KP * 64 && c0 + (e >> 6) < nch)
+        lb_fill_pos(tab + (e >> 6) * kLbTab + (e & 63) * 16, xn[j]);
     }
+    if (c0 + KP < nch) xload(c0 + KP);
     __syncthreads();  // (the first round also waits for the staged rows)
     const int c = c0 + part;
-    if (c < nch) {
-      uint32_t w[9];
-#pragma unroll
-      for (int i = 0; i < 9; i++) w[i] = myrow[9 * c + i];
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const int b0 = 2 + j, b1 = 20 + j;  // bits of group 2c and of group 2c+1
-        const uint32_t v0 = (w[b0 >> 2] >> (8 * (b0 & 3))) & 0xFFu;
-        const uint32_t v1 = (w[b1 >> 2] >> (8 * (b1 & 3))) & 0xFFu;
-        s0 += mytab[(2 * j) * 16 + (v0 & 15u)] + mytab[(2 * j + 1) * 16 + (v0 >> 4)];
-        s1 += mytab[(32 + 2 * j) * 16 + (v1 & 15u)] + mytab[(33 + 2 * j) * 16 + (v1 >> 4)];
-      }
-      acc = fmaf(lb_f16(w[0] & 0xFFFFu), s0, acc);
-      acc = fmaf(lb_f16(w[4] >> 16), s1, acc);
-    }
+    if (c < nch) acc = lb_chunk(myrow + 9 * c, mytab, acc);
     __syncthreads();
   }
   red[part * RB + rl] = acc;
@@ -199,11 +254,11 @@ static hipError_t lb_nib_launch(const uint8_t* blocks, const uint16_t* x, uint16
 hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
                             hipStream_t stream) {
   // the nibble-table form: rows per block the largest of 128, 64, 32, 16 that
-  // still gives 256 blocks (or 16), whose rows fit the staging area
+  // still gives 2048 blocks (or 16), whose rows fit the staging area
   const int rb = 18 * (k / 128);
   if (k % 256 == 0) {
     int rbk = 128;
-    while (rbk > 16 && ((n + rbk - 1) / rbk < 256 || rbk * rb > kLbStageMax)) rbk >>= 1;
+    while (rbk > 16 && ((n + rbk - 1) / rbk < 2048 || rbk * rb > kLbStageMax)) rbk >>= 1;
     if (rbk * rb <= kLbStageMax) {
       switch (rbk) {
         case 128: return lb_nib_launch<128>(blocks, x, y, n, k, stream);
