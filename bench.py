@@ -10,8 +10,9 @@ copies of the layer's weights are rotated step by step so that no step finds
 another step's weights in the 256 MB MALL or the L2s; a pool of 16 token rows
 varies the routing.
 
-One step = one moe_decode_step call (router, routing, up/gate, mid, down and
-combine kernels).  Value =
+One step = one moe_decode_step call: router, routing (up to 4 rows with the
+shared expert's up/gate beside it), up/gate (with mid), down (with the mid
+quantisation) and combine kernels.  Value =
 algorithmic bytes of the step (each distinct expert counted once, read from
 the step's own dedup table, plus the shared expert, router, gamma, x and out)
 divided by the step time, timed over back-to-back steps.  The same steps are
@@ -63,9 +64,13 @@ def step_bytes(layer, rows, d):
 
 
 def upgate_bytes(layer, rows, d):
+    """Algorithmic bytes of one up/gate launch: the D distinct experts' gate
+    and up matrices, the activation codes and scales, and above 4 rows the
+    shared expert's gate and up (up to 4 rows the library runs those beside
+    the routing, in the routing launch)."""
     H, I, Is = layer.hidden, layer.inter, layer.shared_inter
-    return (d * 2 * routed_matrix_bytes(layer, I, H) + (2 * fp8_matrix_bytes(Is, H) if Is else 0)
-            + rows * H + rows * (H // 128) * 4)
+    shared = 2 * fp8_matrix_bytes(Is, H) if (Is and rows > 4) else 0
+    return d * 2 * routed_matrix_bytes(layer, I, H) + shared + rows * H + rows * (H // 128) * 4
 
 
 def layer_copies(S, base, n):

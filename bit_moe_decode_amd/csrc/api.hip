@@ -10,7 +10,7 @@
 namespace moe {
 hipError_t launch_router(const uint16_t* x, const Weights& w, const Ws& ws, const Dims& d,
                          hipStream_t stream);
-hipError_t launch_route(const Ws& ws, const Dims& d, hipStream_t stream);
+hipError_t launch_route(const Weights& w, const Ws& ws, const Dims& d, hipStream_t stream);
 hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& ws,
                          const Dims& d, hipStream_t stream);
 hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws, const Dims& d,
@@ -221,7 +221,8 @@ moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
   if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (launch_router(x, wt, ctx->view, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (launch_route(ctx->view, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
+  // routing, with the shared expert's up/gate alongside
+  if (launch_route(wt, ctx->view, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_ERR_DEVICE;
   // groups this step can produce: at most 8 * rows (and E with dedup)
   const int picks = 8 * rows;

@@ -253,19 +253,22 @@ static hipError_t lb_nib_launch(const uint8_t* blocks, const uint16_t* x, uint16
 
 hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
                             hipStream_t stream) {
-  // the nibble-table form: rows per block the largest of 128, 64, 32, 16 that
-  // still gives 2048 blocks (or 16), whose rows fit the staging area
+  // the nibble-table form: rows per block the largest of 128, 64, 32 that
+  // gives 2048 blocks, else the largest that gives 256, else 16, among those
+  // whose rows fit the staging area
   const int rb = 18 * (k / 128);
-  if (k % 256 == 0) {
-    int rbk = 128;
-    while (rbk > 16 && ((n + rbk - 1) / rbk < 2048 || rbk * rb > kLbStageMax)) rbk >>= 1;
-    if (rbk * rb <= kLbStageMax) {
-      switch (rbk) {
-        case 128: return lb_nib_launch<128>(blocks, x, y, n, k, stream);
-        case 64: return lb_nib_launch<64>(blocks, x, y, n, k, stream);
-        case 32: return lb_nib_launch<32>(blocks, x, y, n, k, stream);
-        default: return lb_nib_launch<16>(blocks, x, y, n, k, stream);
-      }
+  if (k % 256 == 0 && 16 * rb <= kLbStageMax) {
+    int rbk = 16;
+    for (int want : {2048, 256}) {
+      for (int c = 128; c >= 32 && rbk == 16; c >>= 1)
+        if ((n + c - 1) / c >= want && c * rb <= kLbStageMax) rbk = c;
+      if (rbk != 16) break;
+    }
+    switch (rbk) {
+      case 128: return lb_nib_launch<128>(blocks, x, y, n, k, stream);
+      case 64: return lb_nib_launch<64>(blocks, x, y, n, k, stream);
+      case 32: return lb_nib_launch<32>(blocks, x, y, n, k, stream);
+      default: return lb_nib_launch<16>(blocks, x, y, n, k, stream);
     }
   }
   int rows_blocks = (n + 3) / 4;

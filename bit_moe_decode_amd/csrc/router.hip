@@ -4,8 +4,9 @@
 // #85 Mod. row 10: the router multiplies u = bf16(x * gamma) (the product is
 // exact in fp32, rounded once) and scales each row's dots by its rstd; the
 // same u, quantised per 1x128 block, is the activation of the up/gate GEMV,
-// whose results take the rstd afterwards.  moe_route_kernel then derives the
-// top-8, gates and dedup table from these logits in one block (route.h).
+// whose results take the rstd afterwards.  moe_route_kernel (upgate.hip) then
+// derives the top-8, gates and dedup table from these logits in one block
+// (route.h).
 //
 // Grid E/EB blocks of 16 waves.  A block owns EB experts (4, or 2 above 4
 // rows) over the whole hidden
@@ -16,7 +17,7 @@
 // the block in a fixed order, so every block derives the same rstd.  Each
 // 128-block of activations is quantised by one block of the grid (kb modulo
 // the grid), from the 16 lanes that hold it: s = amax/448, q = e4m3(u/s).
-#include "route.h"
+#include "device_common.h"
 
 namespace moe {
 
@@ -148,25 +149,6 @@ __global__ __launch_bounds__(1024) void moe_router_kernel(const uint16_t* __rest
     for (int i = 0; i < kRtWaves * 4; i++) a += s_dot[i][e][r];
     ws.logits[(size_t)r * E + e0 + e] = s_rstd[r] * a;
   }
-}
-
-// The step's routing decisions (top-8, gates, dedup table) from the logits,
-// in one block of 8 waves (one row per wave), published to the workspace.
-template <int KPL>
-__global__ __launch_bounds__(512) void moe_route_kernel(Ws ws, Dims d) {
-  __shared__ RouteSmem rs;
-  route_block<KPL>(ws, d, rs, true);
-}
-
-hipError_t launch_route(const Ws& ws, const Dims& d, hipStream_t stream) {
-  // key slots per lane of the top-8: 4, 8 or 16 (E <= 256, 512, 1024)
-  if (d.E <= 256)
-    hipLaunchKernelGGL(moe_route_kernel<4>, dim3(1), dim3(512), 0, stream, ws, d);
-  else if (d.E <= 512)
-    hipLaunchKernelGGL(moe_route_kernel<8>, dim3(1), dim3(512), 0, stream, ws, d);
-  else
-    hipLaunchKernelGGL(moe_route_kernel<16>, dim3(1), dim3(512), 0, stream, ws, d);
-  return hipGetLastError();
 }
 
 hipError_t launch_router(const uint16_t* x, const Weights& w, const Ws& ws, const Dims& d,

@@ -10,8 +10,11 @@
 // stays FP8.
 //
 // Block = 4 waves = 4/ks slabs of 16 intermediate rows x ks parts of K; the
-// grid lists the shared expert's slabs, then I/16 slabs for each of the step's
-// possible routed groups (blocks of groups past the step's D exit at once).
+// blocks are numbered over the shared expert's slabs, then I/16 slabs for each
+// of the step's possible routed groups (blocks of groups past the step's D
+// exit at once).  For steps of up to 4 rows the shared expert's blocks run
+// beside the routing block in moe_route_kernel; the routed ones (and else the
+// shared ones too) in moe_upgate_kernel.
 // Many small blocks let the hardware dispatcher even out the load per CU.
 // A wave loads its 16 weight rows of gate and of up row-contiguously (8 lanes
 // read one row's 128-byte line), re-lays them through LDS into MFMA operand
@@ -31,7 +34,7 @@
 //    and the 32 inputs 32*(l/16) .. +32 of the K block as 16 bytes, low nibble
 //    first, with the E8M0 of those 32 as its scale; B lane l holds column l%16
 //    and the FP8 inputs 16*(l/16) .. +16 and 64 + 16*(l/16) .. +16.
-#include "device_common.h"
+#include "route.h"
 
 namespace moe {
 
@@ -210,9 +213,13 @@ __device__ __forceinline__ void ug_fp4(const Weights& w, const Ws& ws, const Dim
   for (int p = 0; p < P; p++) consume(st[p]);
 }
 
+typedef uint8_t UgTiles[4][2][kTileBytes];  // per wave: gate and up weight tiles
+
+// Up/gate block number `blk` of the numbering above (the shared expert's
+// slabs, then those of each routed group), with 256 threads.
 template <int RF, int P, int P4>
-__global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims d) {
-  __shared__ __align__(16) uint8_t s_tile[4][2][kTileBytes];  // per wave: gate and up weight tiles
+__device__ __forceinline__ void upgate_block(const Weights& w, const Ws& ws, const Dims& d,
+                                             int blk, UgTiles& s_tile) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int KS = d.ks;
   const int spb = 4 / KS;  // slabs per block
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims 
 
   // ---- the block's expert and slab
   const int nb_sh = d.Is / (16 * spb);
-  int b = blockIdx.x, g = -1, nrows, row, e;
+  int b = blk, g = -1, nrows, row, e;
   uint64_t rows8 = 0, picks8 = 0;  // using rows, and the pick of each row (routed)
   if (b < nb_sh) {
     nrows = d.rows;
@@ -281,6 +288,40 @@ __global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims 
   }
 }
 
+// Up/gate blocks base, base + 1, ... (base = 0: the shared expert's slabs and
+// the routed groups'; base = Is/BR: the routed groups' only).
+template <int RF, int P, int P4>
+__global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims d, int base) {
+  __shared__ __align__(16) UgTiles s_tile;
+  upgate_block<RF, P, P4>(w, ws, d, base + blockIdx.x, s_tile);
+}
+
+// Steps of up to 4 rows: the step's routing decisions (top-8, gates, dedup
+// table; route.h) in block 0, and the shared expert's up/gate slabs in blocks
+// 1 .. Is/BR.  The shared expert needs only the router's activation blocks and
+// rstd, so its weights stream while the routing, a latency-bound single
+// block, runs.  (With more rows the routing takes longer on 4 waves than the
+// shared expert saves: moe_route_only_kernel on 8 waves, and the shared
+// slabs go with the routed ones.)
+template <int KPL, int P>
+__global__ __launch_bounds__(256) void moe_route_kernel(Weights w, Ws ws, Dims d) {
+  __shared__ RouteSmem rs;
+  __shared__ __align__(16) UgTiles s_tile;
+  if (blockIdx.x == 0)
+    route_block<KPL>(ws, d, rs, true);
+  else
+    upgate_block<kFmtFp8, P, 1>(w, ws, d, blockIdx.x - 1, s_tile);
+}
+
+template <int KPL>
+__global__ __launch_bounds__(512) void moe_route_only_kernel(Ws ws, Dims d) {
+  __shared__ RouteSmem rs;
+  route_block<KPL>(ws, d, rs, true);
+}
+
+// Whether the shared expert's up/gate runs in the routing launch.
+bool shared_with_route(const Dims& d) { return d.rows <= 4 && d.Is > 0; }
+
 // Items in flight per wave: the largest of 4, 2, 1 (3, 2, 1 for MXFP4 items)
 // that divides the wave's items.
 static int ring_depth(int nk) { return nk % 4 == 0 ? 4 : (nk % 2 == 0 ? 2 : 1); }
@@ -293,37 +334,71 @@ int upgate_k_parts(int hidden, int routed_fmt) {
   return n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1);
 }
 
+template <int RF, int P, int P4>
+static void launch_one(dim3 grid, int base, const Weights& w, const Ws& ws, const Dims& d,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL((moe_upgate_kernel<RF, P, P4>), grid, dim3(256), 0, stream, w, ws, d, base);
+}
+
 template <int RF, int P>
-static void launch_p4(int p4, dim3 grid, const Weights& w, const Ws& ws, const Dims& d,
-                      hipStream_t stream) {
+static void launch_p4(int p4, dim3 grid, int base, const Weights& w, const Ws& ws,
+                      const Dims& d, hipStream_t stream) {
   switch (p4) {
-    case 3: hipLaunchKernelGGL((moe_upgate_kernel<RF, P, 3>), grid, dim3(256), 0, stream, w, ws, d); break;
-    case 2: hipLaunchKernelGGL((moe_upgate_kernel<RF, P, 2>), grid, dim3(256), 0, stream, w, ws, d); break;
-    default: hipLaunchKernelGGL((moe_upgate_kernel<RF, P, 1>), grid, dim3(256), 0, stream, w, ws, d); break;
+    case 3: launch_one<RF, P, 3>(grid, base, w, ws, d, stream); break;
+    case 2: launch_one<RF, P, 2>(grid, base, w, ws, d, stream); break;
+    default: launch_one<RF, P, 1>(grid, base, w, ws, d, stream); break;
   }
 }
 
 hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& ws,
                          const Dims& d, hipStream_t stream) {
   const int br = 16 * (4 / d.ks);
-  const dim3 grid(d.Is / br + max_groups * (d.I / br));
+  const int nb_sh = d.Is / br, base = shared_with_route(d) ? nb_sh : 0;
+  const dim3 grid(nb_sh - base + max_groups * (d.I / br));
   const int p = ring_depth(d.H / 128 / d.ks);
   if (rfmt == kFmtFp8) {
     switch (p) {
-      case 4: hipLaunchKernelGGL((moe_upgate_kernel<kFmtFp8, 4, 1>), grid, dim3(256), 0, stream, w, ws, d); break;
-      case 2: hipLaunchKernelGGL((moe_upgate_kernel<kFmtFp8, 2, 1>), grid, dim3(256), 0, stream, w, ws, d); break;
-      default: hipLaunchKernelGGL((moe_upgate_kernel<kFmtFp8, 1, 1>), grid, dim3(256), 0, stream, w, ws, d); break;
+      case 4: launch_one<kFmtFp8, 4, 1>(grid, base, w, ws, d, stream); break;
+      case 2: launch_one<kFmtFp8, 2, 1>(grid, base, w, ws, d, stream); break;
+      default: launch_one<kFmtFp8, 1, 1>(grid, base, w, ws, d, stream); break;
     }
   } else if (rfmt == kFmtMxfp4) {
     const int p4 = ring_depth4(d.H / 256 / d.ks);
     switch (p) {
-      case 4: launch_p4<kFmtMxfp4, 4>(p4, grid, w, ws, d, stream); break;
-      case 2: launch_p4<kFmtMxfp4, 2>(p4, grid, w, ws, d, stream); break;
-      default: launch_p4<kFmtMxfp4, 1>(p4, grid, w, ws, d, stream); break;
+      case 4: launch_p4<kFmtMxfp4, 4>(p4, grid, base, w, ws, d, stream); break;
+      case 2: launch_p4<kFmtMxfp4, 2>(p4, grid, base, w, ws, d, stream); break;
+      default: launch_p4<kFmtMxfp4, 1>(p4, grid, base, w, ws, d, stream); break;
     }
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+template <int KPL>
+static void launch_route_k(int p, const Weights& w, const Ws& ws, const Dims& d,
+                           hipStream_t stream) {
+  if (!shared_with_route(d)) {
+    hipLaunchKernelGGL((moe_route_only_kernel<KPL>), dim3(1), dim3(512), 0, stream, ws, d);
+    return;
+  }
+  const dim3 grid(1 + d.Is / (16 * (4 / d.ks)));
+  switch (p) {
+    case 4: hipLaunchKernelGGL((moe_route_kernel<KPL, 4>), grid, dim3(256), 0, stream, w, ws, d); break;
+    case 2: hipLaunchKernelGGL((moe_route_kernel<KPL, 2>), grid, dim3(256), 0, stream, w, ws, d); break;
+    default: hipLaunchKernelGGL((moe_route_kernel<KPL, 1>), grid, dim3(256), 0, stream, w, ws, d); break;
+  }
+}
+
+hipError_t launch_route(const Weights& w, const Ws& ws, const Dims& d, hipStream_t stream) {
+  const int p = ring_depth(d.H / 128 / d.ks);
+  // key slots per lane of the top-8: 4, 8 or 16 (E <= 256, 512, 1024)
+  if (d.E <= 256)
+    launch_route_k<4>(p, w, ws, d, stream);
+  else if (d.E <= 512)
+    launch_route_k<8>(p, w, ws, d, stream);
+  else
+    launch_route_k<16>(p, w, ws, d, stream);
   return hipGetLastError();
 }
 

@@ -166,7 +166,8 @@ moe_status moe_decode_debug_view(const moe_decode_ctx* ctx, moe_decode_debug* vi
  * records events[0] before its first kernel and events[i+1] after kernel i
  * (MOE_DECODE_N_KERNELS kernels), on the step's stream.  The caller owns the
  * events (hipEventCreate) and must keep them alive; pass NULL to stop. */
-#define MOE_DECODE_N_KERNELS 5 /* router, routing, up/gate + mid, down, combine */
+#define MOE_DECODE_N_KERNELS 5 /* router, routing (+ the shared expert's up/gate up to 4
+                                  rows), up/gate + mid, down, combine */
 moe_status moe_decode_set_timing(moe_decode_ctx* ctx, hipEvent_t* events);
 
 void moe_decode_destroy(moe_decode_ctx* ctx);
