@@ -29,12 +29,11 @@
 // (row, pick) belongs to exactly one expert of the step, so no two writes
 // collide.
 //
-// MXFP4 routed experts (mid kept in fp32, as the oracle does): a VALU path in
-// the same blocks, one mid column at a time.  Per K chunk of 512 the block
-// stages the column's fp32 mid in LDS (4 pad floats per 32, so the 4 lanes of
-// a row read disjoint banks); each 16-byte run of weights -- 32 inputs, one
-// E8M0 block -- is decoded with the hardware FP4 -> fp32 conversion scaled by
-// 2^(E8M0-127) and multiplied into an fp32 sum.
+// MXFP4 routed experts (mid kept in fp32, as the oracle does): the block
+// splits its columns' mid into bf16 hi + lo (mid = hi + lo to about 2^-17) in
+// LDS; a wave converts each 32 inputs of E2M1 weights (one E8M0 block) to bf16
+// with the hardware's scaled conversion and runs two 16x16x32 bf16 MFMAs, one
+// against hi and one against lo, accumulating in fp32.
 //
 // moe_combine_kernel:
 //   out[r][h] = bf16( sum_{j<8} g_rj * y_rj[h] + y_r8[h] )
@@ -105,10 +104,7 @@ __device__ __forceinline__ void dn_quant_mid(const Ws& ws, const Dims& d, int nr
   }
 }
 
-constexpr int kDnChunk = 512;                  // K inputs per staged mid chunk (MXFP4)
-constexpr int kDnMidStride = kDnChunk + kDnChunk / 8;  // 4 pad floats per 32
-
-typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
 
 // 2^(e-127) as fp32 for an E8M0 code (0xFF, NaN, is not produced by the
 // generator; it decodes to a NaN here as well).
@@ -119,82 +115,114 @@ __device__ __forceinline__ float e8m0_scale(uint32_t e) {
   return __uint_as_float(b);
 }
 
-// The MXFP4 down GEMV of one block: 64 output rows of routed expert e against
-// its nrows mid columns u_c (fp32, unquantised), one column at a time.  Lane l
-// takes row hb + 16*wave + l/4 and, of each staged K chunk, the 16-byte runs
-// 16(l%4) + 64i (32 inputs, one E8M0 block each); the 4 lanes of a row are
-// summed at the end.
-__device__ __forceinline__ void down_fp4_block(const Weights& w, const Ws& ws, const Dims& d,
-                                               int e, int nrows, const DnCols& cols, int hb,
-                                               float* s_mid) {
-  constexpr int R = kDnChunk / 128;  // runs of a lane per chunk
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int H = d.H, I = d.I;
+// LDS of an MXFP4 block's mid columns: per column, K bf16 "hi" values then K
+// bf16 "lo" values (mid = hi + lo to about 2^-17), the column stride padded by
+// 32 bytes so that the columns of one MFMA read start on different banks.
+__host__ __device__ inline int dn4_col_stride(int inter) { return 4 * inter + 32; }
+__host__ __device__ inline size_t dn4_lds_bytes(int rows, int inter) {
+  return (size_t)rows * dn4_col_stride(inter);
+}
+
+// 16x16x32 bf16 MFMA, fp32 accumulate.  A: lane l holds row l%16, K
+// 8*(l/16) .. +8; B: lane l holds column l%16, same K; D: lane l holds rows
+// 4*(l/16)+v of column l%16 (layout checked on the device).
+__device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// The MXFP4 down GEMV of one wave: 16 output rows h0 .. h0+15 of routed
+// expert e over the whole K, against the block's nrows mid columns (fp32 mid,
+// unquantised, split into bf16 hi + lo in LDS by the block).  Item k = the
+// 128 inputs 128k .. +128 of the 16 rows (64 bytes a row): lane L loads row
+// L/4, 16-byte chunk L%4, re-laid through the wave's LDS tile; then per 32
+// inputs (one E8M0 block) lane l converts 8 E2M1 of row l%16 to bf16 scaled
+// by 2^(E8M0-127) (v_cvt_scalef32_pk_bf16_fp4) and runs two bf16 MFMAs, one
+// against the hi and one against the lo parts of mid.
+template <int P>
+__device__ __forceinline__ void down_fp4_wave(const Weights& w, const Dims& d, int e, int nrows,
+                                              int h0, uint8_t* tile, const uint8_t* smid,
+                                              float* acc) {
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+  const int H = d.H, I = d.I, nki = I / 128;
   const size_t rbytes = I / 2;
-  const int h = hb + wv * 16 + (lane >> 2), q = lane & 3;
-  const uint8_t* wrow = w.down_c + ((size_t)e * H + h) * rbytes;
-  const uint8_t* erow = reinterpret_cast<const uint8_t*>(w.down_s) + ((size_t)e * H + h) * (I / 32);
-#pragma unroll 1
-  for (int c = 0; c < nrows; c++) {
-    const int uc = cols.u(c);
-    const float* mcol = ws.mid + (size_t)uc * d.imax;
-    float a = 0.f;
-#pragma unroll 1
-    for (int k0 = 0; k0 < I; k0 += kDnChunk) {
-      const int kc = I - k0 < kDnChunk ? I - k0 : kDnChunk;  // a multiple of 128
-      const int nrun = kc / 128;
-      u32x4 wq[R];
-      uint32_t ev[R];
+  const uint8_t* wrow = w.down_c + ((size_t)e * H + h0 + (lane >> 2)) * rbytes + (lane & 3) * 16;
+  const uint8_t* erow =
+      reinterpret_cast<const uint8_t*>(w.down_s) + ((size_t)e * H + h0 + col) * (I / 32);
+  const int cc = col < nrows ? col : 0;  // columns past the rows reuse column 0
+  const uint8_t* mh = smid + cc * dn4_col_stride(I) + 16 * g;  // hi of K 8g.. of a 32-step
+  const uint8_t* ml = mh + 2 * I;                               // lo
+  struct It {
+    u32x4 w;
+    uint32_t e;
+  };
+  auto issue = [&](It& s, int k) {
+    s.w = ld_nt16(wrow + (size_t)k * 64);
+    s.e = *reinterpret_cast<const uint32_t*>(erow + 4 * k);
+  };
+  v4f c = {acc[0], acc[1], acc[2], acc[3]};
+  auto consume = [&](It& s, int k) {
+    *reinterpret_cast<u32x4*>(tile + (lane >> 2) * kTileStride + (lane & 3) * 16) = s.w;
+    asm volatile("" ::: "memory");
 #pragma unroll
-      for (int i = 0; i < R; i++)
-        if (i < nrun) {
-          const int byte = k0 / 2 + 64 * i + 16 * q;
-          wq[i] = ld_nt16(wrow + byte);
-          ev[i] = erow[byte / 16];
-        }
-      __syncthreads();  // the previous chunk's readers are done
-      for (int f4 = tid; f4 < kc / 4; f4 += 256)
-        *reinterpret_cast<v4f*>(s_mid + 4 * f4 + (f4 / 8) * 4) =
-            *reinterpret_cast<const v4f*>(mcol + k0 + 4 * f4);
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < R; i++) {
-        if (i >= nrun) break;
-        const float sc = e8m0_scale(ev[i]);
-        const int kl = 128 * i + 32 * q;  // first input of the run within the chunk
-        const float* mp = s_mid + kl + (kl / 32) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {  // 8 inputs per dword of codes
-          const v2f_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wq[i][j], sc, 0);
-          const v2f_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wq[i][j], sc, 1);
-          const v2f_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wq[i][j], sc, 2);
-          const v2f_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wq[i][j], sc, 3);
-          const v4f m0 = *reinterpret_cast<const v4f*>(mp + 8 * j);
-          const v4f m1 = *reinterpret_cast<const v4f*>(mp + 8 * j + 4);
-          a = fmaf(p0[0], m0[0], a);
-          a = fmaf(p0[1], m0[1], a);
-          a = fmaf(p1[0], m0[2], a);
-          a = fmaf(p1[1], m0[3], a);
-          a = fmaf(p2[0], m1[0], a);
-          a = fmaf(p2[1], m1[1], a);
-          a = fmaf(p3[0], m1[2], a);
-          a = fmaf(p3[1], m1[3], a);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // one run decoded at a time
-      }
+    for (int st = 0; st < 4; st++) {
+      const uint32_t a4 = *reinterpret_cast<const uint32_t*>(tile + col * kTileStride + 16 * st + 4 * g);
+      const float sc = e8m0_scale((s.e >> (8 * st)) & 0xFFu);
+      const v2bf_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4, sc, 0);
+      const v2bf_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4, sc, 1);
+      const v2bf_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4, sc, 2);
+      const v2bf_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4, sc, 3);
+      const v8bf a = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      const int ko = 2 * (128 * k + 32 * st);
+      const v8bf bh = *reinterpret_cast<const v8bf*>(mh + ko);
+      const v8bf bl = *reinterpret_cast<const v8bf*>(ml + ko);
+      c = mfma_bf16(a, bh, c);
+      c = mfma_bf16(a, bl, c);
     }
-    // sum over the 4 lanes of the row (xor 1, xor 2 within quads)
-    a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xF, 0xF, false));
-    a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF, false));
-    if (q == 0) ws.ypart[(size_t)uc * H + h] = a;
+    asm volatile("" ::: "memory");
+  };
+  // ring of P items (P divides I/128): every issued load is used
+  It st[P];
+#pragma unroll
+  for (int p = 0; p < P; p++) issue(st[p], p);
+  for (int k0 = 0; k0 < nki - P; k0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+      consume(st[p], k0 + p);
+      issue(st[p], k0 + P + p);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; p++) consume(st[p], nki - P + p);
+  acc[0] = c[0];
+  acc[1] = c[1];
+  acc[2] = c[2];
+  acc[3] = c[3];
+}
+
+// The block's mid columns as bf16 hi + lo: hi = bf16(m), lo = bf16(m - hi)
+// (m - hi is exact in fp32), 4 values a thread per pass.
+__device__ __forceinline__ void dn4_split_mid(const Ws& ws, const Dims& d, int nrows,
+                                              const DnCols& cols, uint8_t* smid) {
+  const int I = d.I, n4 = I / 4;
+  for (int t = threadIdx.x; t < nrows * n4; t += blockDim.x) {
+    const int c = t / n4, k = 4 * (t - c * n4);
+    const v4f m = *reinterpret_cast<const v4f*>(ws.mid + (size_t)cols.u(c) * d.imax + k);
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      hi[i] = f32_to_bf16(m[i]);
+      lo[i] = f32_to_bf16(m[i] - bf16_to_f32(hi[i]));
+    }
+    uint8_t* p = smid + c * dn4_col_stride(I) + 2 * k;
+    *reinterpret_cast<uint2*>(p) = uint2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
+    *reinterpret_cast<uint2*>(p + 2 * I) =
+        uint2{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
   }
 }
 
 template <int RF, int P, int WPB>
 __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Dims d) {
-  static_assert(RF != kFmtMxfp4 || WPB == 4, "the MXFP4 path takes blocks of 4 waves");
   __shared__ __align__(16) uint8_t s_tile[WPB][kTileBytes];
-  __shared__ __align__(16) float s_mid[RF == kFmtMxfp4 ? kDnMidStride : 1];
   extern __shared__ __align__(16) uint8_t dyn[];  // dn_lds_bytes(rows, I)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = d.H, I = d.I, nkb = I / 128;
@@ -223,7 +251,18 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
   }
   const DnCols cols{g, rows8, picks8};
   if (RF == kFmtMxfp4 && g >= 0) {
-    down_fp4_block(w, ws, d, e, nrows, cols, b * 64, s_mid);
+    // MXFP4 routed expert: mid columns split into bf16 hi + lo in LDS while
+    // the first weight items are in flight (issued inside down_fp4_wave after
+    // the barrier below; the split is short next to the stream)
+    dn4_split_mid(ws, d, nrows, cols, dyn);
+    __syncthreads();
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const int h0 = b * 16 * WPB + wv * 16;
+    down_fp4_wave<P>(w, d, e, nrows, h0, s_tile[wv], dyn, acc);
+    pin4(acc);
+    if (col < nrows)
+      *reinterpret_cast<v4f*>(ws.ypart + (size_t)cols.u(col) * H + h0 + 4 * (lane >> 4)) =
+          v4f{acc[0], acc[1], acc[2], acc[3]};
     return;
   }
   const int cc = col < nrows ? col : 0;  // columns past the rows reuse column 0
@@ -357,7 +396,8 @@ static hipError_t launch_rf(int max_groups, size_t lds, const Weights& w, const 
 
 hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws, const Dims& d,
                        hipStream_t stream) {
-  const size_t lds = dn_lds_bytes(d.rows, d.I);
+  size_t lds = dn_lds_bytes(d.rows, d.I);
+  if (rfmt == kFmtMxfp4 && dn4_lds_bytes(d.rows, d.I) > lds) lds = dn4_lds_bytes(d.rows, d.I);
   if (rfmt == kFmtFp8) return launch_rf<kFmtFp8>(max_groups, lds, w, ws, d, stream);
   if (rfmt == kFmtMxfp4) return launch_rf<kFmtMxfp4>(max_groups, lds, w, ws, d, stream);
   return hipErrorInvalidValue;
