@@ -22,8 +22,11 @@ trials of 50 steps.  Context figures: the step with one weight copy reused
 (hot), torch's copy of 2 GiB (read + write), lowbit_gemv against its VALU floor (one
 lane-op per weight), and the oracle on one thread with the host CPU model.  A second pass over
 the same steps has the library record HIP events around each kernel on the
-step's stream; the dominant kernel's (up/gate) average duration gives the
-roofline figure.  The fp64 CPU oracle is timed on the host for a bounded sample of the
+step's stream.  The roofline figure is the dominant kernel's (up/gate)
+algorithmic bytes over its average launch duration, timed by HIP events
+around 64 back-to-back relaunches of it (moe_decode_relaunch) after one step,
+each over another weight copy (an event pair per kernel inside a step adds
+about 3-5 us).  The fp64 CPU oracle is timed on the host for a bounded sample of the
 1-row workload.
 
 Prints one JSON line on stdout; progress goes to stderr.
@@ -42,6 +45,7 @@ PEAK_GBS = 8000.0  # MI355X HBM3E, published
 VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9  # fp32 lane-ops per second (157.3 TFLOP/s as FMAs)
 POOL = 16
 GSTEPS = 2 * POOL  # steps per captured graph
+RELAUNCH = 64  # back-to-back launches of one kernel for its average duration
 
 
 def log(*a):
@@ -204,6 +208,21 @@ def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base):
     runner.ctx.set_timing(None)
     kern = [sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(steps)) / steps
             for k in range(nk)]
+    # (d) the up/gate and down kernels alone: after one step, back-to-back
+    # relaunches over the other weight copies (the same experts at other
+    # addresses, so each streams from HBM), bracketed by two events
+    runner.ctx.step(pool[0], rows, weights[0], out, stream)
+    alone = {}
+    for name, kid in (("upgate", B.K_UPGATE), ("down", B.K_DOWN)):
+        runner.ctx.relaunch(kid, weights[1 % len(weights)], 1, stream)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(RELAUNCH):
+            runner.ctx.relaunch(kid, weights[(i + 2) % len(weights)], 1, stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        alone[name] = t0.elapsed_time(t1) * 1e3 / RELAUNCH
+    ug_alone_bytes = upgate_bytes(layer, rows, dvals[0])
     # (c) the same kind of steps captured once into a HIP graph and replayed:
     # GSTEPS steps per graph (every pool entry and weight copy), replayed back to back
     g = torch.cuda.CUDAGraph()
@@ -236,7 +255,8 @@ def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base):
     graph = dict(us_per_step=graph_ms * 1e3, gbs=gbytes / (graph_ms * 1e-3) / 1e9,
                  distinct_experts=gd)
     return dict(rows=rows, us_per_step=ms * 1e3, gbs=gbs, frac=gbs / PEAK_GBS, d_mean=d_mean,
-                graph=graph, us_per_step_protocol=proto_ms * 1e3,
+                graph=graph, us_per_step_protocol=proto_ms * 1e3, alone_us=alone,
+                upgate_alone_bytes=ug_alone_bytes,
                 bytes_per_step=nbytes,
                 kernel_us=kernel_us,
                 upgate_gbs=ug_gbs, upgate_bytes=ug_bytes, runner=runner, pool=pool,
@@ -443,10 +463,14 @@ def main():
                                "FP8 activations and mid, bf16 in/out",
                    "rows": main_rows, "layer_copies": ncopies, "x_pool": POOL},
         "roofline": {"bound": "hbm", "kernel": "moe_upgate_kernel",
-                     "achieved": round(m["upgate_gbs"], 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(m["upgate_gbs"] / PEAK_GBS, 4),
-                     "bytes_per_launch": int(m["upgate_bytes"]),
-                     "us_per_launch": round(m["kernel_us"]["upgate"], 2),
+                     "achieved": round(m["upgate_alone_bytes"] / (m["alone_us"]["upgate"] * 1e-6) / 1e9, 1),
+                     "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(m["upgate_alone_bytes"] / (m["alone_us"]["upgate"] * 1e-6) / 1e9
+                                   / PEAK_GBS, 4),
+                     "bytes_per_launch": int(m["upgate_alone_bytes"]),
+                     "us_per_launch": round(m["alone_us"]["upgate"], 2),
+                     "launches_timed": RELAUNCH,
+                     "us_per_launch_in_step_events": round(m["kernel_us"]["upgate"], 2),
                      "traffic": measured_traffic() if main_rows == 1 else None},
         "cpu_baseline": cpu,
         "oracle_check_out_err_rel_max": err,
@@ -456,6 +480,9 @@ def main():
                              "kernel_us": {k: round(t, 2) for k, t in v["kernel_us"].items()},
                              "upgate_gbs": round(v["upgate_gbs"], 1),
                              "us_per_step_median7x50_mean2": round(v["us_per_step_protocol"], 2),
+                             "kernel_alone_us": {k: round(t, 2) for k, t in v["alone_us"].items()},
+                             "upgate_alone_gbs": round(v["upgate_alone_bytes"]
+                                                       / (v["alone_us"]["upgate"] * 1e-6) / 1e9, 1),
                              "graph_replay": {k: round(t, 2) for k, t in v["graph"].items()}}
                     for r, v in results.items()},
         "hot_us_per_step": hot,

@@ -18,6 +18,7 @@ FMT_MXFP4 = 2
 FMT_Q1 = 3
 F_NO_DEDUP = 1 << 1
 N_KERNELS = 5
+K_UPGATE, K_DOWN = 2, 3  # kernels moe_decode_relaunch repeats
 KERNEL_NAMES = ("router", "route", "upgate", "down", "combine")  # launch order
 
 
@@ -83,6 +84,9 @@ def lib():
         L.moe_decode_debug_view.argtypes = [ctypes.c_void_p, ctypes.POINTER(Debug)]
         L.moe_decode_set_timing.restype = ctypes.c_int
         L.moe_decode_set_timing.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.moe_decode_relaunch.restype = ctypes.c_int
+        L.moe_decode_relaunch.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(Weights),
+                                          ctypes.c_int32, ctypes.c_void_p]
         L.moe_decode_destroy.restype = None
         L.moe_decode_destroy.argtypes = [ctypes.c_void_p]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -164,6 +168,17 @@ class Context:
             st = lib().moe_decode_set_timing(self.handle, ctypes.cast(arr, ctypes.c_void_p))
         if st != MOE_OK:
             raise MoeError(st, "moe_decode_set_timing")
+
+    def relaunch_status(self, kernel, weights: Weights, reps, stream=None):
+        return lib().moe_decode_relaunch(self.handle, int(kernel), ctypes.byref(weights), int(reps),
+                                         _stream(stream))
+
+    def relaunch(self, kernel, weights: Weights, reps, stream=None):
+        """Enqueue `reps` more launches of one kernel of the last step (K_UPGATE
+        or K_DOWN) with the weights `weights` (same experts, e.g. another copy)."""
+        st = self.relaunch_status(kernel, weights, reps, stream)
+        if st != MOE_OK:
+            raise MoeError(st, "moe_decode_relaunch")
 
     def close(self):
         if getattr(self, "handle", None):

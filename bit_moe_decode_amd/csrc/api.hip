@@ -111,6 +111,7 @@ struct moe_decode_ctx {
   Ws view;
   hipEvent_t events[MOE_DECODE_N_KERNELS + 1];
   bool timing;
+  int last_rows;  // rows of the last step enqueued, 0 before the first
 };
 
 extern "C" {
@@ -136,6 +137,7 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
   c->plan = p;
   c->ws = static_cast<char*>(workspace);
   c->timing = false;
+  c->last_rows = 0;
   char* b = c->ws;
   Ws& v = c->view;
   v.logits = reinterpret_cast<float*>(b + p.off_logits);
@@ -168,16 +170,13 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
   return MOE_OK;
 }
 
-moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
-                           const moe_decode_weights* w, uint16_t* out, hipStream_t stream) {
-  if (!ctx) return MOE_ERR_INVALID_ARG;
+namespace {
+// Validates the weights and fills the kernels' argument views for a step of
+// `rows` rows on this context.
+moe_status step_args(const moe_decode_ctx* ctx, int rows, const moe_decode_weights* w,
+                     Weights* wtp, Dims* dp) {
   const Plan& p = ctx->plan;
-  if (rows < 0 || rows > p.R) return MOE_ERR_INVALID_ARG;
-  if (rows == 0) return MOE_OK;
-  if (!x || !w || !out || !aligned16(x) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
-  const size_t bytes = (size_t)rows * p.H * 2;
-  const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out;
-  if (xa < oa + bytes && oa < xa + bytes) return MOE_ERR_INVALID_ARG;
+  if (!w) return MOE_ERR_INVALID_ARG;
   const void* need[] = {w->rms_gamma, w->router_w, w->gate.codes, w->gate.scales, w->up.codes,
                         w->up.scales, w->down.codes, w->down.scales};
   for (const void* q : need)
@@ -188,8 +187,7 @@ moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
     for (const void* q : sh)
       if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
   }
-
-  Weights wt;
+  Weights& wt = *wtp;
   wt.gamma = w->rms_gamma;
   wt.router = w->router_w;
   wt.gate_c = static_cast<const uint8_t*>(w->gate.codes);
@@ -205,7 +203,7 @@ moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
   wt.su_s = static_cast<const float*>(w->sh_up.scales);
   wt.sd_s = static_cast<const float*>(w->sh_down.scales);
 
-  Dims d;
+  Dims& d = *dp;
   d.H = p.H;
   d.I = p.I;
   d.E = p.E;
@@ -216,6 +214,31 @@ moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
   d.ks = p.ks;
   d.no_dedup = (ctx->cfg.flags & MOE_F_NO_DEDUP) ? 1 : 0;
   d.eps = ctx->cfg.rms_eps;
+  return MOE_OK;
+}
+
+// Groups a step of `rows` rows can produce: at most 8 * rows (and E with dedup).
+int step_groups(const Plan& p, const Dims& d) {
+  const int picks = 8 * d.rows;
+  return d.no_dedup ? picks : (picks < p.E ? picks : p.E);
+}
+}  // namespace
+
+moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
+                           const moe_decode_weights* w, uint16_t* out, hipStream_t stream) {
+  if (!ctx) return MOE_ERR_INVALID_ARG;
+  const Plan& p = ctx->plan;
+  if (rows < 0 || rows > p.R) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!x || !w || !out || !aligned16(x) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)rows * p.H * 2;
+  const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out;
+  if (xa < oa + bytes && oa < xa + bytes) return MOE_ERR_INVALID_ARG;
+  Weights wt;
+  Dims d;
+  const moe_status st = step_args(ctx, rows, w, &wt, &d);
+  if (st != MOE_OK) return st;
+  ctx->last_rows = rows;
 
   hipEvent_t* ev = ctx->timing ? ctx->events : nullptr;
   if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ERR_DEVICE;
@@ -224,9 +247,7 @@ moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
   // routing, with the shared expert's up/gate alongside
   if (launch_route(wt, ctx->view, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  // groups this step can produce: at most 8 * rows (and E with dedup)
-  const int picks = 8 * rows;
-  const int groups = d.no_dedup ? picks : (picks < p.E ? picks : p.E);
+  const int groups = step_groups(p, d);
   if (launch_upgate(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream) != hipSuccess)
     return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_ERR_DEVICE;
@@ -271,6 +292,25 @@ moe_status moe_decode_set_timing(moe_decode_ctx* ctx, hipEvent_t* events) {
     ctx->events[i] = events[i];
   }
   ctx->timing = true;
+  return MOE_OK;
+}
+
+moe_status moe_decode_relaunch(moe_decode_ctx* ctx, int32_t kernel,
+                               const moe_decode_weights* w, int32_t reps, hipStream_t stream) {
+  if (!ctx || reps < 0) return MOE_ERR_INVALID_ARG;
+  if (kernel != MOE_DECODE_K_UPGATE && kernel != MOE_DECODE_K_DOWN) return MOE_ERR_INVALID_ARG;
+  if (ctx->last_rows == 0) return MOE_ERR_INVALID_ARG;
+  Weights wt;
+  Dims d;
+  const moe_status st = step_args(ctx, ctx->last_rows, w, &wt, &d);
+  if (st != MOE_OK) return st;
+  const int groups = step_groups(ctx->plan, d);
+  for (int i = 0; i < reps; i++) {
+    const hipError_t e = kernel == MOE_DECODE_K_UPGATE
+                             ? launch_upgate(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream)
+                             : launch_down(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+  }
   return MOE_OK;
 }
 

@@ -170,6 +170,22 @@ moe_status moe_decode_debug_view(const moe_decode_ctx* ctx, moe_decode_debug* vi
                                   rows), up/gate + mid, down, combine */
 moe_status moe_decode_set_timing(moe_decode_ctx* ctx, hipEvent_t* events);
 
+/* Kernel timing without per-kernel events: enqueues `reps` more launches of
+ * one kernel of the last step enqueued on this context (the up/gate or the
+ * down GEMV), with that step's row count, routing table and activations in the
+ * workspace, and the weights `w` -- which must hold the same experts at
+ * possibly other addresses, e.g. another copy of the layer, so that repeated
+ * launches stream from HBM rather than from a cache.  The relaunched kernel
+ * rewrites the same workspace values (mid, or the down outputs); the step's
+ * output is not touched.  For measurement only (the caller brackets the
+ * launches with its own events).
+ * Returns MOE_ERR_INVALID_ARG without a previous step, for another kernel, for
+ * reps < 0 or for weights that step validation rejects. */
+#define MOE_DECODE_K_UPGATE 2
+#define MOE_DECODE_K_DOWN 3
+moe_status moe_decode_relaunch(moe_decode_ctx* ctx, int32_t kernel,
+                               const moe_decode_weights* w, int32_t reps, hipStream_t stream);
+
 void moe_decode_destroy(moe_decode_ctx* ctx);
 
 const char* moe_status_string(moe_status s);

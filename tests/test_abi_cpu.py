@@ -13,7 +13,8 @@ def test_library_exports_every_declared_function():
     names = B.declared_functions()
     assert set(names) >= {"moe_decode_init", "moe_decode_step", "lowbit_gemv",
                           "moe_decode_workspace_size", "moe_decode_debug_view",
-                          "moe_decode_destroy", "moe_status_string", "moe_decode_set_timing"}
+                          "moe_decode_destroy", "moe_status_string", "moe_decode_set_timing",
+                          "moe_decode_relaunch"}
     for n in names:
         assert hasattr(L, n), n
 

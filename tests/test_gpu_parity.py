@@ -174,3 +174,33 @@ def test_glm_dedup_off_is_bitwise_equal(glm):
     off = B.LayerRunner(glm, 8, flags=B.F_NO_DEDUP).run(x)
     torch.cuda.synchronize()
     assert torch.equal(on.view(torch.int16), off.view(torch.int16))
+
+
+def test_relaunch_rewrites_the_same_values(tiny):
+    """moe_decode_relaunch repeats the last step's up/gate or down with
+    another copy of the same weights: mid and the output are unchanged
+    bitwise; without a previous step, or for another kernel, it is refused."""
+    runner = B.LayerRunner(tiny, 4)
+    st = runner.ctx.relaunch_status(B.K_UPGATE, runner.weights, 1)
+    assert st == B.MOE_ERR_INVALID_ARG  # no step yet
+    x = S.make_x(3, tiny.hidden, seed=2600).cuda()
+    out = runner.run(x)
+    torch.cuda.synchronize()
+    before = runner.debug(3)
+    copy = S.Layer(tiny.shape, tiny.hidden, tiny.inter, tiny.n_experts, tiny.shared_inter,
+                   tiny.rms_eps, tiny.gamma.clone(), tiny.router_w.clone(),
+                   S.ExpertWeights(tiny.routed.fmt, *[tuple(t.clone() for t in m) for m in
+                                                      (tiny.routed.gate, tiny.routed.up,
+                                                       tiny.routed.down)]), None)
+    wc = B.LayerRunner.weights_for(copy)
+    runner.ctx.relaunch(B.K_UPGATE, wc, 3)
+    runner.ctx.relaunch(B.K_DOWN, wc, 2)
+    torch.cuda.synchronize()
+    after = runner.debug(3)
+    for k in ("mid", "midq", "midqs", "ids", "gates"):
+        assert np.array_equal(before[k], after[k]), k
+    assert runner.ctx.relaunch_status(0, wc, 1) == B.MOE_ERR_INVALID_ARG
+    assert runner.ctx.relaunch_status(B.K_UPGATE, wc, -1) == B.MOE_ERR_INVALID_ARG
+    assert runner.ctx.relaunch_status(B.K_UPGATE, wc, 0) == B.MOE_OK
+    out2 = runner.run(x)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
