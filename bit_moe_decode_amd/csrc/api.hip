@@ -55,8 +55,11 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   if (c->max_rows < 1 || c->max_rows > 8) return MOE_ERR_INVALID_ARG;
   if (c->routed_fmt != MOE_FMT_FP8_E4M3_B128 && c->routed_fmt != MOE_FMT_MXFP4)
     return MOE_ERR_UNSUPPORTED;
-  // MXFP4 up/gate items are two K blocks wide
-  if (c->routed_fmt == MOE_FMT_MXFP4 && c->hidden % 256) return MOE_ERR_UNSUPPORTED;
+  // MXFP4 up/gate items are two K blocks wide; the down GEMV keeps its
+  // columns' mid split into bf16 hi + lo in LDS (4 bytes an element, up to 8
+  // columns): I <= 4096
+  if (c->routed_fmt == MOE_FMT_MXFP4 && (c->hidden % 256 || c->inter > 4096))
+    return MOE_ERR_UNSUPPORTED;
   if (c->shared_inter > 0 && c->shared_fmt != MOE_FMT_FP8_E4M3_B128) return MOE_ERR_UNSUPPORTED;
   if (c->flags & ~kKnownFlags) return MOE_ERR_UNSUPPORTED;
   if (!(c->rms_eps >= 0.0f) || c->rms_eps > 1.0f) return MOE_ERR_INVALID_ARG;

@@ -63,7 +63,8 @@ typedef enum {
   /* MXFP4: E2M1 codes packed two per byte, element 2i in the low nibble,
    * uint8 [N, K/2], with one E8M0 exponent per 32 elements along K, uint8
    * [N, K/32] (MXFP4 page; #85 Mod. row 1: MXFP4 experts).  Routed experts
-   * only; their mid is kept in fp32 (not re-quantised). */
+   * only; their mid is kept in fp32 (not re-quantised).  Needs hidden % 256
+   * == 0 and inter <= 4096. */
   MOE_FMT_MXFP4 = 2,
   /* 1-bit group-128: [N, K/128] blocks of 18 bytes, an fp16 scale d
    * (little-endian) then 16 bytes of sign bits; bit i of byte b is element

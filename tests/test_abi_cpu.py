@@ -38,6 +38,7 @@ def test_workspace_size_supported_shapes():
 @pytest.mark.parametrize("kw", [dict(top_k=4), dict(hidden=6100), dict(inter=100),
                                 dict(n_experts=24), dict(n_experts=2048), dict(shared_inter=64),
                                 dict(routed_fmt=B.FMT_Q1), dict(shared_fmt=B.FMT_MXFP4),
+                                dict(routed_fmt=B.FMT_MXFP4, inter=4224, shared_inter=4224),
                                 dict(flags=1 << 7), dict(hidden=32768), dict(max_rows=9),
                                 dict(max_rows=0)])
 def test_unsupported_configs(kw):
