@@ -65,10 +65,11 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_kernel(const uint8_t* __re
 
 // Nibble-table form, for K a multiple of 256 (an even number of groups: a row
 // is a whole number of 36-byte, dword-aligned pairs of groups).  Block = 256
-// threads = RB rows x KP = 256/RB parts of K.  The block's rows are one
-// contiguous run of bytes; they are staged into LDS with coalesced 16-byte
-// loads (a lane reading its own row straight from memory would touch a
-// different cache line per lane).  K is taken in chunks of 256 inputs (two
+// threads = RB rows x KP = 256/RB parts of K.  Each thread reads the 36
+// bytes of its row's chunk straight from memory at the start of a round (the
+// lanes of a load touch one line per row, and the L2 keeps the block's rows
+// between rounds; staging the rows through LDS first measured slower, 23.5
+// against 21.4 us on the LM head).  K is taken in chunks of 256 inputs (two
 // groups, 64 positions of 4 inputs); in each round the block fills, for KP
 // chunks at once, a table of the signed sums of every position's 4 inputs
 // for all 16 nibble values,
@@ -79,7 +80,6 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_kernel(const uint8_t* __re
 // added in part order at the end.  The lanes of a wave read one position's
 // 16 entries at a time (a broadcast or a distinct bank each), and the tables
 // of different parts are offset by 16 floats so that they use different banks.
-constexpr int kLbStageMax = 64 * 1024;
 constexpr int kLbTab = 64 * 16 + 16;  // floats per chunk table, padded
 
 // Bits o .. o+3 of v as one v_bfe_u32 (the compiler would otherwise split a
@@ -111,10 +111,7 @@ __device__ __forceinline__ float lb_f16(uint32_t h) {
 // bytes, d of group 1, 16 bit bytes), tab = the chunk's 64 positions x 16
 // entries.  Returns acc + d0 * s0 + d1 * s1, s = the sum of the entries of
 // the group's 32 nibbles.
-__device__ __forceinline__ float lb_chunk(const uint32_t* wp, const float* tab, float acc) {
-  uint32_t w[9];
-#pragma unroll
-  for (int i = 0; i < 9; i++) w[i] = wp[i];
+__device__ __forceinline__ float lb_chunk(const uint32_t* w, const float* tab, float acc) {
   // the 16 bit-bytes of each group as 4 aligned dwords (group 0 starts 2
   // bytes in)
   uint32_t u[8];
@@ -161,35 +158,14 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_nib_kernel(
   extern __shared__ __align__(16) uint8_t smem[];
   float* tab = reinterpret_cast<float*>(smem);                    // [KP][kLbTab]
   float* red = tab + KP * kLbTab;                                  // [KP][RB]
-  uint8_t* stage = reinterpret_cast<uint8_t*>(red + KP * RB);      // the block's rows
   const int tid = threadIdx.x;
   const int G = k / 128, nch = G / 2, rb = 18 * G;
   const int r0 = blockIdx.x * RB;
   const int nr = n - r0 < RB ? n - r0 : RB;
 
-  // ---- stage the block's rows: [r0 * rb, (r0 + nr) * rb), 16-byte aligned
-  // start (RB rows are a multiple of 16 bytes); a tail shorter than 16 bytes
-  // goes by 2-byte loads, so nothing past the matrix is read
-  {
-    const uint8_t* src = blocks + (size_t)r0 * rb;
-    const int bytes = nr * rb, n16 = bytes >> 4;
-    for (int i0 = tid; i0 < n16; i0 += 8 * 256) {  // 8 loads in flight per thread
-      u32x4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; u++)
-        if (i0 + u * 256 < n16) v[u] = ld_nt16(src + 16 * (i0 + u * 256));
-#pragma unroll
-      for (int u = 0; u < 8; u++)
-        if (i0 + u * 256 < n16) *reinterpret_cast<u32x4*>(stage + 16 * (i0 + u * 256)) = v[u];
-    }
-    const int tail = bytes - 16 * n16;  // even
-    if (tid < (tail >> 1))
-      *reinterpret_cast<uint16_t*>(stage + 16 * n16 + 2 * tid) =
-          *reinterpret_cast<const uint16_t*>(src + 16 * n16 + 2 * tid);
-  }
   const int rl = tid % RB, part = tid / RB;
   const int rowl = rl < nr ? rl : nr - 1;  // threads past n decode the last row
-  const uint32_t* myrow = reinterpret_cast<const uint32_t*>(stage + rowl * rb);
+  const uint32_t* myrow = reinterpret_cast<const uint32_t*>(blocks + (size_t)(r0 + rowl) * rb);
   const float* mytab = tab + part * kLbTab;
 
   // table positions of this thread in a round: e = tid + 256 j (j < NE), the
@@ -207,6 +183,12 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_nib_kernel(
   xload(0);
   float acc = 0.f;
   for (int c0 = 0; c0 < nch; c0 += KP) {
+    // this thread's chunk of its row, loaded before the table fill
+    uint32_t w9[9];
+    if (c0 + part < nch) {
+#pragma unroll
+      for (int i = 0; i < 9; i++) w9[i] = myrow[9 * (c0 + part) + i];
+    }
     // ---- tables of chunks c0 .. c0 + KP - 1: one position (4 inputs) at a time
 #pragma unroll
     for (int j = 0; j < NE; j++) {
@@ -215,9 +197,8 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_nib_kernel(
         lb_fill_pos(tab + (e >> 6) * kLbTab + (e & 63) * 16, xn[j]);
     }
     if (c0 + KP < nch) xload(c0 + KP);
-    __syncthreads();  // (the first round also waits for the staged rows)
-    const int c = c0 + part;
-    if (c < nch) acc = lb_chunk(myrow + 9 * c, mytab, acc);
+    __syncthreads();
+    if (c0 + part < nch) acc = lb_chunk(w9, mytab, acc);
     __syncthreads();
   }
   red[part * RB + rl] = acc;
@@ -230,19 +211,16 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_nib_kernel(
   }
 }
 
-static size_t lb_nib_lds(int rbk, int rb) {
-  return (size_t)(256 / rbk) * kLbTab * 4 + 256 * 4 + (size_t)rbk * rb;
-}
+static size_t lb_nib_lds(int rbk) { return (size_t)(256 / rbk) * kLbTab * 4 + 256 * 4; }
 
 template <int RB>
 static hipError_t lb_nib_launch(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n,
                                 int k, hipStream_t stream) {
-  const size_t sh = lb_nib_lds(RB, 18 * (k / 128));
+  const size_t sh = lb_nib_lds(RB);
   static bool raised = false;
-  if (!raised) {
-    const int mx = (256 / RB) * kLbTab * 4 + 256 * 4 + kLbStageMax;  // lb_nib_lds at most
+  if (!raised && sh > 65536) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(lowbit_gemv_q1_nib_kernel<RB>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, mx) != hipSuccess)
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh) != hipSuccess)
       return hipErrorInvalidValue;
     raised = true;
   }
@@ -254,14 +232,12 @@ static hipError_t lb_nib_launch(const uint8_t* blocks, const uint16_t* x, uint16
 hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
                             hipStream_t stream) {
   // the nibble-table form: rows per block the largest of 128, 64, 32 that
-  // gives 2048 blocks, else the largest that gives 256, else 16, among those
-  // whose rows fit the staging area
-  const int rb = 18 * (k / 128);
-  if (k % 256 == 0 && 16 * rb <= kLbStageMax) {
+  // gives 2048 blocks, else the largest that gives 256, else 16
+  if (k % 256 == 0) {
     int rbk = 16;
     for (int want : {2048, 256}) {
       for (int c = 128; c >= 32 && rbk == 16; c >>= 1)
-        if ((n + c - 1) / c >= want && c * rb <= kLbStageMax) rbk = c;
+        if ((n + c - 1) / c >= want) rbk = c;
       if (rbk != 16) break;
     }
     switch (rbk) {

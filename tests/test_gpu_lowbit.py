@@ -86,6 +86,6 @@ def test_lowbit_zero_rows_and_zero_n():
 
 @pytest.mark.parametrize("n,k", [(16384, 256), (16385, 768), (20000, 5632)])
 def test_lowbit_table_form_edges(n, k):
-    """The table form's limits: its smallest row count, a ragged last block,
-    and a K where only 64 rows fit the staging area."""
+    """The table form's edges: one chunk of K, a ragged last block of rows,
+    and an odd number of chunks with 64-row blocks."""
     _check(n, k, seed=n + k)
