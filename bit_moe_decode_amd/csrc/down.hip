@@ -141,7 +141,7 @@ __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f
 template <int P>
 __device__ __forceinline__ void down_fp4_wave(const Weights& w, const Dims& d, int e, int nrows,
                                               int h0, uint8_t* tile, const uint8_t* smid,
-                                              float* acc) {
+                                              const float* e8tab, float* acc) {
   const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
   const int H = d.H, I = d.I, nki = I / 128;
   const size_t rbytes = I / 2;
@@ -166,7 +166,7 @@ __device__ __forceinline__ void down_fp4_wave(const Weights& w, const Dims& d, i
 #pragma unroll
     for (int st = 0; st < 4; st++) {
       const uint32_t a4 = *reinterpret_cast<const uint32_t*>(tile + col * kTileStride + 16 * st + 4 * g);
-      const float sc = e8m0_scale((s.e >> (8 * st)) & 0xFFu);
+      const float sc = e8tab[__builtin_amdgcn_ubfe(s.e, 8 * st, 8)];
       const v2bf_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4, sc, 0);
       const v2bf_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4, sc, 1);
       const v2bf_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4, sc, 2);
@@ -223,6 +223,8 @@ __device__ __forceinline__ void dn4_split_mid(const Ws& ws, const Dims& d, int n
 template <int RF, int P, int WPB>
 __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Dims d) {
   __shared__ __align__(16) uint8_t s_tile[WPB][kTileBytes];
+  __shared__ float s_e8tab[RF == kFmtMxfp4 ? 256 : 1];  // 2^(e-127) for each E8M0 code
+  static_assert(RF != kFmtMxfp4 || WPB == 4, "the E8M0 table takes one code a thread");
   extern __shared__ __align__(16) uint8_t dyn[];  // dn_lds_bytes(rows, I)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = d.H, I = d.I, nkb = I / 128;
@@ -255,10 +257,11 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
     // the first weight items are in flight (issued inside down_fp4_wave after
     // the barrier below; the split is short next to the stream)
     dn4_split_mid(ws, d, nrows, cols, dyn);
+    s_e8tab[tid] = e8m0_scale(tid);  // blockDim.x >= 256 for the MXFP4 path
     __syncthreads();
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const int h0 = b * 16 * WPB + wv * 16;
-    down_fp4_wave<P>(w, d, e, nrows, h0, s_tile[wv], dyn, acc);
+    down_fp4_wave<P>(w, d, e, nrows, h0, s_tile[wv], dyn, s_e8tab, acc);
     pin4(acc);
     if (col < nrows)
       *reinterpret_cast<v4f*>(ws.ypart + (size_t)cols.u(col) * H + h0 + 4 * (lane >> 4)) =
