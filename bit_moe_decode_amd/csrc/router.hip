@@ -14,9 +14,11 @@
 // (wave w, q = lane/16, s = lane%16) takes columns 8s..8s+7 of the 128-blocks
 // w + 16*(q + 4*it), keeps fp32 dots for its EB experts and every row and the
 // row's sum of x^2; the 16 lanes of a DPP row are summed, then the 64 rows of
-// the block in a fixed order, so every block derives the same rstd.  Each
-// 128-block of activations is quantised by one block of the grid (kb modulo
-// the grid), from the 16 lanes that hold it: s = amax/448, q = e4m3(u/s).
+// the block in a fixed order, so every block derives the same rstd.  Row r's
+// 128-block kb of activations is quantised by block (kb*R + r) modulo the
+// grid, from the 16 lanes that hold it: s = amax/448, q = e4m3(u/s).  With at
+// least R blocks, the R rows of a 128-block go to R different blocks, so a
+// lane quantises at most one row of each 128-block it holds.
 #include "device_common.h"
 
 namespace moe {
@@ -91,11 +93,12 @@ __global__ __launch_bounds__(1024) void moe_router_kernel(const uint16_t* __rest
                                                       dot[e][r], false);
       }
     }
-    // The block that owns this 128-block of activations quantises it, a row
-    // at a time, from the 16 lanes that hold it: s = amax/448, q = e4m3(u/s).
-    if (on && (kb % gridDim.x) == blockIdx.x) {  // uniform over the 16 lanes
+    // The owner of (row, 128-block) quantises it from the 16 lanes that hold
+    // it: s = amax/448, q = e4m3(u/s).
+    if (on) {
 #pragma unroll 1
       for (int r = 0; r < R; r++) {
+        if ((uint32_t)(kb * R + r) % gridDim.x != blockIdx.x) continue;  // uniform over 16 lanes
         const u32x4 xr = ld16(x + ((uint32_t)r * H + col));  // cache hit
         float u[8], m = 0.f;
 #pragma unroll
