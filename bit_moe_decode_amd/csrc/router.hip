@@ -8,13 +8,13 @@
 // derives the top-8, gates and dedup table from these logits in one block
 // (route.h).
 //
-// Grid E/EB blocks of 16 waves.  A block owns EB experts (4, or 2 above 4
-// rows) over the whole hidden
-// dimension, so its logits need no partial sums from other blocks: lane
-// (wave w, q = lane/16, s = lane%16) takes columns 8s..8s+7 of the 128-blocks
-// w + 16*(q + 4*it), keeps fp32 dots for its EB experts and every row and the
-// row's sum of x^2; the 16 lanes of a DPP row are summed, then the 64 rows of
-// the block in a fixed order, so every block derives the same rstd.  Row r's
+// Grid E/EB blocks of 16 waves.  A block owns EB experts (1 at one row, else
+// 2) over the whole hidden dimension, so its logits need no partial sums from
+// other blocks: lane (wave w, q = lane/16, s = lane%16) takes columns
+// 8s..8s+7 of the 128-blocks w + 16*(q + 4*it), keeps fp32 dots for its EB
+// experts and every row and the row's sum of x^2; the 16 lanes of a DPP row
+// are summed, then the 64 rows of the block in a fixed order, so every block
+// derives the same rstd.  Row r's
 // 128-block kb of activations is quantised by block (kb*R + r) modulo the
 // grid, from the 16 lanes that hold it: s = amax/448, q = e4m3(u/s).  With at
 // least R blocks, the R rows of a 128-block go to R different blocks, so a
@@ -31,8 +31,9 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ v2bf as_bf16x2(uint32_t v) { return __builtin_bit_cast(v2bf, v); }
 
 constexpr int kRtWaves = 16;   // waves per block
-// experts per block: 4, or 2 for more than 4 rows (register budget)
-__host__ __device__ constexpr int router_experts(int rows) { return rows <= 4 ? 4 : 2; }
+// experts per block: 1 at one row, else 2 (more blocks spread the router's
+// bytes over more CUs; above 4 rows the registers would not hold 4 anyway)
+__host__ __device__ constexpr int router_experts(int rows) { return rows == 1 ? 1 : 2; }
 
 // Element j (0..7) of eight packed bf16 values.
 __device__ __forceinline__ float bf16_elem(const u32x4& v, int j) {
