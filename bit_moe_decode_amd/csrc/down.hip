@@ -33,7 +33,10 @@
 // splits its columns' mid into bf16 hi + lo (mid = hi + lo to about 2^-17) in
 // LDS; a wave converts each 32 inputs of E2M1 weights (one E8M0 block) to bf16
 // with the hardware's scaled conversion and runs two 16x16x32 bf16 MFMAs, one
-// against hi and one against lo, accumulating in fp32.
+// against hi and one against lo, accumulating in fp32.  From 6 rows a wave
+// takes two 16-row tiles, so that each LDS read of the mid operand serves
+// both (the block's LDS, 4 bytes per mid element and column, then allows only
+// two or three blocks a CU).
 //
 // moe_combine_kernel:
 //   out[r][h] = bf16( sum_{j<8} g_rj * y_rj[h] + y_r8[h] )
@@ -130,55 +133,71 @@ __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// The MXFP4 down GEMV of one wave: 16 output rows h0 .. h0+15 of routed
+// The MXFP4 down GEMV of one wave: output rows h0 .. h0 + 16*T of routed
 // expert e over the whole K, against the block's nrows mid columns (fp32 mid,
 // unquantised, split into bf16 hi + lo in LDS by the block).  Item k = the
-// 128 inputs 128k .. +128 of the 16 rows (64 bytes a row): lane L loads row
-// L/4, 16-byte chunk L%4, re-laid through the wave's LDS tile; then per 32
-// inputs (one E8M0 block) lane l converts 8 E2M1 of row l%16 to bf16 scaled
-// by 2^(E8M0-127) (v_cvt_scalef32_pk_bf16_fp4) and runs two bf16 MFMAs, one
-// against the hi and one against the lo parts of mid.
-template <int P>
+// 128 inputs 128k .. +128 of every row (64 bytes a row): per tile, lane L
+// loads row L/4, 16-byte chunk L%4 (row-contiguous), re-laid through the
+// wave's LDS tile into MFMA operand order; then per 32 inputs (one E8M0
+// block) lane l converts 8 E2M1 of row l%16 to bf16 scaled by 2^(E8M0-127)
+// (v_cvt_scalef32_pk_bf16_fp4) and runs two 16x16x32 bf16 MFMAs per tile,
+// against the hi and the lo parts of mid.  The mid operand is read from LDS
+// once per 32 inputs for all T tiles.
+template <int P, int T>
 __device__ __forceinline__ void down_fp4_wave(const Weights& w, const Dims& d, int e, int nrows,
                                               int h0, uint8_t* tile, const uint8_t* smid,
-                                              const float* e8tab, float* acc) {
+                                              const float* e8tab, float (*acc)[4]) {
   const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
   const int H = d.H, I = d.I, nki = I / 128;
-  const size_t rbytes = I / 2;
+  const size_t rbytes = I / 2, ebytes = I / 32;
   const uint8_t* wrow = w.down_c + ((size_t)e * H + h0 + (lane >> 2)) * rbytes + (lane & 3) * 16;
   const uint8_t* erow =
-      reinterpret_cast<const uint8_t*>(w.down_s) + ((size_t)e * H + h0 + col) * (I / 32);
+      reinterpret_cast<const uint8_t*>(w.down_s) + ((size_t)e * H + h0 + col) * ebytes;
   const int cc = col < nrows ? col : 0;  // columns past the rows reuse column 0
   const uint8_t* mh = smid + cc * dn4_col_stride(I) + 16 * g;  // hi of K 8g.. of a 32-step
   const uint8_t* ml = mh + 2 * I;                               // lo
   struct It {
-    u32x4 w;
-    uint32_t e;
+    u32x4 w[T];
+    uint32_t e[T];
   };
   auto issue = [&](It& s, int k) {
-    s.w = ld_nt16(wrow + (size_t)k * 64);
-    s.e = *reinterpret_cast<const uint32_t*>(erow + 4 * k);
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+      s.w[t] = ld_nt16(wrow + (size_t)t * 16 * rbytes + (size_t)k * 64);
+      s.e[t] = *reinterpret_cast<const uint32_t*>(erow + (size_t)t * 16 * ebytes + 4 * k);
+    }
   };
-  v4f c = {acc[0], acc[1], acc[2], acc[3]};
+  v4f c[T];
+#pragma unroll
+  for (int t = 0; t < T; t++) c[t] = v4f{0.f, 0.f, 0.f, 0.f};
   auto consume = [&](It& s, int k) {
-    *reinterpret_cast<u32x4*>(tile + (lane >> 2) * kTileStride + (lane & 3) * 16) = s.w;
-    asm volatile("" ::: "memory");
+    uint32_t a4[T][4];
+#pragma unroll
+    for (int t = 0; t < T; t++) {  // re-lay each tile through the wave's LDS tile
+      *reinterpret_cast<u32x4*>(tile + (lane >> 2) * kTileStride + (lane & 3) * 16) = s.w[t];
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int st = 0; st < 4; st++)
+        a4[t][st] = *reinterpret_cast<const uint32_t*>(tile + col * kTileStride + 16 * st + 4 * g);
+      asm volatile("" ::: "memory");
+    }
 #pragma unroll
     for (int st = 0; st < 4; st++) {
-      const uint32_t a4 = *reinterpret_cast<const uint32_t*>(tile + col * kTileStride + 16 * st + 4 * g);
-      const float sc = e8tab[__builtin_amdgcn_ubfe(s.e, 8 * st, 8)];
-      const v2bf_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4, sc, 0);
-      const v2bf_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4, sc, 1);
-      const v2bf_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4, sc, 2);
-      const v2bf_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4, sc, 3);
-      const v8bf a = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
       const int ko = 2 * (128 * k + 32 * st);
       const v8bf bh = *reinterpret_cast<const v8bf*>(mh + ko);
       const v8bf bl = *reinterpret_cast<const v8bf*>(ml + ko);
-      c = mfma_bf16(a, bh, c);
-      c = mfma_bf16(a, bl, c);
+#pragma unroll
+      for (int t = 0; t < T; t++) {
+        const float sc = e8tab[__builtin_amdgcn_ubfe(s.e[t], 8 * st, 8)];
+        const v2bf_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4[t][st], sc, 0);
+        const v2bf_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4[t][st], sc, 1);
+        const v2bf_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4[t][st], sc, 2);
+        const v2bf_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(a4[t][st], sc, 3);
+        const v8bf a = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        c[t] = mfma_bf16(a, bh, c[t]);
+        c[t] = mfma_bf16(a, bl, c[t]);
+      }
     }
-    asm volatile("" ::: "memory");
   };
   // ring of P items (P divides I/128): every issued load is used
   It st[P];
@@ -193,10 +212,13 @@ __device__ __forceinline__ void down_fp4_wave(const Weights& w, const Dims& d, i
   }
 #pragma unroll
   for (int p = 0; p < P; p++) consume(st[p], nki - P + p);
-  acc[0] = c[0];
-  acc[1] = c[1];
-  acc[2] = c[2];
-  acc[3] = c[3];
+#pragma unroll
+  for (int t = 0; t < T; t++) {
+    acc[t][0] = c[t][0];
+    acc[t][1] = c[t][1];
+    acc[t][2] = c[t][2];
+    acc[t][3] = c[t][3];
+  }
 }
 
 // The block's mid columns as bf16 hi + lo: hi = bf16(m), lo = bf16(m - hi)
@@ -220,7 +242,7 @@ __device__ __forceinline__ void dn4_split_mid(const Ws& ws, const Dims& d, int n
   }
 }
 
-template <int RF, int P, int WPB>
+template <int RF, int P, int WPB, int T4>
 __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Dims d) {
   __shared__ __align__(16) uint8_t s_tile[WPB][kTileBytes];
   __shared__ float s_e8tab[RF == kFmtMxfp4 ? 256 : 1];  // 2^(e-127) for each E8M0 code
@@ -230,7 +252,8 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
   const int H = d.H, I = d.I, nkb = I / 128;
   const int col = lane & 15;
 
-  // ---- the block's expert and rows
+  // ---- the block's expert and rows (MXFP4 routed blocks: T4 times the rows
+  // of an FP8 block)
   const int per = H / (16 * WPB);
   const int nb_sh = d.Is > 0 ? per : 0;
   int b = blockIdx.x, g = -1, nrows, e;
@@ -240,8 +263,9 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
     e = -1;
   } else {
     b -= nb_sh;
-    g = b / per;
-    b -= g * per;
+    const int perg = RF == kFmtMxfp4 ? per / T4 : per;
+    g = b / perg;
+    b -= g * perg;
     // one round of independent loads; the table of a group past D is stale
     // but in bounds, and unused
     const int D = *ws.n_groups;
@@ -259,13 +283,17 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
     dn4_split_mid(ws, d, nrows, cols, dyn);
     s_e8tab[tid] = e8m0_scale(tid);  // blockDim.x >= 256 for the MXFP4 path
     __syncthreads();
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    const int h0 = b * 16 * WPB + wv * 16;
-    down_fp4_wave<P>(w, d, e, nrows, h0, s_tile[wv], dyn, s_e8tab, acc);
-    pin4(acc);
-    if (col < nrows)
-      *reinterpret_cast<v4f*>(ws.ypart + (size_t)cols.u(col) * H + h0 + 4 * (lane >> 4)) =
-          v4f{acc[0], acc[1], acc[2], acc[3]};
+    float acc[T4][4];
+    const int h0 = (b * WPB + wv) * 16 * T4;
+    down_fp4_wave<P, T4>(w, d, e, nrows, h0, s_tile[wv], dyn, s_e8tab, acc);
+#pragma unroll
+    for (int t = 0; t < T4; t++) pin4(acc[t]);
+    if (col < nrows) {
+#pragma unroll
+      for (int t = 0; t < T4; t++)
+        *reinterpret_cast<v4f*>(ws.ypart + (size_t)cols.u(col) * H + h0 + 16 * t +
+                                4 * (lane >> 4)) = v4f{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
+    }
     return;
   }
   const int cc = col < nrows ? col : 0;  // columns past the rows reuse column 0
@@ -359,31 +387,42 @@ static int down_ring(int inter) {
 
 // Launches one instantiation with `lds` bytes of dynamic LDS, raising the
 // kernel's dynamic-LDS limit first when it is above the default 64 KB.
-template <int RF, int P, int WPB>
+template <int RF, int P, int WPB, int T4>
 static hipError_t launch_one(int max_groups, size_t lds, const Weights& w, const Ws& ws,
                              const Dims& d, hipStream_t stream) {
   static size_t raised = 0;  // the limit already set for this instantiation
   if (lds > 65536 && lds > raised) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_down_kernel<RF, P, WPB>),
+        reinterpret_cast<const void*>(&moe_down_kernel<RF, P, WPB, T4>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     raised = lds;
   }
-  const dim3 grid((d.H / (16 * WPB)) * ((d.Is > 0 ? 1 : 0) + max_groups));
-  hipLaunchKernelGGL((moe_down_kernel<RF, P, WPB>), grid, dim3(64 * WPB), lds, stream, w, ws, d);
+  const int per = d.H / (16 * WPB);
+  const dim3 grid(per * (d.Is > 0 ? 1 : 0) +
+                  (RF == kFmtMxfp4 ? per / T4 : per) * max_groups);
+  hipLaunchKernelGGL((moe_down_kernel<RF, P, WPB, T4>), grid, dim3(64 * WPB), lds, stream, w, ws,
+                     d);
   return hipGetLastError();
 }
 
 // Blocks of 2 waves (32 output rows) for FP8 steps of one or two rows, whose
 // few experts otherwise leave some CUs a block more than others; 4 waves
-// (64 rows) otherwise.
+// (64 rows) otherwise.  MXFP4 routed waves take 2 tiles of 16 rows from
+// kDn4TwoTileRows rows up (the mid operand's LDS reads then serve 32 rows),
+// else 1 (more blocks for the few experts of small steps); measured: 2 tiles
+// are faster from 6 rows, slower at 4 and 5.
+constexpr int kDn4TwoTileRows = 6;
 template <int RF, int P>
 static hipError_t launch_wpb(int max_groups, size_t lds, const Weights& w, const Ws& ws,
                              const Dims& d, hipStream_t stream) {
-  if (RF == kFmtFp8 && d.rows <= 2)
-    return launch_one<RF, P, RF == kFmtFp8 ? 2 : 4>(max_groups, lds, w, ws, d, stream);
-  return launch_one<RF, P, 4>(max_groups, lds, w, ws, d, stream);
+  if constexpr (RF == kFmtFp8)
+    return d.rows <= 2 ? launch_one<RF, P, 2, 1>(max_groups, lds, w, ws, d, stream)
+                       : launch_one<RF, P, 4, 1>(max_groups, lds, w, ws, d, stream);
+  else
+    return d.rows >= kDn4TwoTileRows
+               ? launch_one<RF, P, 4, 2>(max_groups, lds, w, ws, d, stream)
+               : launch_one<RF, P, 4, 1>(max_groups, lds, w, ws, d, stream);
 }
 
 template <int RF>

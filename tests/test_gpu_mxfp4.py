@@ -53,6 +53,18 @@ def test_tiny_mxfp4_parity(tiny4, rows, mode):
     _say(_run(tiny4, x))
 
 
+@pytest.mark.parametrize("inter", [256, 512, 1024])
+def test_mxfp4_other_intermediate_sizes(inter):
+    """MXFP4 down rings of 2, 4 and 8 items (I/128 of them) and up/gate items
+    per K part of one and two, with a shared expert, at 1, 3 and 8 rows."""
+    shape = dict(hidden=512, inter=inter, n_experts=32, shared_inter=inter, router_std=0.02)
+    layer = S.make_layer(shape, routed_fmt=S.FMT_MXFP4, seed=4200 + inter, device="cuda")
+    for rows in (1, 3, 8):
+        _say(f"mxfp4 inter={inter} rows={rows}")
+        x = S.make_x(rows, layer.hidden, seed=4300 + rows, mode="corr")
+        _say(_run(layer, x))
+
+
 def test_tiny_mxfp4_dedup_off_is_bitwise_equal(tiny4):
     x = S.make_x(8, tiny4.hidden, seed=4100, mode="corr").cuda()
     on = B.LayerRunner(tiny4, 8).run(x)
