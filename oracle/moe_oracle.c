@@ -366,6 +366,7 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
   const int Imax = Is > I ? Is : I;
   if (R < 1 || R > 8 || H % 128 || I % 128 || Is % 128 || E < 8 || Is < 0) return ORC_ERR;
   if (cfg->routed_fmt != ORC_FMT_FP8 && cfg->routed_fmt != ORC_FMT_MXFP4) return ORC_ERR;
+  if (cfg->act_fmt != ORC_ACT_FP8 && cfg->act_fmt != ORC_ACT_BF16) return ORC_ERR;
   if (Is > 0 && (!sh_gate || !sh_up || !sh_down)) return ORC_ERR;
   orc_init_luts();
   orc_debug none;
@@ -408,9 +409,16 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
     double zs[8], g[8];
     for (int j = 0; j < 8; j++) zs[j] = z[(size_t)r * E + ids[j]];
     orc_softmax8(zs, g);
-    /* 3. FP8 activation blocks */
-    orc_quant_blocks(u32, H, aq, as);
-    for (int k = 0; k < H; k++) hin[k] = lut_e4m3[aq[k]] * (double)as[k / 128] * rstd;
+    /* 3. the experts' input: FP8 activation blocks (dequantised, times rstd),
+     * or with ORC_ACT_BF16 u itself times rstd (no codes, scales 0) */
+    if (cfg->act_fmt == ORC_ACT_BF16) {
+      memset(aq, 0, H);
+      for (int b = 0; b < H / 128; b++) as[b] = 0.0f;
+      for (int k = 0; k < H; k++) hin[k] = uf[k] * rstd;
+    } else {
+      orc_quant_blocks(u32, H, aq, as);
+      for (int k = 0; k < H; k++) hin[k] = lut_e4m3[aq[k]] * (double)as[k / 128] * rstd;
+    }
     /* 4. experts */
     for (int j = 0; j < 9; j++) {
       if (j == 8 && Is == 0) break;

@@ -34,6 +34,10 @@ extern "C" {
 
 #define ORC_FMT_FP8 1   /* E4M3FN codes, one fp32 scale per 128x128 block  */
 #define ORC_FMT_MXFP4 2 /* E2M1 codes, 2 per byte (low nibble first), E8M0 per 32 along K */
+/* Expert inputs: FP8 E4M3 per 1x128 block of u (#85 Mod. row 10, the default),
+ * or u itself (bf16) -- an option for comparing what the FP8 blocks cost. */
+#define ORC_ACT_FP8 0
+#define ORC_ACT_BF16 1
 
 /* ---- scalar codecs ---- */
 double orc_dec_bf16(uint16_t h);
@@ -67,6 +71,7 @@ typedef struct {
   float rms_eps;
   int32_t routed_fmt; /* ORC_FMT_FP8 or ORC_FMT_MXFP4; the shared expert is always FP8 */
   int32_t nthreads;
+  int32_t act_fmt;    /* ORC_ACT_FP8 or ORC_ACT_BF16 */
 } orc_cfg;
 
 /* Debug outputs of one step; any pointer may be NULL.  "slot" 0..7 is the

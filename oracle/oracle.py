@@ -18,6 +18,7 @@ _LIB = None
 
 FMT_FP8 = 1
 FMT_MXFP4 = 2
+ACT_FP8, ACT_BF16 = 0, 1  # the experts' input: FP8 blocks of u (default) or u itself
 
 
 class OrcMat(ctypes.Structure):
@@ -30,6 +31,7 @@ class OrcCfg(ctypes.Structure):
         ("n_experts", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
         ("rows", ctypes.c_int32), ("rms_eps", ctypes.c_float),
         ("routed_fmt", ctypes.c_int32), ("nthreads", ctypes.c_int32),
+        ("act_fmt", ctypes.c_int32),
     ]
 
 
@@ -181,7 +183,8 @@ def quant_blocks(v):
 def moe_step(cfg, x, gamma, router_w, experts, shared=None, anchor_z=None, nthreads=1):
     """Run the oracle's decode step.
 
-    cfg: dict(hidden, inter, n_experts, shared_inter, rows, rms_eps, routed_fmt)
+    cfg: dict(hidden, inter, n_experts, shared_inter, rows, rms_eps, routed_fmt, act_fmt)
+         (act_fmt ACT_FP8, the default, or ACT_BF16: u itself as the experts' input)
     x: uint16 [R, H] bf16 codes; gamma: uint16 [H]; router_w: uint16 [E, H]
     experts: dict expert_id -> (gate_codes, gate_scales, up_codes, up_scales,
              down_codes, down_scales); only experts that are picked are needed.
@@ -193,7 +196,7 @@ def moe_step(cfg, x, gamma, router_w, experts, shared=None, anchor_z=None, nthre
     Is, R = cfg.get("shared_inter", 0), cfg["rows"]
     Imax = max(I, Is)
     c = OrcCfg(H, I, E, Is, R, float(cfg.get("rms_eps", 1e-6)),
-               int(cfg.get("routed_fmt", FMT_FP8)), int(nthreads))
+               int(cfg.get("routed_fmt", FMT_FP8)), int(nthreads), int(cfg.get("act_fmt", ACT_FP8)))
     keep = []
 
     def mat(codes, scales):

@@ -63,7 +63,7 @@ def _hand_layer_fp8():
     return experts, shared
 
 
-def _closed_form_fp8():
+def _closed_form_fp8(act_bf16=False):
     """The step by hand.  x = 1 on block 0 and -2 on block 1, gamma = 1:
     sum x^2 = 640, rstd = 1/sqrt(640/256 + eps).  Router rows are constant per
     block, so raw_e = 128 (e+1)/64 - 256 (e%3)/128 = 2(e+1) - 2(e%3):
@@ -73,12 +73,13 @@ def _closed_form_fp8():
     with A = 448 s0.  All weight codes are 1.0, so an output block of a matrix
     with block scales S is 128 A rstd (S[.,0] - 2 S[.,1]); mid is constant per
     block, its FP8 code is +-448 and mhat = sign(mid) 448 s_m with
-    s_m = fp32(fp32|mid| / 448)."""
+    s_m = fp32(fp32|mid| / 448).  With bf16 activations the experts' input is
+    u rstd itself: A = 1 exactly."""
     a, b, c, sa, sb, sc = _hand_scales()
     eps = float(F32(1e-6))
     rstd = 1.0 / np.sqrt(640.0 / 256 + eps)
     s0 = float(F32(1.0) / F32(448.0))
-    A = 448.0 * s0
+    A = 1.0 if act_bf16 else 448.0 * s0
     raw = np.array([2 * (e + 1) - 2 * (e % 3) for e in range(E)], float)
     z = rstd * raw
     ids = [6, 7, 8, 3, 4, 5, 0, 1]
@@ -135,6 +136,30 @@ def test_hand_worked_layer_fp8():
     assert np.array_equal(out[0], O.round_bf16_n(d["out_f64"][0]))
 
 
+def test_hand_worked_layer_bf16_activations():
+    """The same layer with the experts' input left in bf16 (no FP8 blocks):
+    h = +-rstd and -+2 rstd exactly, no activation codes or scales."""
+    x, gamma, w = _hand_inputs()
+    experts, shared = _hand_layer_fp8()
+    cfg = dict(hidden=H, inter=I, n_experts=E, shared_inter=IS, rows=1, rms_eps=1e-6,
+               routed_fmt=O.FMT_FP8, act_fmt=O.ACT_BF16)
+    out, d = O.moe_step(cfg, x, gamma, w, experts, shared)
+    cf = _closed_form_fp8(act_bf16=True)
+    assert list(d["ids"][0]) == cf["ids"]
+    assert not d["act_q"].any() and not d["act_s"].any()
+    for j in range(8):
+        mid, sm, y = cf["ys"][j]
+        assert np.allclose(d["mid"][0, j, :I], np.repeat(mid, 128), rtol=1e-13, atol=0)
+        assert np.array_equal(d["midqs"][0, j, :2], sm.astype(F32))
+        assert np.allclose(d["y"][0, j], np.repeat(y, 128), rtol=1e-13, atol=0)
+    assert np.allclose(d["out_f64"][0], cf["out"], rtol=1e-13, atol=0)
+    # the FP8 blocks' scale is not exactly 1/448 of amax in fp32, so the two
+    # modes differ (a dropped or doubled activation scale would show here)
+    _, d8 = O.moe_step(dict(cfg, act_fmt=O.ACT_FP8), x, gamma, w, experts, shared)
+    assert not np.array_equal(d8["mid"], d["mid"])
+    assert np.allclose(d8["mid"], d["mid"], rtol=1e-6, atol=0)
+
+
 def test_hand_worked_layer_mxfp4():
     """MXFP4 routed experts: every E2M1 code is 1.0 (nibble 0x2), E8M0
     exponents differ per (row, 32-group), mid is not re-quantised."""
@@ -186,7 +211,7 @@ def _np_mxfp4(codes, e8m0):
     return v * np.repeat(2.0 ** (e8m0.astype(float) - 127), 32, axis=1)
 
 
-def _np_step(layer, x, routed_fmt):
+def _np_step(layer, x, routed_fmt, act_fmt=0):
     """Numpy + torch-dtype reimplementation used only as a cross-check."""
     import bit_moe_decode_amd.synth as S  # generator only
     tb = lambda t: t.float().double().numpy() if t.dtype == torch.bfloat16 else t.numpy()
@@ -206,6 +231,8 @@ def _np_step(layer, x, routed_fmt):
         s = (np.abs(ub).max(axis=1).astype(F32) / F32(448)).astype(F32)
         q = torch.from_numpy((ub.astype(F32) / s[:, None]).astype(F32)).to(torch.float8_e4m3fn)
         h = (q.double().numpy() * s[:, None]).ravel() * rstd
+        if act_fmt == O.ACT_BF16:
+            h = u * rstd
 
         def ffn(mats, fmt):
             dec = _np_fp8 if fmt == O.FMT_FP8 else _np_mxfp4
@@ -227,20 +254,21 @@ def _np_step(layer, x, routed_fmt):
     return out
 
 
-def _run_oracle(layer, x, **kw):
+def _run_oracle(layer, x, act_fmt=0, **kw):
     import bit_moe_decode_amd.synth as S
     xb = S.bf16_bits(x).numpy().view(np.uint16)
     experts = {e: tuple(t.numpy() for t in layer.routed.expert(e)) for e in range(layer.n_experts)}
     shared = tuple(t.numpy() for t in layer.shared.expert(0)) if layer.shared is not None else None
     cfg = dict(hidden=layer.hidden, inter=layer.inter, n_experts=layer.n_experts,
                shared_inter=layer.shared_inter, rows=x.shape[0], rms_eps=layer.rms_eps,
-               routed_fmt=layer.routed_fmt)
+               routed_fmt=layer.routed_fmt, act_fmt=act_fmt)
     return O.moe_step(cfg, xb, S.bf16_bits(layer.gamma).numpy().view(np.uint16),
                       S.bf16_bits(layer.router_w).numpy().view(np.uint16), experts, shared, **kw)
 
 
-@pytest.mark.parametrize("fmt", [O.FMT_FP8, O.FMT_MXFP4])
-def test_oracle_matches_independent_numpy_pipeline(fmt):
+@pytest.mark.parametrize("fmt,act", [(O.FMT_FP8, O.ACT_FP8), (O.FMT_MXFP4, O.ACT_FP8),
+                                     (O.FMT_FP8, O.ACT_BF16)])
+def test_oracle_matches_independent_numpy_pipeline(fmt, act):
     import bit_moe_decode_amd.synth as S
     layer = S.make_layer("tiny", routed_fmt=fmt, seed=1000)
     # give the tiny layer a shared expert too, so that path is pinned as well
@@ -249,8 +277,8 @@ def test_oracle_matches_independent_numpy_pipeline(fmt):
                                                (layer.shared.gate, layer.shared.up, layer.shared.down)])
     layer.shared_inter = layer.inter
     x = S.make_x(4, layer.hidden, seed=2000)
-    out, d = _run_oracle(layer, x)
-    ref = _np_step(layer, x, fmt)
+    out, d = _run_oracle(layer, x, act_fmt=act)
+    ref = _np_step(layer, x, fmt, act)
     assert np.allclose(d["out_f64"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
