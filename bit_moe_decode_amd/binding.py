@@ -16,6 +16,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEV
 FMT_FP8 = 1
 FMT_MXFP4 = 2
 FMT_Q1 = 3
+ACT_FP8, ACT_BF16 = 0, 1  # moe_afmt
 F_NO_DEDUP = 1 << 1
 N_KERNELS = 5
 K_UPGATE, K_DOWN = 2, 3  # kernels moe_decode_relaunch repeats
@@ -33,7 +34,7 @@ class Config(ctypes.Structure):
         ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
         ("top_k", ctypes.c_int32), ("shared_inter", ctypes.c_int32), ("max_rows", ctypes.c_int32),
         ("rms_eps", ctypes.c_float), ("routed_fmt", ctypes.c_int32), ("shared_fmt", ctypes.c_int32),
-        ("flags", ctypes.c_uint32),
+        ("flags", ctypes.c_uint32), ("act_fmt", ctypes.c_int32),
     ]
 
 
@@ -225,12 +226,13 @@ class LayerRunner:
     layer: bit_moe_decode_amd.synth.Layer whose tensors live on `device`.
     """
 
-    def __init__(self, layer, max_rows, flags=0, device="cuda", stream=None):
+    def __init__(self, layer, max_rows, flags=0, device="cuda", stream=None, act_fmt=ACT_FP8):
         import torch
         self.layer = layer
         self.device = device
         self.cfg = Config(layer.hidden, layer.inter, layer.n_experts, 8, layer.shared_inter,
-                          max_rows, float(layer.rms_eps), layer.routed_fmt, FMT_FP8, flags)
+                          max_rows, float(layer.rms_eps), layer.routed_fmt, FMT_FP8, flags,
+                          act_fmt)
         n = workspace_size(self.cfg)
         if n == 0:
             raise MoeError(MOE_ERR_UNSUPPORTED, "moe_decode_workspace_size")

@@ -39,7 +39,7 @@ struct Plan {
   int H, I, E, Is, R, imax, groups, ks;
   size_t off_logits, off_rstd, off_ids, off_gates, off_ngroups, off_gexpert,
       off_gowner, off_gmask, off_gslot, off_grows, off_gnrows, off_actq, off_acts, off_mid,
-      off_midq, off_midqs, off_ypart, total;
+      off_midq, off_midqs, off_ypart, off_actu, total;
 };
 
 bool is_mult(int v, int m) { return v > 0 && v % m == 0; }
@@ -62,6 +62,10 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
     return MOE_ERR_UNSUPPORTED;
   if (c->shared_inter > 0 && c->shared_fmt != MOE_FMT_FP8_E4M3_B128) return MOE_ERR_UNSUPPORTED;
   if (c->flags & ~kKnownFlags) return MOE_ERR_UNSUPPORTED;
+  if (c->act_fmt != MOE_ACT_FP8_B128 && c->act_fmt != MOE_ACT_BF16) return MOE_ERR_UNSUPPORTED;
+  // bf16 activations: the up/gate's bf16 MFMA takes FP8 weights only
+  if (c->act_fmt == MOE_ACT_BF16 && c->routed_fmt != MOE_FMT_FP8_E4M3_B128)
+    return MOE_ERR_UNSUPPORTED;
   if (!(c->rms_eps >= 0.0f) || c->rms_eps > 1.0f) return MOE_ERR_INVALID_ARG;
 
   p->H = c->hidden;
@@ -99,6 +103,7 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   p->off_midq = take(U * IM);
   p->off_midqs = take(U * (IM / 128) * 4);
   p->off_ypart = take(U * H * 4);
+  p->off_actu = take(R * H * 2);
   p->total = o;
   return MOE_OK;
 }
@@ -160,6 +165,7 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
   v.midq = reinterpret_cast<uint8_t*>(b + p.off_midq);
   v.midqs = reinterpret_cast<float*>(b + p.off_midqs);
   v.ypart = reinterpret_cast<float*>(b + p.off_ypart);
+  v.act_u = reinterpret_cast<uint16_t*>(b + p.off_actu);
   // clear the whole workspace once, so that debug views read before the
   // first step are well defined
   const size_t words = p.total / 4;
@@ -217,6 +223,7 @@ moe_status step_args(const moe_decode_ctx* ctx, int rows, const moe_decode_weigh
   d.ks = p.ks;
   d.no_dedup = (ctx->cfg.flags & MOE_F_NO_DEDUP) ? 1 : 0;
   d.eps = ctx->cfg.rms_eps;
+  d.act_bf16 = ctx->cfg.act_fmt == MOE_ACT_BF16 ? 1 : 0;
   return MOE_OK;
 }
 

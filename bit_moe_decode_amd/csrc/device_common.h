@@ -32,6 +32,7 @@ struct Ws {
   uint8_t* grp_nrows;     // [G]
   uint8_t* act_q;         // [max_rows][H]
   float* act_s;           // [max_rows][H/128]
+  uint16_t* act_u;        // [max_rows][H] u = bf16(x * gamma) (bf16 activations only)
   // per (row, pick) with pick 8 = the shared expert: u = row * 9 + pick
   float* mid;             // [max_rows * 9][imax]
   uint8_t* midq;          // [max_rows * 9][imax]
@@ -46,6 +47,7 @@ struct Dims {
   int imax;            // max(I, Is)
   int ks;              // up/gate K parts (divides H/128)
   int no_dedup;        // 1: one group per (row, pick)
+  int act_bf16;        // 1: the experts take u (bf16), not FP8 activation blocks
   float eps;
 };
 
@@ -202,6 +204,13 @@ __device__ __forceinline__ v8i cat8(const u32x4& lo, const u32x4& hi) {
   r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
   r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
   return r;
+}
+
+// 16x16x32 bf16 MFMA, fp32 accumulate.  A: lane l holds row l%16, K
+// 8*(l/16) .. +8; B: lane l holds column l%16, same K; D: lane l holds rows
+// 4*(l/16)+v of column l%16 (layout checked on the device).
+__device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 }  // namespace moe

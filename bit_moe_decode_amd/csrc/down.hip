@@ -126,12 +126,6 @@ __host__ __device__ inline size_t dn4_lds_bytes(int rows, int inter) {
   return (size_t)rows * dn4_col_stride(inter);
 }
 
-// 16x16x32 bf16 MFMA, fp32 accumulate.  A: lane l holds row l%16, K
-// 8*(l/16) .. +8; B: lane l holds column l%16, same K; D: lane l holds rows
-// 4*(l/16)+v of column l%16 (layout checked on the device).
-__device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 // The MXFP4 down GEMV of one wave: output rows h0 .. h0 + 16*T of routed
 // expert e over the whole K, against the block's nrows mid columns (fp32 mid,

@@ -18,7 +18,8 @@
 // 128-block kb of activations is quantised by block (kb*R + r) modulo the
 // grid, from the 16 lanes that hold it: s = amax/448, q = e4m3(u/s).  With at
 // least R blocks, the R rows of a 128-block go to R different blocks, so a
-// lane quantises at most one row of each 128-block it holds.
+// lane quantises at most one row of each 128-block it holds.  With bf16
+// activations the owner stores u itself instead.
 #include "device_common.h"
 
 namespace moe {
@@ -101,6 +102,16 @@ __global__ __launch_bounds__(1024) void moe_router_kernel(const uint16_t* __rest
       for (int r = 0; r < R; r++) {
         if ((uint32_t)(kb * R + r) % gridDim.x != blockIdx.x) continue;  // uniform over 16 lanes
         const u32x4 xr = ld16(x + ((uint32_t)r * H + col));  // cache hit
+        if (d.act_bf16) {  // the experts take u itself: store its 8 bf16
+          u32x4 ub;
+#pragma unroll
+          for (int p = 0; p < 4; p++)
+            ub[p] = (uint32_t)f32_to_bf16(bf16_elem(xr, 2 * p) * bf16_elem(gm, 2 * p)) |
+                    ((uint32_t)f32_to_bf16(bf16_elem(xr, 2 * p + 1) * bf16_elem(gm, 2 * p + 1))
+                     << 16);
+          *reinterpret_cast<u32x4*>(ws.act_u + ((uint32_t)r * H + col)) = ub;
+          continue;
+        }
         float u[8], m = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; j++) {

@@ -27,6 +27,9 @@
 //
 //  FP8 item = one 128-wide K block: one FP8 x FP8 MFMA per matrix, scaled by
 //    weight block scale x activation block scale.
+//  FP8 item with bf16 activations (MOE_ACT_BF16, u itself as the input): the
+//    K block's codes converted to bf16 exactly, four 16x16x32 bf16 MFMAs per
+//    matrix against u, scaled by the weight block scale.
 //  MXFP4 item = two 128-wide K blocks (a 128-byte line per row): per K block
 //    one scaled FP4 x FP8 MFMA per matrix, the E8M0 exponents entering as the
 //    MFMA's A scales, then the activation block scale.  Operand layout of that
@@ -139,6 +142,92 @@ __device__ __forceinline__ void ug_fp8(const Weights& w, const Ws& ws, const Dim
   for (int p = 0; p < P; p++) consume(st[p]);
 }
 
+// FP8 weights against bf16 activations (u itself): K blocks kb0 .. kb0 + nk
+// of the slab.  The weight rows are re-laid through LDS as for FP8; then per
+// 32 inputs of the K block, lane l converts the 8 codes of row l%16 at inputs
+// 32s + 8(l/16) .. +8 to bf16 (exact: every E4M3 value is a bf16 value; the
+// conversion's scale is 1) and runs one 16x16x32 bf16 MFMA per matrix against
+// its using row's u at the same inputs; the K block's fp32 result is scaled
+// by the weight block scale (rstd comes in the epilogue).
+struct UgStageB {
+  u32x4 g0, g1, u0, u1, a[4];
+  float sg, su;
+};
+typedef __bf16 v2bf_u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v8bf fp8x8_to_bf16(uint2 c) {
+  const v2bf_u p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false);
+  const v2bf_u p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true);
+  const v2bf_u p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false);
+  const v2bf_u p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true);
+  return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+template <int P>
+__device__ __forceinline__ void ug_fp8_bf16a(const Weights& w, const Ws& ws, const Dims& d,
+                                             UgJob j, int kb0, int nk, uint8_t* tg, uint8_t* tu,
+                                             int lane, float* accg, float* accu) {
+  const int H = d.H, nkbh = H / 128;
+  const size_t ebytes = (size_t)d.I * H;
+  const size_t escl = (size_t)(d.I / 128) * nkbh;
+  const uint8_t* bg = j.e < 0 ? w.sg_c : w.gate_c + (size_t)j.e * ebytes;
+  const uint8_t* bu = j.e < 0 ? w.su_c : w.up_c + (size_t)j.e * ebytes;
+  const float* sg =
+      j.e < 0 ? w.sg_s : reinterpret_cast<const float*>(w.gate_s) + (size_t)j.e * escl;
+  const float* su = j.e < 0 ? w.su_s : reinterpret_cast<const float*>(w.up_s) + (size_t)j.e * escl;
+  const uint8_t* pg = bg + (size_t)(j.n0 + (lane >> 3)) * H + (lane & 7) * 16 + (size_t)kb0 * 128;
+  const uint8_t* pu = bu + (pg - bg);
+  const size_t r8 = (size_t)8 * H;
+  // u of the lane's column at inputs 8(l/16) .. +8 of each 32-input step
+  const uint16_t* pa = ws.act_u + (size_t)j.row * H + (lane >> 4) * 8 + (size_t)kb0 * 128;
+  const float* psg = sg + (size_t)(j.n0 / 128) * nkbh + kb0;
+  const float* psu = su + (size_t)(j.n0 / 128) * nkbh + kb0;
+  const int col = lane & 15, g = lane >> 4;
+
+  auto issue = [&](UgStageB& st, int k) {
+    const size_t o = (size_t)k * 128;
+    st.g0 = ld_nt16(pg + o);
+    st.g1 = ld_nt16(pg + r8 + o);
+    st.u0 = ld_nt16(pu + o);
+    st.u1 = ld_nt16(pu + r8 + o);
+#pragma unroll
+    for (int s = 0; s < 4; s++) st.a[s] = ld16(pa + o + 32 * s);
+    st.sg = psg[k];
+    st.su = psu[k];
+  };
+  auto consume = [&](UgStageB& st) {
+    tile_put(tg, lane, st.g0, st.g1);
+    tile_put(tu, lane, st.u0, st.u1);
+    asm volatile("" ::: "memory");
+    v4f cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const int off = col * kTileStride + 32 * s + 8 * g;
+      const v8bf ag = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(tg + off));
+      const v8bf au = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(tu + off));
+      const v8bf b = __builtin_bit_cast(v8bf, st.a[s]);
+      cg = mfma_bf16(ag, b, cg);
+      cu = mfma_bf16(au, b, cu);
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      accg[v] = fmaf(cg[v], st.sg, accg[v]);
+      accu[v] = fmaf(cu[v], st.su, accu[v]);
+    }
+  };
+  UgStageB st[P];
+#pragma unroll
+  for (int p = 0; p < P; p++) issue(st[p], p);
+  for (int k0 = 0; k0 < nk - P; k0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+      consume(st[p]);
+      issue(st[p], k0 + P + p);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; p++) consume(st[p]);
+}
+
 // MXFP4 weights: items (pairs of K blocks) it0 .. it0 + ni of the slab.
 template <int P>
 __device__ __forceinline__ void ug_fp4(const Weights& w, const Ws& ws, const Dims& d, UgJob j,
@@ -217,7 +306,7 @@ typedef uint8_t UgTiles[4][2][kTileBytes];  // per wave: gate and up weight tile
 
 // Up/gate block number `blk` of the numbering above (the shared expert's
 // slabs, then those of each routed group), with 256 threads.
-template <int RF, int P, int P4>
+template <int RF, int P, int P4, bool AB>
 __device__ __forceinline__ void upgate_block(const Weights& w, const Ws& ws, const Dims& d,
                                              int blk, UgTiles& s_tile) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -251,7 +340,10 @@ __device__ __forceinline__ void upgate_block(const Weights& w, const Ws& ws, con
   const int slab = b * spb + wv / KS, kp = wv % KS;
   const UgJob j{e, row, slab * 16};
   float accg[4] = {0.f, 0.f, 0.f, 0.f}, accu[4] = {0.f, 0.f, 0.f, 0.f};
-  if (RF == kFmtMxfp4 && e >= 0) {
+  if constexpr (AB) {  // bf16 activations (FP8 weights only)
+    const int nk = d.H / 128 / KS;
+    ug_fp8_bf16a<P>(w, ws, d, j, kp * nk, nk, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
+  } else if (RF == kFmtMxfp4 && e >= 0) {
     const int ni = d.H / 256 / KS;  // items of two K blocks per part
     ug_fp4<P4>(w, ws, d, j, kp * ni, ni, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
   } else {
@@ -290,10 +382,10 @@ __device__ __forceinline__ void upgate_block(const Weights& w, const Ws& ws, con
 
 // Up/gate blocks base, base + 1, ... (base = 0: the shared expert's slabs and
 // the routed groups'; base = Is/BR: the routed groups' only).
-template <int RF, int P, int P4>
+template <int RF, int P, int P4, bool AB>
 __global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims d, int base) {
   __shared__ __align__(16) UgTiles s_tile;
-  upgate_block<RF, P, P4>(w, ws, d, base + blockIdx.x, s_tile);
+  upgate_block<RF, P, P4, AB>(w, ws, d, base + blockIdx.x, s_tile);
 }
 
 // Steps of up to 4 rows: the step's routing decisions (top-8, gates, dedup
@@ -303,14 +395,14 @@ __global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims 
 // block, runs.  (With more rows the routing takes longer on 4 waves than the
 // shared expert saves: moe_route_only_kernel on 8 waves, and the shared
 // slabs go with the routed ones.)
-template <int KPL, int P>
+template <int KPL, int P, bool AB>
 __global__ __launch_bounds__(256) void moe_route_kernel(Weights w, Ws ws, Dims d) {
   __shared__ RouteSmem rs;
   __shared__ __align__(16) UgTiles s_tile;
   if (blockIdx.x == 0)
     route_block<KPL>(ws, d, rs, true);
   else
-    upgate_block<kFmtFp8, P, 1>(w, ws, d, blockIdx.x - 1, s_tile);
+    upgate_block<kFmtFp8, P, 1, AB>(w, ws, d, blockIdx.x - 1, s_tile);
 }
 
 template <int KPL>
@@ -337,7 +429,15 @@ int upgate_k_parts(int hidden, int routed_fmt) {
 template <int RF, int P, int P4>
 static void launch_one(dim3 grid, int base, const Weights& w, const Ws& ws, const Dims& d,
                        hipStream_t stream) {
-  hipLaunchKernelGGL((moe_upgate_kernel<RF, P, P4>), grid, dim3(256), 0, stream, w, ws, d, base);
+  if constexpr (RF == kFmtFp8) {  // bf16 activations: FP8 routed experts only
+    if (d.act_bf16) {
+      hipLaunchKernelGGL((moe_upgate_kernel<RF, P, P4, true>), grid, dim3(256), 0, stream, w, ws,
+                         d, base);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((moe_upgate_kernel<RF, P, P4, false>), grid, dim3(256), 0, stream, w, ws, d,
+                     base);
 }
 
 template <int RF, int P>
@@ -383,10 +483,18 @@ static void launch_route_k(int p, const Weights& w, const Ws& ws, const Dims& d,
     return;
   }
   const dim3 grid(1 + d.Is / (16 * (4 / d.ks)));
+  if (d.act_bf16) {
+    switch (p) {
+      case 4: hipLaunchKernelGGL((moe_route_kernel<KPL, 4, true>), grid, dim3(256), 0, stream, w, ws, d); break;
+      case 2: hipLaunchKernelGGL((moe_route_kernel<KPL, 2, true>), grid, dim3(256), 0, stream, w, ws, d); break;
+      default: hipLaunchKernelGGL((moe_route_kernel<KPL, 1, true>), grid, dim3(256), 0, stream, w, ws, d); break;
+    }
+    return;
+  }
   switch (p) {
-    case 4: hipLaunchKernelGGL((moe_route_kernel<KPL, 4>), grid, dim3(256), 0, stream, w, ws, d); break;
-    case 2: hipLaunchKernelGGL((moe_route_kernel<KPL, 2>), grid, dim3(256), 0, stream, w, ws, d); break;
-    default: hipLaunchKernelGGL((moe_route_kernel<KPL, 1>), grid, dim3(256), 0, stream, w, ws, d); break;
+    case 4: hipLaunchKernelGGL((moe_route_kernel<KPL, 4, false>), grid, dim3(256), 0, stream, w, ws, d); break;
+    case 2: hipLaunchKernelGGL((moe_route_kernel<KPL, 2, false>), grid, dim3(256), 0, stream, w, ws, d); break;
+    default: hipLaunchKernelGGL((moe_route_kernel<KPL, 1, false>), grid, dim3(256), 0, stream, w, ws, d); break;
   }
 }
 

@@ -73,6 +73,18 @@ typedef enum {
   MOE_FMT_Q1_G128 = 3
 } moe_wfmt;
 
+/* The experts' input (the up/gate activation). */
+typedef enum {
+  /* FP8 E4M3 per 1x128 block of u = bf16(x * gamma), scale amax/448 in fp32,
+   * rstd applied after the dot (#85 Mod. row 10: FP8 activation blocks).  The
+   * default (0, so a zero-initialised config gets it). */
+  MOE_ACT_FP8_B128 = 0,
+  /* u itself (bf16), rstd applied after the dot: no activation rounding, for
+   * measuring what the FP8 blocks cost.  FP8 routed experts only (with
+   * MXFP4 routed experts the config is MOE_ERR_UNSUPPORTED). */
+  MOE_ACT_BF16 = 1
+} moe_afmt;
+
 /* flags */
 enum {
   /* Skip the dedup: every (row, pick) streams its expert separately.  For the
@@ -92,6 +104,7 @@ typedef struct {
   int32_t routed_fmt;   /* MOE_FMT_FP8_E4M3_B128 or MOE_FMT_MXFP4 */
   int32_t shared_fmt;   /* MOE_FMT_FP8_E4M3_B128 */
   uint32_t flags;       /* MOE_F_* */
+  int32_t act_fmt;      /* moe_afmt: MOE_ACT_FP8_B128 (0) or MOE_ACT_BF16 */
 } moe_decode_config;
 
 /* One stored matrix: codes and scales in the layout its format fixes. */
@@ -149,8 +162,8 @@ typedef struct {
   const uint8_t* grp_owner;  /* [max_groups, 2] (slot, row) of the group's first use */
   const uint8_t* grp_mask;   /* [max_groups] bit r set when row r uses the group */
   const uint8_t* grp_slot;   /* [max_groups, 8] slot where row r picked it, 0xFF if none */
-  const uint8_t* act_q;      /* [max_rows, H] FP8 activation codes */
-  const float* act_s;        /* [max_rows, H/128] their block scales */
+  const uint8_t* act_q;      /* [max_rows, H] FP8 activation codes (zero with MOE_ACT_BF16) */
+  const float* act_s;        /* [max_rows, H/128] their block scales (zero with MOE_ACT_BF16) */
   /* mid, per (row r, pick j) with j = 8 for the shared expert, at index
    * r * 9 + j, with stride mid_stride elements (a deduplicated expert's mid
    * appears under every (row, pick) that uses it): */

@@ -23,7 +23,7 @@ def shared_host(layer):
     return tuple(t.cpu().numpy() for t in layer.shared.expert(0))
 
 
-def oracle_for(layer, x, gpu_logits, nthreads=1, host_cache=None):
+def oracle_for(layer, x, gpu_logits, nthreads=1, host_cache=None, act_fmt=0):
     """Oracle step on the same inputs, selection anchored on the GPU's fp32
     logits.  Only the experts those logits pick are copied to the host."""
     R = x.shape[0]
@@ -36,7 +36,7 @@ def oracle_for(layer, x, gpu_logits, nthreads=1, host_cache=None):
     experts = {int(e): cache[int(e)] for e in np.unique(ids)}
     cfg = dict(hidden=layer.hidden, inter=layer.inter, n_experts=E,
                shared_inter=layer.shared_inter, rows=R, rms_eps=layer.rms_eps,
-               routed_fmt=layer.routed_fmt)
+               routed_fmt=layer.routed_fmt, act_fmt=act_fmt)
     if "shared" not in cache:
         cache["shared"] = shared_host(layer)
     out, dbg = O.moe_step(cfg, np_u16(x), np_u16(layer.gamma), np_u16(layer.router_w), experts,

@@ -21,7 +21,8 @@ def test_library_exports_every_declared_function():
 
 def cfg(**kw):
     base = dict(hidden=6144, inter=2048, n_experts=256, top_k=8, shared_inter=2048, max_rows=8,
-                rms_eps=1e-6, routed_fmt=B.FMT_FP8, shared_fmt=B.FMT_FP8, flags=0)
+                rms_eps=1e-6, routed_fmt=B.FMT_FP8, shared_fmt=B.FMT_FP8, flags=0,
+                act_fmt=B.ACT_FP8)
     base.update(kw)
     return B.Config(*base.values())
 
@@ -33,6 +34,8 @@ def test_workspace_size_supported_shapes():
     assert B.workspace_size(cfg(hidden=256, inter=128, n_experts=32, shared_inter=0)) > 0
     # without dedup every pick is its own group: more mid slots
     assert B.workspace_size(cfg(flags=B.F_NO_DEDUP, n_experts=32)) > B.workspace_size(cfg(n_experts=32))
+    # bf16 activations with FP8 experts
+    assert B.workspace_size(cfg(act_fmt=B.ACT_BF16)) == n8
 
 
 @pytest.mark.parametrize("kw", [dict(top_k=4), dict(hidden=6100), dict(inter=100),
@@ -40,7 +43,8 @@ def test_workspace_size_supported_shapes():
                                 dict(routed_fmt=B.FMT_Q1), dict(shared_fmt=B.FMT_MXFP4),
                                 dict(routed_fmt=B.FMT_MXFP4, inter=4224, shared_inter=4224),
                                 dict(flags=1 << 7), dict(hidden=32768), dict(max_rows=9),
-                                dict(max_rows=0)])
+                                dict(max_rows=0), dict(act_fmt=2), dict(act_fmt=-1),
+                                dict(act_fmt=B.ACT_BF16, routed_fmt=B.FMT_MXFP4)])
 def test_unsupported_configs(kw):
     assert B.workspace_size(cfg(**kw)) == 0
     h = ctypes.c_void_p()

@@ -40,14 +40,15 @@ def glm():
     return layer
 
 
-def _run(layer, x, max_rows=None, flags=0, cache=None, check_mid_codes=True):
+def _run(layer, x, max_rows=None, flags=0, cache=None, check_mid_codes=True, act_fmt=B.ACT_FP8):
     rows = x.shape[0]
-    runner = B.LayerRunner(layer, max_rows or rows, flags=flags)
+    runner = B.LayerRunner(layer, max_rows or rows, flags=flags, act_fmt=act_fmt)
     xd = x.to("cuda")
     out = runner.run(xd)
     torch.cuda.synchronize()
     gpu = runner.debug(rows)
-    ref_out, ref = P.oracle_for(layer, x, gpu["logits"], nthreads=NTHREADS, host_cache=cache)
+    ref_out, ref = P.oracle_for(layer, x, gpu["logits"], nthreads=NTHREADS, host_cache=cache,
+                                act_fmt=act_fmt)
     rep = P.compare(layer, x, gpu, out, ref_out, ref, check_mid_codes=check_mid_codes)
     return runner, out, gpu, rep
 
@@ -165,6 +166,29 @@ def test_glm_parity(glm, rows, mode):
     _say(f"glm rows={rows} mode={mode}")
     x = S.make_x(rows, glm.hidden, seed=3000 + 10 * rows + (mode == "corr"), mode=mode)
     _, _, gpu, rep = _run(glm, x, cache=glm.extra.setdefault("host", {}))
+    _say(rep)
+
+
+@pytest.mark.parametrize("rows", [1, 4, 8])
+def test_tiny_bf16_activations(tiny, rows):
+    """MOE_ACT_BF16: the experts take u itself (no FP8 activation blocks);
+    the same checks against the oracle in that mode, activation codes and
+    scales all zero on both sides; dedup on/off bitwise equal."""
+    _say(f"tiny bf16 activations rows={rows}")
+    x = S.make_x(rows, tiny.hidden, seed=2700 + rows, mode="corr")
+    _, out, gpu, rep = _run(tiny, x, act_fmt=B.ACT_BF16)
+    _say(rep)
+    assert not np.asarray(gpu["act_q"]).any() and not np.asarray(gpu["act_s"]).any()
+    off = B.LayerRunner(tiny, rows, flags=B.F_NO_DEDUP, act_fmt=B.ACT_BF16).run(x.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), off.view(torch.int16))
+
+
+@pytest.mark.parametrize("rows", [1, 8])
+def test_glm_bf16_activations(glm, rows):
+    _say(f"glm bf16 activations rows={rows}")
+    x = S.make_x(rows, glm.hidden, seed=2800 + rows, mode="corr")
+    _, _, _, rep = _run(glm, x, act_fmt=B.ACT_BF16, cache=glm.extra.setdefault("host", {}))
     _say(rep)
 
 
