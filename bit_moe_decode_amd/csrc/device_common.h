@@ -4,7 +4,29 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace moe {
+
+// Host side: sets kernel `fn`'s dynamic-LDS limit on the current device to at
+// least `bytes` when that is above the 64 KB default.  `raised` (kLdsDevices
+// slots, one per device, kept by the caller for this kernel) records what
+// each device already has, so the attribute call is made once per device and
+// size; the check and the call run under one lock, so concurrent callers
+// never leave a device below what a recorded size promises.
+constexpr int kLdsDevices = 64;
+inline hipError_t ensure_dyn_lds(const void* fn, size_t bytes, size_t* raised) {
+  if (bytes <= 65536) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && dev < kLdsDevices && raised[dev] >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess && dev >= 0 && dev < kLdsDevices) raised[dev] = bytes;
+  return e;
+}
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));

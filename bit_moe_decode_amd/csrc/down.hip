@@ -384,14 +384,10 @@ static int down_ring(int inter) {
 template <int RF, int P, int WPB, int T4>
 static hipError_t launch_one(int max_groups, size_t lds, const Weights& w, const Ws& ws,
                              const Dims& d, hipStream_t stream) {
-  static size_t raised = 0;  // the limit already set for this instantiation
-  if (lds > 65536 && lds > raised) {
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_down_kernel<RF, P, WPB, T4>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    raised = lds;
-  }
+  static size_t raised[kLdsDevices] = {};  // the limit set per device, this instantiation
+  const hipError_t e =
+      ensure_dyn_lds(reinterpret_cast<const void*>(&moe_down_kernel<RF, P, WPB, T4>), lds, raised);
+  if (e != hipSuccess) return e;
   const int per = d.H / (16 * WPB);
   const dim3 grid(per * (d.Is > 0 ? 1 : 0) +
                   (RF == kFmtMxfp4 ? per / T4 : per) * max_groups);

@@ -217,13 +217,10 @@ template <int RB>
 static hipError_t lb_nib_launch(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n,
                                 int k, hipStream_t stream) {
   const size_t sh = lb_nib_lds(RB);
-  static bool raised = false;
-  if (!raised && sh > 65536) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(lowbit_gemv_q1_nib_kernel<RB>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh) != hipSuccess)
-      return hipErrorInvalidValue;
-    raised = true;
-  }
+  static size_t raised[kLdsDevices] = {};  // the limit set per device
+  if (ensure_dyn_lds(reinterpret_cast<const void*>(lowbit_gemv_q1_nib_kernel<RB>), sh, raised) !=
+      hipSuccess)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(lowbit_gemv_q1_nib_kernel<RB>, dim3((n + RB - 1) / RB), dim3(256), sh,
                      stream, blocks, x, y, n, k);
   return hipGetLastError();
