@@ -65,6 +65,18 @@ def test_mxfp4_other_intermediate_sizes(inter):
         _say(_run(layer, x))
 
 
+@pytest.mark.parametrize("hidden,inter", [(16384, 256), (512, 4096)])
+def test_mxfp4_maximum_sizes(hidden, inter):
+    """MXFP4 at hidden 16384 and at the largest intermediate size it accepts
+    (4096: 131 KB of split mid in LDS per down block at 8 rows)."""
+    shape = dict(hidden=hidden, inter=inter, n_experts=32, shared_inter=inter, router_std=0.02)
+    layer = S.make_layer(shape, routed_fmt=S.FMT_MXFP4, seed=4400 + hidden, device="cuda")
+    for rows in (1, 8):
+        _say(f"mxfp4 hidden={hidden} inter={inter} rows={rows}")
+        x = S.make_x(rows, layer.hidden, seed=4500 + rows, mode="corr")
+        _say(_run(layer, x))
+
+
 def test_tiny_mxfp4_dedup_off_is_bitwise_equal(tiny4):
     x = S.make_x(8, tiny4.hidden, seed=4100, mode="corr").cuda()
     on = B.LayerRunner(tiny4, 8).run(x)

@@ -160,6 +160,21 @@ def test_other_intermediate_sizes(inter, shared):
         _say(rep)
 
 
+@pytest.mark.parametrize("hidden,inter", [(16384, 256), (256, 16384)])
+def test_maximum_hidden_and_intermediate(hidden, inter):
+    """The largest sizes the library accepts, one at a time (with a shared
+    expert): hidden 16384 (two rounds of 64 activation blocks per router
+    block, 32 K blocks per up/gate wave) and intermediate 16384 (a 128-block
+    down ring; at 8 rows 135 KB of dynamic LDS per down block)."""
+    shape = dict(hidden=hidden, inter=inter, n_experts=32, shared_inter=inter, router_std=0.02)
+    layer = S.make_layer(shape, seed=3500 + hidden, device="cuda")
+    for rows in (1, 8):
+        _say(f"hidden={hidden} inter={inter} rows={rows}")
+        x = S.make_x(rows, hidden, seed=3600 + rows, mode="corr")
+        _, _, _, rep = _run(layer, x)
+        _say(rep)
+
+
 @pytest.mark.parametrize("rows,mode", [(1, "indep"), (4, "indep"), (4, "corr"),
                                        (8, "indep"), (8, "corr")])
 def test_glm_parity(glm, rows, mode):
