@@ -160,6 +160,20 @@ def test_other_intermediate_sizes(inter, shared):
         _say(rep)
 
 
+def test_smallest_layer():
+    """The smallest accepted shapes: hidden 128 (one activation block, one K
+    block per up/gate slab), intermediate 128, 16 experts (8 rows then pick
+    most of them), with a shared expert, at 1 to 8 rows."""
+    shape = dict(hidden=128, inter=128, n_experts=16, shared_inter=128, router_std=0.05)
+    layer = S.make_layer(shape, seed=3700, device="cuda")
+    for rows in (1, 2, 5, 8):
+        _say(f"smallest layer rows={rows}")
+        x = S.make_x(rows, 128, seed=3800 + rows)
+        _, _, gpu, rep = _run(layer, x)
+        _say(rep)
+        assert int(np.asarray(gpu["n_groups"]).ravel()[0]) <= 16
+
+
 @pytest.mark.parametrize("hidden,inter", [(16384, 256), (256, 16384)])
 def test_maximum_hidden_and_intermediate(hidden, inter):
     """The largest sizes the library accepts, one at a time (with a shared
