@@ -161,8 +161,11 @@ __device__ __forceinline__ void route_block(const Ws& ws, const Dims& d, RouteSm
   }
   __syncthreads();
 
-  // gates: softmax of a row's 8 picked logits, in pick order
-  if (publish && tid < R) publish_gates(ws, tid, rs.zsel[tid], rs.ids[tid]);
+  // gates: softmax of a row's 8 picked logits, in pick order (on wave 1, so
+  // that they overlap the dedup on wave 0; one wave does both when the block
+  // has one)
+  const int gt0 = nw > 1 ? 64 : 0;
+  if (publish && tid >= gt0 && tid < gt0 + R) publish_gates(ws, tid - gt0, rs.zsel[tid - gt0], rs.ids[tid - gt0]);
 
   // dedup: lane p holds pick p in slot-major order (p = j*R + r).  Lanes with
   // the same expert are found with one ballot per ID bit; the lowest of them
@@ -213,10 +216,13 @@ __device__ __forceinline__ void route_block(const Ws& ws, const Dims& d, RouteSm
       ws.grp_owner[2 * tid] = rs.g_owner[tid][0];
       ws.grp_owner[2 * tid + 1] = rs.g_owner[tid][1];
       ws.grp_mask[tid] = (uint8_t)m;
+      uint64_t slots = 0, rows = 0;  // the 8 bytes of each, stored at once
       for (int r = 0; r < 8; r++) {
-        ws.grp_slot[tid * 8 + r] = rs.g_slot[tid][r];
-        ws.grp_rows[tid * 8 + r] = r < n ? rs.g_rows[tid][r] : (uint8_t)0;
+        slots |= (uint64_t)rs.g_slot[tid][r] << (8 * r);
+        if (r < n) rows |= (uint64_t)rs.g_rows[tid][r] << (8 * r);
       }
+      *reinterpret_cast<uint64_t*>(ws.grp_slot + tid * 8) = slots;
+      *reinterpret_cast<uint64_t*>(ws.grp_rows + tid * 8) = rows;
       ws.grp_nrows[tid] = (uint8_t)n;
     }
   }
