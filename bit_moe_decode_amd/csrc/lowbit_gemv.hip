@@ -65,22 +65,25 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_kernel(const uint8_t* __re
 
 // Nibble-table form, for K a multiple of 256 (an even number of groups: a row
 // is a whole number of 36-byte, dword-aligned pairs of groups).  Block = 256
-// threads = RB rows x KP = 256/RB parts of K.  Each thread reads the 36
-// bytes of its row's chunk straight from memory at the start of a round (the
-// lanes of a load touch one line per row, and the L2 keeps the block's rows
-// between rounds; staging the rows through LDS first measured slower, 23.5
-// against 21.4 us on the LM head).  K is taken in chunks of 256 inputs (two
-// groups, 64 positions of 4 inputs); in each round the block fills, for KP
-// chunks at once, a table of the signed sums of every position's 4 inputs
-// for all 16 nibble values,
+// threads = RB rows x KP = 256/RB parts of K.  K is taken in chunks of 256
+// inputs (two groups, 64 positions of 4 inputs), CH = KP * M chunks a round
+// (M = 1..5: all of K in one round when the round's tables fit).  Each thread
+// reads the 36 bytes of each of its row's chunks of the round straight from
+// memory at the start of the round (the lanes of a load touch one line per
+// row; staging the rows through LDS first measured slower, 23.5 against
+// 21.4 us on the LM head).  The block fills, for the CH chunks at once, a
+// table of the signed sums of every position's 4 inputs for all 16 nibble
+// values,
 //   T[p][v] = sum_{i<4} (bit i of v ? -x : +x)[256c + 4p + i],
-// and thread (row r, part q) adds T[p][nibble] over the 64 nibbles of chunk
-// c = round * KP + q of its row, scales each group's sum by its d and
+// and thread (row r, part q) adds T[p][nibble] over the 64 nibbles of chunks
+// c0 + q, c0 + q + KP, ... of its row, scales each group's sum by its d and
 // accumulates in fp32: one table read per 4 weights.  The parts of a row are
 // added in part order at the end.  The lanes of a wave read one position's
 // 16 entries at a time (a broadcast or a distinct bank each), and the tables
 // of different parts are offset by 16 floats so that they use different banks.
 constexpr int kLbTab = 64 * 16 + 16;  // floats per chunk table, padded
+// chunks whose tables one round may hold (19 x 4160 bytes: two blocks a CU)
+constexpr int kLbRoundChunks = 19;
 
 // Bits o .. o+3 of v as one v_bfe_u32 (the compiler would otherwise split a
 // constant-offset field extract into a shift and a mask).
@@ -150,14 +153,15 @@ __device__ __forceinline__ void lb_fill_pos(float* t, uint2 xv) {
     *reinterpret_cast<float4*>(t + 4 * hb) = float4{a0 + b[hb], a1 + b[hb], a2 + b[hb], a3 + b[hb]};
 }
 
-template <int RB>
+template <int RB, int M>
 __global__ __launch_bounds__(256) void lowbit_gemv_q1_nib_kernel(
     const uint8_t* __restrict__ blocks, const uint16_t* __restrict__ x,
     uint16_t* __restrict__ y, int n, int k) {
   constexpr int KP = 256 / RB;
+  constexpr int CH = KP * M;  // chunks a round: part q takes q, q + KP, ..
   extern __shared__ __align__(16) uint8_t smem[];
-  float* tab = reinterpret_cast<float*>(smem);                    // [KP][kLbTab]
-  float* red = tab + KP * kLbTab;                                  // [KP][RB]
+  float* tab = reinterpret_cast<float*>(smem);                    // [CH][kLbTab]
+  float* red = tab + CH * kLbTab;                                  // [KP][RB]
   const int tid = threadIdx.x;
   const int G = k / 128, nch = G / 2, rb = 18 * G;
   const int r0 = blockIdx.x * RB;
@@ -166,40 +170,45 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_nib_kernel(
   const int rl = tid % RB, part = tid / RB;
   const int rowl = rl < nr ? rl : nr - 1;  // threads past n decode the last row
   const uint32_t* myrow = reinterpret_cast<const uint32_t*>(blocks + (size_t)(r0 + rowl) * rb);
-  const float* mytab = tab + part * kLbTab;
 
   // table positions of this thread in a round: e = tid + 256 j (j < NE), the
   // inputs of each loaded one round ahead
-  constexpr int NE = KP >= 4 ? KP / 4 : 1;
+  constexpr int NE = (CH * 64 + 255) / 256;
   uint2 xn[NE];
   auto xload = [&](int c0) {
 #pragma unroll
     for (int j = 0; j < NE; j++) {
       const int e = tid + 256 * j;
-      if (e < KP * 64 && c0 + (e >> 6) < nch)
+      if (e < CH * 64 && c0 + (e >> 6) < nch)
         xn[j] = *reinterpret_cast<const uint2*>(x + 256 * c0 + 4 * e);
     }
   };
   xload(0);
   float acc = 0.f;
-  for (int c0 = 0; c0 < nch; c0 += KP) {
-    // this thread's chunk of its row, loaded before the table fill
-    uint32_t w9[9];
-    if (c0 + part < nch) {
+  for (int c0 = 0; c0 < nch; c0 += CH) {
+    // this thread's chunks of its row, loaded before the table fill
+    uint32_t w9[M][9];
 #pragma unroll
-      for (int i = 0; i < 9; i++) w9[i] = myrow[9 * (c0 + part) + i];
+    for (int m = 0; m < M; m++) {
+      const int c = c0 + part + KP * m;
+      if (c < nch) {
+#pragma unroll
+        for (int i = 0; i < 9; i++) w9[m][i] = myrow[9 * c + i];
+      }
     }
-    // ---- tables of chunks c0 .. c0 + KP - 1: one position (4 inputs) at a time
+    // ---- tables of chunks c0 .. c0 + CH - 1: one position (4 inputs) at a time
 #pragma unroll
     for (int j = 0; j < NE; j++) {
       const int e = tid + 256 * j;
-      if (e < KP * 64 && c0 + (e >> 6) < nch)
+      if (e < CH * 64 && c0 + (e >> 6) < nch)
         lb_fill_pos(tab + (e >> 6) * kLbTab + (e & 63) * 16, xn[j]);
     }
-    if (c0 + KP < nch) xload(c0 + KP);
+    if (c0 + CH < nch) xload(c0 + CH);
     __syncthreads();
-    if (c0 + part < nch) acc = lb_chunk(w9, mytab, acc);
-    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; m++)
+      if (c0 + part + KP * m < nch) acc = lb_chunk(w9[m], tab + (part + KP * m) * kLbTab, acc);
+    if (c0 + CH < nch) __syncthreads();
   }
   red[part * RB + rl] = acc;
   __syncthreads();
@@ -211,25 +220,27 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_nib_kernel(
   }
 }
 
-static size_t lb_nib_lds(int rbk) { return (size_t)(256 / rbk) * kLbTab * 4 + 256 * 4; }
+static size_t lb_nib_lds(int rbk, int m) { return (size_t)(256 / rbk) * m * kLbTab * 4 + 256 * 4; }
 
-template <int RB>
+template <int RB, int M>
 static hipError_t lb_nib_launch(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n,
                                 int k, hipStream_t stream) {
-  const size_t sh = lb_nib_lds(RB);
+  const size_t sh = lb_nib_lds(RB, M);
   static size_t raised[kLdsDevices] = {};  // the limit set per device
-  if (ensure_dyn_lds(reinterpret_cast<const void*>(lowbit_gemv_q1_nib_kernel<RB>), sh, raised) !=
-      hipSuccess)
+  if (ensure_dyn_lds(reinterpret_cast<const void*>(lowbit_gemv_q1_nib_kernel<RB, M>), sh,
+                     raised) != hipSuccess)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lowbit_gemv_q1_nib_kernel<RB>, dim3((n + RB - 1) / RB), dim3(256), sh,
+  hipLaunchKernelGGL((lowbit_gemv_q1_nib_kernel<RB, M>), dim3((n + RB - 1) / RB), dim3(256), sh,
                      stream, blocks, x, y, n, k);
   return hipGetLastError();
 }
 
 hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
                             hipStream_t stream) {
-  // the nibble-table form: rows per block the largest of 128, 64, 32 that
-  // gives 2048 blocks, else the largest that gives 256, else 16
+  // the nibble-table form: rows per block RB the largest of 128, 64, 32 that
+  // gives 2048 blocks, else the largest that gives 256, else 16; chunks per
+  // thread and round M the fewest (up to 5) that take all of K in one round,
+  // as long as the round's tables stay within kLbRoundChunks chunks
   if (k % 256 == 0) {
     int rbk = 16;
     for (int want : {2048, 256}) {
@@ -237,12 +248,26 @@ hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* 
         if ((n + c - 1) / c >= want) rbk = c;
       if (rbk != 16) break;
     }
-    switch (rbk) {
-      case 128: return lb_nib_launch<128>(blocks, x, y, n, k, stream);
-      case 64: return lb_nib_launch<64>(blocks, x, y, n, k, stream);
-      case 32: return lb_nib_launch<32>(blocks, x, y, n, k, stream);
-      default: return lb_nib_launch<16>(blocks, x, y, n, k, stream);
+    const int nch = k / 256, kp = 256 / rbk;
+    int m = (nch + kp - 1) / kp;
+    if (m > 5) m = 5;
+    while (m > 1 && kp * m > kLbRoundChunks) m--;
+#define LB_CASE(R)                                                           \
+  case R:                                                                    \
+    switch (m) {                                                             \
+      case 5: return lb_nib_launch<R, 5>(blocks, x, y, n, k, stream);        \
+      case 4: return lb_nib_launch<R, 4>(blocks, x, y, n, k, stream);        \
+      case 3: return lb_nib_launch<R, 3>(blocks, x, y, n, k, stream);        \
+      case 2: return lb_nib_launch<R, 2>(blocks, x, y, n, k, stream);        \
+      default: return lb_nib_launch<R, 1>(blocks, x, y, n, k, stream);       \
     }
+    switch (rbk) {
+      LB_CASE(128)
+      LB_CASE(64)
+      LB_CASE(32)
+      LB_CASE(16)
+    }
+#undef LB_CASE
   }
   int rows_blocks = (n + 3) / 4;
   int grid = rows_blocks < 1024 ? rows_blocks : 1024;
