@@ -4,7 +4,11 @@
 Workload: a GLM-scale MoE layer (hidden 6144, 256 routed experts of
 intermediate 2048 with FP8 E4M3 weights and 128x128 fp32 block scales, top-8,
 one always-on FP8 shared expert of intermediate 2048), decoded for 1 row; the
-same layer is also timed at 4 and 8 independent rows.  All inputs are seeded,
+same layer is also timed at 2, 4 and 8 independent rows, at 4 and 8 correlated
+rows (x_i = 0.8 x_0 + 0.6 N(0,1), so rows share experts and the dedup table is
+smaller), with MXFP4 routed experts at 1 and 8 rows, and as the per-GPU share
+of an 8- and a 4-way split of the intermediate dimension (intermediate 256 and
+512, same hidden size, experts and router) at 1, 4 and 8 rows.  All inputs are seeded,
 synthetic and already resident in HBM when the timed region starts.  Eight
 copies of the layer's weights are rotated step by step so that no step finds
 another step's weights in the 256 MB MALL or the L2s; a pool of 16 token rows
@@ -154,11 +158,11 @@ def copy_stream_gbs(torch):
     return gbs
 
 
-def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base):
+def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base, mode="indep"):
     stream = torch.cuda.current_stream()
     runner = B.LayerRunner(layer, rows, stream=stream)
     weights = [B.LayerRunner.weights_for(c) for c in copies]
-    pool = [S.make_x(rows, layer.hidden, seed=seed_base + t).cuda() for t in range(POOL)]
+    pool = [S.make_x(rows, layer.hidden, seed=seed_base + t, mode=mode).cuda() for t in range(POOL)]
     out = torch.empty(rows, layer.hidden, dtype=torch.bfloat16, device="cuda")
     # distinct experts of each pool entry (selection does not depend on the copy)
     dvals = []
@@ -263,6 +267,22 @@ def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base):
                 weights=weights, dvals=dvals)
 
 
+def row_summary(r):
+    """The figures of one time_rows result that go into the JSON line."""
+    return {"us_per_step": round(r["us_per_step"], 2), "gbs": round(r["gbs"], 1),
+            "frac_of_peak": round(r["frac"], 4), "distinct_experts": r["d_mean"],
+            "bytes_per_step": int(r["bytes_per_step"]),
+            "kernel_us": {k: round(t, 2) for k, t in r["kernel_us"].items()},
+            "kernel_alone_us": {k: round(t, 2) for k, t in r["alone_us"].items()},
+            "graph_replay": {k: round(t, 2) for k, t in r["graph"].items()}}
+
+
+# Per-GPU expert shares of the GLM layer when its intermediate dimension is
+# split over 8 or 4 GPUs (each GPU streams 1/8 or 1/4 of every selected
+# expert); same hidden size, experts and router.
+TP_SHARES = (("tp8_inter256", 256), ("tp4_inter512", 512))
+
+
 LOWBIT_SHAPES = (("mlp_up_gate", 9728, 2560), ("mlp_down", 2560, 9728), ("lm_head", 151936, 2560))
 
 
@@ -364,12 +384,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--rows", default="1,4,8")
+    ap.add_argument("--rows", default="1,2,4,8")
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lowbit", action="store_true")
     ap.add_argument("--no-mxfp4", action="store_true")
+    ap.add_argument("--no-corr", action="store_true")
+    ap.add_argument("--no-tp-share", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the decode step has no multi-GPU path in this "
@@ -412,10 +434,21 @@ def main():
     if not args.no_cpu_baseline and main_rows == 1:
         log("timing the oracle on the host")
         cpu, err = cpu_baseline(torch, base, m, args.cpu_seconds)
+    corr = None
+    if not args.no_corr:
+        # correlated rows (x_i = 0.8 x_0 + 0.6 N(0,1)): rows share experts, the
+        # dedup table has fewer groups and each is streamed once
+        corr = {}
+        for rows in (4, 8):
+            r = time_rows(torch, B, S, base, copies, rows, args.steps, args.warmup,
+                          seed_base=8000 + 100 * rows, mode="corr")
+            log(f"corr rows={rows}: {r['us_per_step']:.1f} us/step, {r['gbs']:.0f} GB/s "
+                f"({100 * r['frac']:.1f}% of peak), D={r['d_mean']:.1f}, kernels {r['kernel_us']}")
+            corr[str(rows)] = row_summary(r)
     mx = None
     if not args.no_mxfp4:
         log("generating the GLM-scale layer with MXFP4 routed experts")
-        del copies
+        copies = None
         torch.cuda.empty_cache()
         mbase = S.make_layer("glm", routed_fmt=S.FMT_MXFP4, seed=1002, device="cuda")
         mcopies = layer_copies(S, mbase, args.copies)
@@ -433,6 +466,28 @@ def main():
                              "graph_replay": {k: round(t, 2) for k, t in r["graph"].items()}}
         del mcopies, mbase
         torch.cuda.empty_cache()
+
+    tp = None
+    if not args.no_tp_share:
+        copies = None
+        torch.cuda.empty_cache()
+        tp = {}
+        for name, inter in TP_SHARES:
+            shape = dict(S.SHAPES["glm"], inter=inter, shared_inter=inter)
+            log(f"generating the {name} share of the GLM-scale layer")
+            tbase = S.make_layer(shape, seed=1003, device="cuda")
+            tcopies = layer_copies(S, tbase, args.copies)
+            torch.cuda.synchronize()
+            tp[name] = {}
+            for rows in (1, 4, 8):
+                r = time_rows(torch, B, S, tbase, tcopies, rows, args.steps, args.warmup,
+                              seed_base=9000 + 100 * rows)
+                log(f"{name} rows={rows}: {r['us_per_step']:.1f} us/step, {r['gbs']:.0f} GB/s "
+                    f"({100 * r['frac']:.1f}% of peak), D={r['d_mean']:.1f}, "
+                    f"kernels {r['kernel_us']}")
+                tp[name][str(rows)] = row_summary(r)
+            del tcopies, tbase
+            torch.cuda.empty_cache()
 
     lowbit = None
     if not args.no_lowbit:
@@ -487,7 +542,9 @@ def main():
                     for r, v in results.items()},
         "hot_us_per_step": hot,
         "copy_stream_gbs": round(stream_gbs, 1),
+        "corr_rows": corr,
         "mxfp4_routed": mx,
+        "tp_share": tp,
         "lowbit_gemv": lowbit,
     }
     print(json.dumps(line), flush=True)
