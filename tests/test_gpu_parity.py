@@ -189,7 +189,7 @@ def test_maximum_hidden_and_intermediate(hidden, inter):
         _say(rep)
 
 
-@pytest.mark.parametrize("rows,mode", [(1, "indep"), (4, "indep"), (4, "corr"),
+@pytest.mark.parametrize("rows,mode", [(1, "indep"), (2, "corr"), (4, "indep"), (4, "corr"),
                                        (8, "indep"), (8, "corr")])
 def test_glm_parity(glm, rows, mode):
     _say(f"glm rows={rows} mode={mode}")
@@ -219,6 +219,22 @@ def test_glm_bf16_activations(glm, rows):
     x = S.make_x(rows, glm.hidden, seed=2800 + rows, mode="corr")
     _, _, _, rep = _run(glm, x, act_fmt=B.ACT_BF16, cache=glm.extra.setdefault("host", {}))
     _say(rep)
+
+
+@pytest.mark.parametrize("inter", [256, 512])
+def test_glm_intermediate_shares(inter):
+    """The share of the GLM-scale layer one GPU streams when the intermediate
+    dimension is split over 8 or 4 GPUs (intermediate 256 or 512, the same
+    hidden size, 256 experts and router, a shared expert of the same share;
+    the benchmark's seed), at 1, 2, 4 and 8 rows, independent and correlated."""
+    shape = dict(S.SHAPES["glm"], inter=inter, shared_inter=inter)
+    layer = S.make_layer(shape, seed=1003, device="cuda")
+    cache = {}
+    for rows, mode in ((1, "indep"), (2, "corr"), (4, "indep"), (8, "corr")):
+        _say(f"glm share inter={inter} rows={rows} mode={mode}")
+        x = S.make_x(rows, layer.hidden, seed=9100 + rows, mode=mode)
+        _, _, _, rep = _run(layer, x, cache=cache)
+        _say(rep)
 
 
 def test_glm_dedup_off_is_bitwise_equal(glm):
