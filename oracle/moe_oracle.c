@@ -523,6 +523,35 @@ int orc_lowbit_gemv_q1(const uint8_t* blocks, const uint16_t* x, int n, int k, i
   return ORC_OK;
 }
 
+/* Dense decode GEMV over FP8 weights, for the tail after the last layer (the
+ * LM-head GEMV of the #85 page's tail launch, Mod. row 24; the page names
+ * no weight format for it, and FP8 E4M3 with one fp32 scale per 128x128
+ * block is the format of every other weight stream on the path).  READING:
+ * the inputs are bf16 rows used as they are, no activation quantisation.
+ *   y[r][n] = sum_k dec(W[n][k]) * s[n/128][k/128] * x[r][k]
+ * accumulated in double (each product is exact in double); y16 = bf16 RNE of
+ * y.  W: codes [n][k]; s: [n/128][k/128]; x: [rows][k]. */
+int orc_gemv_fp8(const uint8_t* codes, const float* scales, const uint16_t* x, int rows, int n,
+                 int k, int nthreads, uint16_t* y16, double* y) {
+  if (rows < 0 || n < 0 || k <= 0 || n % 128 || k % 128) return ORC_ERR;
+  const int kb_n = k / 128;
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+  for (int row = 0; row < n; row++) {
+    for (int r = 0; r < rows; r++) {
+      double acc = 0.0;
+      for (int kk = 0; kk < k; kk++) {
+        const double w = orc_dec_e4m3(codes[(size_t)row * k + kk]);
+        const double s = (double)scales[(size_t)(row / 128) * kb_n + kk / 128];
+        acc += w * s * orc_dec_bf16(x[(size_t)r * k + kk]);
+      }
+      if (y) y[(size_t)r * n + row] = acc;
+      if (y16) y16[(size_t)r * n + row] = orc_round_bf16(acc);
+    }
+  }
+  return ORC_OK;
+}
+
 /* ---------------------------------------------- array forms for the tests */
 
 void orc_dec_e4m3_n(const uint8_t* c, int n, double* v) {

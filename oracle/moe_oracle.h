@@ -111,6 +111,10 @@ void orc_round_bf16_n(const double* v, int n, uint16_t* h);
 int orc_lowbit_gemv_q1(const uint8_t* blocks, const uint16_t* x, int n, int k, int nthreads,
                        uint16_t* y, double* y_f64);
 
+/* FP8 E4M3 weights with one fp32 scale per 128x128 block, bf16 input rows */
+int orc_gemv_fp8(const uint8_t* codes, const float* scales, const uint16_t* x, int rows, int n,
+                 int k, int nthreads, uint16_t* y16, double* y);
+
 #ifdef __cplusplus
 }
 #endif

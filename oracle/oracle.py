@@ -267,3 +267,21 @@ def lowbit_gemv_q1(blocks, x, n, k, nthreads=1):
     if rc != 0:
         raise ValueError("orc_lowbit_gemv_q1 failed")
     return y, yf
+
+
+def gemv_fp8(codes, scales, x, nthreads=1):
+    """codes uint8 [n, k] (E4M3), scales float32 [n/128, k/128], x uint16 [rows, k]
+    (bf16) -> (y uint16 [rows, n] bf16, y_f64 [rows, n])."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    sc = np.ascontiguousarray(scales, dtype=np.float32)
+    xx = np.ascontiguousarray(np.atleast_2d(x), dtype=np.uint16)
+    rows, k = xx.shape
+    n = c.shape[0]
+    assert c.shape == (n, k) and sc.shape == (n // 128, k // 128)
+    y = np.zeros((rows, n), np.uint16)
+    yf = np.zeros((rows, n), np.float64)
+    rc = lib().orc_gemv_fp8(_p(c), _p(sc), _p(xx), ctypes.c_int(rows), ctypes.c_int(n),
+                            ctypes.c_int(k), ctypes.c_int(nthreads), _p(y), _p(yf))
+    if rc != 0:
+        raise ValueError("orc_gemv_fp8 failed")
+    return y, yf
