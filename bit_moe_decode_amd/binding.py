@@ -214,6 +214,20 @@ def lowbit_gemv(blocks, x, y, n, k, rows=1, stream=None, fmt=FMT_Q1):
         raise MoeError(st, "lowbit_gemv")
 
 
+def gemv_fp8(codes, scales, x, y, n, k, rows=1, stream=None):
+    """lowbit_gemv with FP8 weights: codes uint8 [n, k], scales float32
+    [n/128, k/128], x bf16 [rows, k], y bf16 [rows, n] (device tensors)."""
+    st = gemv_fp8_status(codes, scales, x, y, n, k, rows, stream)
+    if st != MOE_OK:
+        raise MoeError(st, "lowbit_gemv")
+
+
+def gemv_fp8_status(codes, scales, x, y, n, k, rows=1, stream=None):
+    m = LowbitMatrix(FMT_FP8, int(n), int(k), codes.data_ptr() if codes is not None else None,
+                     scales.data_ptr() if scales is not None else None)
+    return lib().lowbit_gemv(ctypes.byref(m), _ptr(x), int(rows), _ptr(y), _stream(stream))
+
+
 def lowbit_gemv_status(blocks, x, y, n, k, rows=1, stream=None, fmt=FMT_Q1):
     m = LowbitMatrix(fmt, int(n), int(k), blocks.data_ptr() if blocks is not None else None, None)
     return lib().lowbit_gemv(ctypes.byref(m), _ptr(x), int(rows), _ptr(y), _stream(stream))

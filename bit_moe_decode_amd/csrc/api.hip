@@ -19,6 +19,8 @@ hipError_t launch_combine(const Ws& ws, const Dims& d, uint16_t* out, hipStream_
 int upgate_k_parts(int hidden, int routed_fmt);
 hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
                             hipStream_t stream);
+hipError_t launch_gemv_fp8(const uint8_t* codes, const float* scales, const uint16_t* x,
+                           uint16_t* y, int rows, int n, int k, hipStream_t stream);
 
 __global__ void moe_fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
@@ -340,6 +342,24 @@ const char* moe_status_string(moe_status s) {
 moe_status lowbit_gemv(const lowbit_matrix* w, const uint16_t* x, int32_t rows, uint16_t* y,
                        hipStream_t stream) {
   if (!w) return MOE_ERR_INVALID_ARG;
+  if (w->fmt == MOE_FMT_FP8_E4M3_B128) {
+    // FP8 weights in 128x128 blocks, 1 to 8 bf16 input rows
+    if (w->n < 0 || w->k <= 0) return MOE_ERR_INVALID_ARG;
+    if (w->n % 128 || w->k % 128) return MOE_ERR_UNSUPPORTED;
+    if (rows < 0) return MOE_ERR_INVALID_ARG;
+    if (rows == 0 || w->n == 0) return MOE_OK;
+    if (rows > 8) return MOE_ERR_UNSUPPORTED;
+    if (!w->codes || !w->scales || !x || !y || !aligned16(w->codes) || !aligned16(x) ||
+        ((uintptr_t)w->scales & 3u) || ((uintptr_t)y & 1u))
+      return MOE_ERR_INVALID_ARG;
+    const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
+    if (xa < ya + (size_t)rows * w->n * 2 && ya < xa + (size_t)rows * w->k * 2)
+      return MOE_ERR_INVALID_ARG;
+    if (launch_gemv_fp8(static_cast<const uint8_t*>(w->codes), static_cast<const float*>(w->scales),
+                        x, y, rows, w->n, w->k, stream) != hipSuccess)
+      return MOE_ERR_DEVICE;
+    return MOE_OK;
+  }
   if (w->fmt != MOE_FMT_Q1_G128) return MOE_ERR_UNSUPPORTED;
   if (w->n < 0 || w->k <= 0) return MOE_ERR_INVALID_ARG;
   if (w->k % 128 || w->k > 16384) return MOE_ERR_UNSUPPORTED;

@@ -1,0 +1,119 @@
+// dense_gemv.hip -- decode GEMV over FP8 E4M3 weights with one fp32 scale per
+// 128x128 block, against 1 to 8 bf16 input rows: the tail's LM-head GEMV after
+// the last layer (#85 Mod. row 24: a tail wave keeps its next weights in
+// flight while the current tile is reduced and stored).
+//   y[r][n] = bf16( sum_k dec(W[n][k]) * s[n/128][k/128] * x[r][k] )
+//
+// Block = 4 waves = 4/KS slabs of 16 weight rows x KS parts of K (KS the
+// largest of 4, 2, 1 dividing K/128).  A wave streams its slab's K part: per
+// 128-wide K block its lanes load the 16 rows row-contiguously (8 lanes per
+// 128-byte line, nontemporal: every weight byte is read once), P K blocks in
+// flight (P the largest of 4, 2, 1 dividing the part's K blocks, so every
+// issued load is used).  Each K block is re-laid through the wave's LDS tile
+// into MFMA operand order; per 32 inputs a lane converts the 8 codes of row
+// l%16 at inputs 8(l/16) .. +8 to bf16 (exact) and runs one 16x16x32 bf16 MFMA
+// against the input rows at the same inputs (the MFMA's columns are the input
+// rows; columns past them repeat row 0 and are not stored).  The K block's
+// fp32 result is scaled by its weight scale and accumulated.  The block then
+// adds its K parts in part order through LDS and stores y as bf16.
+#include "device_common.h"
+
+namespace moe {
+
+struct DgStage {
+  u32x4 w0, w1;  // rows l/8 and 8 + l/8 of the slab, 16-byte chunk l%8
+  u32x4 a[4];    // the lane's input row at inputs 32s + 8(l/16) .. +8, s = 0..3
+  float sw;      // weight block scale
+};
+
+template <int P>
+__global__ __launch_bounds__(256) void dense_gemv_fp8_kernel(
+    const uint8_t* __restrict__ codes, const float* __restrict__ scales,
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int rows, int n, int k, int ks) {
+  __shared__ __align__(16) uint8_t s_tile[4][kTileBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int spb = 4 / ks;  // slabs per block
+  const int slab = blockIdx.x * spb + wv / ks, kp = wv % ks;
+  const int n0 = slab * 16;
+  const int nkb = k / 128, nk = nkb / ks, kb0 = kp * nk;
+
+  const uint8_t* pw = codes + (size_t)(n0 + (lane >> 3)) * k + (lane & 7) * 16 + (size_t)kb0 * 128;
+  const size_t r8 = (size_t)8 * k;
+  const float* psw = scales + (size_t)(n0 / 128) * nkb + kb0;
+  const uint16_t* pa = x + (size_t)(col < rows ? col : 0) * k + 8 * g + (size_t)kb0 * 128;
+  uint8_t* tile = s_tile[wv];
+
+  auto issue = [&](DgStage& st, int kk) {
+    const size_t o = (size_t)kk * 128;  // bytes of a weight row, elements of an input row
+    st.w0 = ld_nt16(pw + o);
+    st.w1 = ld_nt16(pw + r8 + o);
+#pragma unroll
+    for (int s = 0; s < 4; s++) st.a[s] = ld16(pa + o + 32 * s);
+    st.sw = psw[kk];
+  };
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](DgStage& st) {
+    tile_put(tile, lane, st.w0, st.w1);
+    asm volatile("" ::: "memory");
+    v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const v8bf a = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(tile + col * kTileStride + 32 * s + 8 * g));
+      c = mfma_bf16(a, __builtin_bit_cast(v8bf, st.a[s]), c);
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int v = 0; v < 4; v++) acc[v] = fmaf(c[v], st.sw, acc[v]);
+  };
+  DgStage st[P];
+#pragma unroll
+  for (int p = 0; p < P; p++) issue(st[p], p);
+  for (int k0 = 0; k0 < nk - P; k0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+      consume(st[p]);
+      issue(st[p], k0 + P + p);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; p++) consume(st[p]);
+  pin4(acc);  // the MFMAs run with every lane, before any divergent use
+
+  // ---- K parts -> y.  Each wave parks its 16 x 16 sums in its own tile,
+  // column-major (weight row i, input row c at c*16 + i); lane l holds rows
+  // 4(l/16) .. +4 of column l%16.
+  float* part = reinterpret_cast<float*>(tile);
+  __syncthreads();  // every wave is done with its tile's weights
+  *reinterpret_cast<v4f*>(part + col * 16 + 4 * g) = v4f{acc[0], acc[1], acc[2], acc[3]};
+  __syncthreads();
+  const int c = tid >> 4, i = tid & 15;  // input row c, weight row i of each slab
+  if (c >= rows) return;
+  for (int s = 0; s < spb; s++) {
+    float v = reinterpret_cast<const float*>(s_tile[s * ks])[c * 16 + i];
+    for (int q = 1; q < ks; q++) v += reinterpret_cast<const float*>(s_tile[s * ks + q])[c * 16 + i];
+    y[(size_t)c * n + (blockIdx.x * spb + s) * 16 + i] = f32_to_bf16(v);
+  }
+}
+
+// K parts of a slab: the largest of 4, 2, 1 dividing K/128; ring depth: the
+// largest of 4, 2, 1 dividing a part's K blocks.
+hipError_t launch_gemv_fp8(const uint8_t* codes, const float* scales, const uint16_t* x,
+                           uint16_t* y, int rows, int n, int k, hipStream_t stream) {
+  const int nkb = k / 128;
+  const int ks = nkb % 4 == 0 ? 4 : (nkb % 2 == 0 ? 2 : 1);
+  const int nk = nkb / ks;
+  const dim3 grid(n / (16 * (4 / ks)));  // n is a multiple of 128, so of 16 * (4 / ks)
+  if (nk % 4 == 0)
+    hipLaunchKernelGGL(dense_gemv_fp8_kernel<4>, grid, dim3(256), 0, stream, codes, scales, x, y,
+                       rows, n, k, ks);
+  else if (nk % 2 == 0)
+    hipLaunchKernelGGL(dense_gemv_fp8_kernel<2>, grid, dim3(256), 0, stream, codes, scales, x, y,
+                       rows, n, k, ks);
+  else
+    hipLaunchKernelGGL(dense_gemv_fp8_kernel<1>, grid, dim3(256), 0, stream, codes, scales, x, y,
+                       rows, n, k, ks);
+  return hipGetLastError();
+}
+
+}  // namespace moe

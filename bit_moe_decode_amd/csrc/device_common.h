@@ -231,6 +231,17 @@ __device__ __forceinline__ v8i cat8(const u32x4& lo, const u32x4& hi) {
 // 16x16x32 bf16 MFMA, fp32 accumulate.  A: lane l holds row l%16, K
 // 8*(l/16) .. +8; B: lane l holds column l%16, same K; D: lane l holds rows
 // 4*(l/16)+v of column l%16 (layout checked on the device).
+// Eight E4M3 codes (c.x bytes 0..3, then c.y) as eight bf16 values: every
+// E4M3 value is a bf16 value, so the hardware conversion with scale 1 is exact.
+typedef __bf16 v2bf_u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v8bf fp8x8_to_bf16(uint2 c) {
+  const v2bf_u p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false);
+  const v2bf_u p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true);
+  const v2bf_u p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false);
+  const v2bf_u p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true);
+  return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

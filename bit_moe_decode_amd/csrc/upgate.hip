@@ -153,14 +153,6 @@ struct UgStageB {
   u32x4 g0, g1, u0, u1, a[4];
   float sg, su;
 };
-typedef __bf16 v2bf_u __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ v8bf fp8x8_to_bf16(uint2 c) {
-  const v2bf_u p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false);
-  const v2bf_u p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true);
-  const v2bf_u p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false);
-  const v2bf_u p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true);
-  return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
 template <int P>
 __device__ __forceinline__ void ug_fp8_bf16a(const Weights& w, const Ws& ws, const Dims& d,
                                              UgJob j, int kb0, int nk, uint8_t* tg, uint8_t* tu,

@@ -9,7 +9,7 @@
  *   up/gate GEMV over low-bit weights -> SiLU * gate, mid re-quantised to FP8
  *   per 1x128 block -> down GEMV -> gate-weighted combine with a shared expert.
  * A second entry point, lowbit_gemv, is a dense decode GEMV over 1-bit
- * group-128 weights.
+ * group-128 weights or, for the LM head after the last layer, FP8 weights.
  *
  * Sources.  The operations follow the body of sgl-amd-mono PR #85 ("...MoE
  * expert dedup and weight loads, kernarg reload, LM-head loads"), quoted on the
@@ -58,7 +58,7 @@ typedef enum {
 typedef enum {
   /* FP8 E4M3 (OCP E4M3FN, largest finite 448) codes uint8 [N, K] with one fp32
    * scale per 128x128 block, scales float [N/128, K/128] (#85 Mod. rows 18, 21:
-   * FP8 expert weights). */
+   * FP8 expert weights; also lowbit_gemv's FP8 form). */
   MOE_FMT_FP8_E4M3_B128 = 1,
   /* MXFP4: E2M1 codes packed two per byte, element 2i in the low nibble,
    * uint8 [N, K/2], with one E8M0 exponent per 32 elements along K, uint8
@@ -204,13 +204,29 @@ void moe_decode_destroy(moe_decode_ctx* ctx);
 
 const char* moe_status_string(moe_status s);
 
-/* Dense decode GEMV over 1-bit group-128 weights (1-Bit Turbo, Q1_0_G128):
+/* Dense decode GEMV, in one of two weight formats.
+ *
+ * MOE_FMT_Q1_G128 -- 1-bit group-128 weights (1-Bit Turbo, Q1_0_G128):
  *   y[n] = bf16( sum_g d[n,g] * sum_{k in g} sign[n,k] * x[k] ),
- * x used as bf16 directly, fp32 accumulation.
- *  w->fmt must be MOE_FMT_Q1_G128; w->k a multiple of 128; w->codes points to
- *  the [N, K/128, 18] blocks (device); w->scales is unused (the scales are in
- *  the blocks).  rows must be 1 (the reference path is batch 1); 0 is a no-op.
- *  x bf16 [K], y bf16 [N] (device, no overlap). */
+ * x used as bf16 directly, fp32 accumulation.  w->k a multiple of 128 (at
+ * most 16384); w->codes points to the [N, K/128, 18] blocks (device);
+ * w->scales is unused (the scales are in the blocks).  rows must be 1 (the
+ * reference path is batch 1).  x bf16 [K], y bf16 [N].
+ *
+ * MOE_FMT_FP8_E4M3_B128 -- FP8 weights with one fp32 scale per 128x128 block,
+ * for the tail's LM-head GEMV after the last layer (#85 Mod. row 24: the tail
+ * keeps its LM-head weight loads in flight across its tiles):
+ *   y[r][n] = bf16( sum_k dec(W[n,k]) * s[n/128,k/128] * x[r][k] ),
+ * x bf16 used directly (no activation quantisation), fp32 accumulation.
+ * w->n and w->k multiples of 128; w->codes uint8 [N, K] (16-byte aligned),
+ * w->scales float [N/128, K/128]; rows 1..8; x bf16 [rows, K] (16-byte
+ * aligned), y bf16 [rows, N].
+ *
+ * Both: all pointers are device memory owned by the caller; x and y must not
+ * overlap; rows == 0 or N == 0 is a no-op.  Validation runs before anything
+ * is enqueued: a null or misaligned pointer, negative sizes or overlap ->
+ * MOE_ERR_INVALID_ARG; an unknown format, sizes off the 128 grid or too many
+ * rows -> MOE_ERR_UNSUPPORTED; a launch error -> MOE_ERR_DEVICE. */
 typedef struct {
   int32_t fmt, n, k;
   const void* codes;
