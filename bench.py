@@ -8,7 +8,9 @@ same layer is also timed at 2, 4 and 8 independent rows, at 4 and 8 correlated
 rows (x_i = 0.8 x_0 + 0.6 N(0,1), so rows share experts and the dedup table is
 smaller), with MXFP4 routed experts at 1 and 8 rows, and as the per-GPU share
 of an 8- and a 4-way split of the intermediate dimension (intermediate 256 and
-512, same hidden size, experts and router) at 1, 4 and 8 rows.  All inputs are seeded,
+512, same hidden size, experts and router) at 1, 4 and 8 rows.  The
+tail's LM-head GEMV ([151936, 6144] FP8 weights, lowbit_gemv's FP8 form) is
+timed at 1 and 8 rows.  All inputs are seeded,
 synthetic and already resident in HBM when the timed region starts.  Eight
 copies of the layer's weights are rotated step by step so that no step finds
 another step's weights in the 256 MB MALL or the L2s; a pool of 16 token rows
@@ -285,6 +287,44 @@ TP_SHARES = (("tp8_inter256", 256), ("tp4_inter512", 512))
 
 LOWBIT_SHAPES = (("mlp_up_gate", 9728, 2560), ("mlp_down", 2560, 9728), ("lm_head", 151936, 2560))
 
+# The tail's LM-head GEMV in FP8 (lowbit_gemv's FP8 form): the vocabulary of the
+# 1-bit LM head above over the GLM hidden size.
+LM_HEAD_FP8 = (151936, 6144)
+
+
+def gemv_fp8_bytes(n, k, rows):
+    return n * k + (n // 128) * (k // 128) * 4 + rows * k * 2 + rows * n * 2
+
+
+def time_gemv_fp8(torch, B, S, n, k, rows, steps):
+    """lowbit_gemv's FP8 form: back-to-back launches alternating over two
+    weight copies (1.87 GB in all, past the MALL)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(79)
+    w = torch.randn(n, k, generator=g, device="cuda")
+    codes, scales = S.encode_fp8_blocks(w)
+    del w
+    mats = [(codes, scales), (codes.clone(), scales.clone())]
+    x = S.make_x(rows, k, seed=80, device="cuda")
+    y = torch.empty(rows, n, dtype=torch.bfloat16, device="cuda")
+    for i in range(10):
+        B.gemv_fp8(*mats[i % 2], x, y, n, k, rows)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        B.gemv_fp8(*mats[i % 2], x, y, n, k, rows)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / steps
+    nbytes = gemv_fp8_bytes(n, k, rows)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del mats, codes, scales
+    torch.cuda.empty_cache()
+    return dict(n=n, k=k, rows=rows, us=round(us, 2), gbs=round(gbs, 1),
+                frac=round(gbs / PEAK_GBS, 4), bytes=nbytes)
+
 
 def lowbit_bytes(n, k):
     return n * (k // 128) * 18 + k * 2 + n * 2
@@ -490,12 +530,19 @@ def main():
             torch.cuda.empty_cache()
 
     lowbit = None
+    head = None
     if not args.no_lowbit:
         lowbit = {}
         for name, n, k in LOWBIT_SHAPES:
             log(f"timing lowbit_gemv {name} [{n}, {k}]")
             lowbit[name] = time_lowbit(torch, B, S, n, k, steps=max(args.steps, 50))
             log(f"  {lowbit[name]}")
+        head = {}
+        for rows in (1, 8):
+            n, k = LM_HEAD_FP8
+            log(f"timing lowbit_gemv FP8 LM head [{n}, {k}] rows={rows}")
+            head[str(rows)] = time_gemv_fp8(torch, B, S, n, k, rows, steps=max(args.steps, 50))
+            log(f"  {head[str(rows)]}")
 
     line = {
         "metric": METRIC,
@@ -546,6 +593,7 @@ def main():
         "mxfp4_routed": mx,
         "tp_share": tp,
         "lowbit_gemv": lowbit,
+        "lm_head_fp8": head,
     }
     print(json.dumps(line), flush=True)
 
