@@ -17,8 +17,8 @@ hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws,
                        hipStream_t stream);
 hipError_t launch_combine(const Ws& ws, const Dims& d, uint16_t* out, hipStream_t stream);
 int upgate_k_parts(int hidden, int routed_fmt);
-hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
-                            hipStream_t stream);
+hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int rows,
+                            int n, int k, hipStream_t stream);
 hipError_t launch_gemv_fp8(const uint8_t* codes, const float* scales, const uint16_t* x,
                            uint16_t* y, int rows, int n, int k, hipStream_t stream);
 
@@ -365,12 +365,14 @@ moe_status lowbit_gemv(const lowbit_matrix* w, const uint16_t* x, int32_t rows, 
   if (w->k % 128 || w->k > 16384) return MOE_ERR_UNSUPPORTED;
   if (rows < 0) return MOE_ERR_INVALID_ARG;
   if (rows == 0 || w->n == 0) return MOE_OK;
-  if (rows > 1) return MOE_ERR_UNSUPPORTED;
+  // several rows: the MFMA form, which takes K in chunks of 256
+  if (rows > 8 || (rows > 1 && w->k % 256)) return MOE_ERR_UNSUPPORTED;
   if (!w->codes || !x || !y || !aligned16(w->codes) || !aligned16(x) || !aligned16(y))
     return MOE_ERR_INVALID_ARG;
   const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
-  if (xa < ya + (size_t)w->n * 2 && ya < xa + (size_t)w->k * 2) return MOE_ERR_INVALID_ARG;
-  if (launch_lowbit_q1(static_cast<const uint8_t*>(w->codes), x, y, w->n, w->k, stream) !=
+  if (xa < ya + (size_t)rows * w->n * 2 && ya < xa + (size_t)rows * w->k * 2)
+    return MOE_ERR_INVALID_ARG;
+  if (launch_lowbit_q1(static_cast<const uint8_t*>(w->codes), x, y, rows, w->n, w->k, stream) !=
       hipSuccess)
     return MOE_ERR_DEVICE;
   return MOE_OK;

@@ -235,8 +235,138 @@ static hipError_t lb_nib_launch(const uint8_t* blocks, const uint16_t* x, uint16
   return hipGetLastError();
 }
 
-hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n, int k,
-                            hipStream_t stream) {
+// MFMA form, for 1 to 8 input rows (K a multiple of 256): y[r][n] for every
+// input row r at once.  Block = 4 waves = 4/KS slabs of 16 weight rows x KS
+// parts of K (KS = 4, 2 or 1 dividing the chunks of 256 inputs).  A 4 KB LDS
+// table holds, for each byte value b, the 8 bf16 values (bit i of b ? -1 : +1).
+// Per chunk (two groups, 36 bytes a row) lane l holds its row l%16's 9 dwords
+// and, per 32 inputs, looks up the byte of its row at inputs 8(l/16) .. +8 in
+// the table and runs one 16x16x32 bf16 MFMA against the input rows at the same
+// inputs (the MFMA's columns; those past the rows repeat row 0 and are not
+// stored): the products are +-x exactly.  A group's fp32 sum (4 MFMAs) is
+// scaled by its d (fp16) and accumulated; the block adds its K parts in part
+// order through LDS and stores bf16.
+struct QmStage {
+  uint32_t w[9];  // the chunk of the lane's row: d0, 16 bit-bytes, d1, 16 bit-bytes
+  u32x4 xb[8];    // the lane's input row at inputs 128h + 32s + 8(l/16) .. +8
+};
+
+template <int P>
+__global__ __launch_bounds__(256) void lowbit_gemv_q1_mfma_kernel(
+    const uint8_t* __restrict__ blocks, const uint16_t* __restrict__ x,
+    uint16_t* __restrict__ y, int rows, int n, int k, int ks) {
+  __shared__ __align__(16) uint32_t s_tab[256][4];  // bf16 +-1 pairs for each byte value
+  __shared__ __align__(16) float s_part[4][256];    // per wave 16 x 16 sums, column-major
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  {
+    uint32_t e[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+      const uint32_t lo = ((tid >> (2 * p)) & 1) ? 0xBF80u : 0x3F80u;
+      const uint32_t hi = ((tid >> (2 * p + 1)) & 1) ? 0xBF80u : 0x3F80u;
+      e[p] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(s_tab[tid]) = u32x4{e[0], e[1], e[2], e[3]};
+  }
+  __syncthreads();
+  const int spb = 4 / ks;
+  const int slab = blockIdx.x * spb + wv / ks, kp = wv % ks;
+  const int nch = k / 256, nc = nch / ks, c0 = kp * nc;
+  const int row = slab * 16 + col;
+  const int rowc = row < n ? row : n - 1;  // rows past n decode the last row (not stored)
+  const uint32_t* wrow = reinterpret_cast<const uint32_t*>(blocks + (size_t)rowc * 36 * nch);
+  const uint16_t* pa = x + (size_t)(col < rows ? col : 0) * k + 8 * g;
+
+  auto issue = [&](QmStage& st, int c) {
+#pragma unroll
+    for (int i = 0; i < 9; i++) st.w[i] = wrow[9 * c + i];
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+      for (int s2 = 0; s2 < 4; s2++)
+        st.xb[4 * h + s2] = ld16(pa + (size_t)c * 256 + h * 128 + 32 * s2);
+  };
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](QmStage& st) {
+    // the 16 bit-bytes of each group as 4 aligned dwords (group 0 starts 2
+    // bytes in); byte 4s + l/16 of a group is byte l/16 of its dword s
+    uint32_t u[8];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      u[q] = __builtin_amdgcn_alignbyte(st.w[q + 1], st.w[q], 2);
+      u[4 + q] = st.w[5 + q];
+    }
+    const float dg[2] = {lb_f16(st.w[0] & 0xFFFFu), lb_f16(st.w[4] >> 16)};
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < 4; s2++) {
+        const uint32_t byte = __builtin_amdgcn_ubfe(u[4 * h + s2], 8 * g, 8);
+        const v8bf a = *reinterpret_cast<const v8bf*>(s_tab[byte]);
+        c = mfma_bf16(a, __builtin_bit_cast(v8bf, st.xb[4 * h + s2]), c);
+      }
+      // lane l holds weight rows 4(l/16) + v; their d is held by lanes 4(l/16) + v
+#pragma unroll
+      for (int v = 0; v < 4; v++) acc[v] = fmaf(c[v], __shfl(dg[h], 4 * g + v, kWave), acc[v]);
+    }
+  };
+  QmStage st[P];
+#pragma unroll
+  for (int p = 0; p < P; p++) issue(st[p], c0 + p);
+  for (int i0 = 0; i0 < nc - P; i0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+      consume(st[p]);
+      issue(st[p], c0 + i0 + P + p);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; p++) consume(st[p]);
+  pin4(acc);  // the MFMAs run with every lane, before any divergent use
+
+  *reinterpret_cast<v4f*>(&s_part[wv][col * 16 + 4 * g]) = v4f{acc[0], acc[1], acc[2], acc[3]};
+  __syncthreads();
+  const int cc = tid >> 4, i = tid & 15;  // input row cc, weight row i of each slab
+  if (cc >= rows) return;
+  for (int s2 = 0; s2 < spb; s2++) {
+    float v = s_part[s2 * ks][cc * 16 + i];
+    for (int q = 1; q < ks; q++) v += s_part[s2 * ks + q][cc * 16 + i];
+    const int r = (blockIdx.x * spb + s2) * 16 + i;
+    if (r < n) y[(size_t)cc * n + r] = f32_to_bf16(v);
+  }
+}
+
+// The MFMA form's launch: K parts the fewest of 1, 2, 4 dividing the chunks
+// that gives at least 512 blocks, else the most that divide (more parts, more
+// blocks); ring depth 2 where it divides a part's chunks, else 1.
+static hipError_t lb_mfma_launch(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int rows,
+                                 int n, int k, hipStream_t stream) {
+  const int nch = k / 256, slabs = (n + 15) / 16;
+  int ks = 0;
+  for (int c : {1, 2, 4}) {
+    if (nch % c) continue;
+    if ((slabs + 4 / c - 1) / (4 / c) >= 512) {
+      ks = c;
+      break;
+    }
+  }
+  if (ks == 0) ks = nch % 4 == 0 ? 4 : (nch % 2 == 0 ? 2 : 1);
+  const int spb = 4 / ks;
+  const dim3 grid((slabs + spb - 1) / spb);
+  if ((nch / ks) % 2 == 0)
+    hipLaunchKernelGGL(lowbit_gemv_q1_mfma_kernel<2>, grid, dim3(256), 0, stream, blocks, x, y,
+                       rows, n, k, ks);
+  else
+    hipLaunchKernelGGL(lowbit_gemv_q1_mfma_kernel<1>, grid, dim3(256), 0, stream, blocks, x, y,
+                       rows, n, k, ks);
+  return hipGetLastError();
+}
+
+hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int rows,
+                            int n, int k, hipStream_t stream) {
+  if (rows > 1) return lb_mfma_launch(blocks, x, y, rows, n, k, stream);  // K % 256 == 0
   // the nibble-table form: rows per block RB the largest of 128, 64, 32 that
   // gives 2048 blocks, else the largest that gives 256, else 16; chunks per
   // thread and round M the fewest (up to 5) that take all of K in one round,

@@ -80,16 +80,26 @@ def test_step_without_context():
 def test_lowbit_gemv_validation():
     L = B.lib()
 
-    def call(fmt=B.FMT_Q1, n=16, k=256, rows=1, codes=4096, x=8192, y=16384):
-        m = B.LowbitMatrix(fmt, n, k, codes, None)
+    def call(fmt=B.FMT_Q1, n=16, k=256, rows=1, codes=4096, x=8192, y=16384, scales=None):
+        m = B.LowbitMatrix(fmt, n, k, codes, scales)
         return L.lowbit_gemv(ctypes.byref(m), ctypes.c_void_p(x) if x else None, rows,
                              ctypes.c_void_p(y) if y else None, None)
 
-    assert call(fmt=B.FMT_FP8) == B.MOE_ERR_UNSUPPORTED
+    assert call(fmt=B.FMT_MXFP4) == B.MOE_ERR_UNSUPPORTED
     assert call(k=200) == B.MOE_ERR_UNSUPPORTED
     assert call(k=32768) == B.MOE_ERR_UNSUPPORTED
-    assert call(rows=2) == B.MOE_ERR_UNSUPPORTED      # batch 1 only
+    assert call(rows=9) == B.MOE_ERR_UNSUPPORTED      # up to 8 rows
+    assert call(rows=2, k=384) == B.MOE_ERR_UNSUPPORTED  # several rows: K in chunks of 256
     assert call(rows=-1) == B.MOE_ERR_INVALID_ARG
+    # the FP8 form: N and K on the 128 grid, 1..8 rows, a scale pointer
+    fp8 = dict(fmt=B.FMT_FP8, n=128, k=128, x=1 << 20, y=1 << 21, scales=1 << 22)
+    assert call(**dict(fp8, n=100)) == B.MOE_ERR_UNSUPPORTED
+    assert call(**dict(fp8, k=200)) == B.MOE_ERR_UNSUPPORTED
+    assert call(**dict(fp8, rows=9)) == B.MOE_ERR_UNSUPPORTED
+    assert call(**dict(fp8, rows=0)) == B.MOE_OK
+    assert call(**dict(fp8, scales=None)) == B.MOE_ERR_INVALID_ARG
+    assert call(**dict(fp8, x=(1 << 20) + 8)) == B.MOE_ERR_INVALID_ARG  # misaligned
+    assert call(**dict(fp8, y=(1 << 20) + 64)) == B.MOE_ERR_INVALID_ARG  # overlaps x
     assert call(rows=0) == B.MOE_OK                    # no-op, nothing launched
     assert call(n=0) == B.MOE_OK
     assert call(codes=None) == B.MOE_ERR_INVALID_ARG

@@ -81,7 +81,7 @@ def test_lowbit_zero_rows_and_zero_n():
     B.lowbit_gemv(blk, x, y, 0, k, rows=1)
     torch.cuda.synchronize()
     assert (y.float() == 7.0).all()
-    assert B.lowbit_gemv_status(blk, x, y, 4, k, rows=2) == B.MOE_ERR_UNSUPPORTED
+    assert B.lowbit_gemv_status(blk, x, y, 4, k, rows=9) == B.MOE_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("n,k", [(16384, 256), (16385, 768), (20000, 5632)])
@@ -89,3 +89,45 @@ def test_lowbit_table_form_edges(n, k):
     """The table form's edges: one chunk of K, a ragged last block of rows,
     and an odd number of chunks with 64-row blocks."""
     _check(n, k, seed=n + k)
+
+
+def _check_rows(n, k, rows, seed, nthreads=16):
+    """Several input rows at once (the MFMA form) against the oracle run on
+    each row alone, with the single-row bound per output."""
+    _say(f"lowbit_gemv n={n} k={k} rows={rows} seed={seed}")
+    blk = S.make_q1(n, k, seed=seed)
+    x = S.make_x(rows, k, seed=seed + 1)
+    xb = S.bf16_bits(x).numpy().view(np.uint16)
+    y = torch.empty(rows, n, dtype=torch.bfloat16, device="cuda")
+    B.lowbit_gemv(blk.cuda(), x.cuda(), y, n, k, rows=rows)
+    torch.cuda.synchronize()
+    yg = y.float().cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for r in range(rows):
+        _, ref = O.lowbit_gemv_q1(blk.numpy(), xb[r], n, k, nthreads=nthreads)
+        xf = x[r].float().numpy().astype(np.float64)
+        bound = 2.0 ** -8 * np.abs(ref) + (k + 8) * U32 * _abs_terms(blk.numpy(), xf, n, k)
+        err = np.abs(yg[r] - ref)
+        assert (err <= bound).all(), ("row outside its rounding bound", r, n, k,
+                                      int((err > bound).sum()), float((err / bound).max()))
+        assert err.max() <= 2e-2 * np.abs(ref).max()
+        worst = max(worst, float(err.max() / np.abs(ref).max()))
+    return worst
+
+
+@pytest.mark.parametrize("n,k,rows", [(5, 256, 2), (1000, 1280, 8), (9728, 2560, 4),
+                                      (2560, 9728, 8), (64, 16384, 3), (151936, 2560, 8)])
+def test_lowbit_several_rows(n, k, rows):
+    """1-bit GEMV beyond batch 1: ragged rows and a ragged last 16-row slab,
+    every K-part count, the MLP and LM-head shapes, K = 16384."""
+    rel = _check_rows(n, k, rows, seed=n % 997 + k + rows)
+    _say(f"  max err / max|ref| = {rel:.2e}")
+
+
+def test_lowbit_several_rows_need_256_chunks():
+    k = 384
+    blk = S.make_q1(4, k, seed=1).cuda()
+    x = S.make_x(2, k, seed=2).cuda()
+    y = torch.empty(2, 4, dtype=torch.bfloat16, device="cuda")
+    assert B.lowbit_gemv_status(blk, x, y, 4, k, rows=2) == B.MOE_ERR_UNSUPPORTED
+
