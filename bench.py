@@ -330,33 +330,36 @@ def lowbit_bytes(n, k):
     return n * (k // 128) * 18 + k * 2 + n * 2
 
 
-def time_lowbit(torch, B, S, n, k, steps):
-    """lowbit_gemv at batch 1: back-to-back launches over enough weight copies
-    (>= 512 MB in all) that no launch finds its matrix in the MALL."""
+def time_lowbit(torch, B, S, n, k, steps, rows=1):
+    """lowbit_gemv for `rows` input rows: back-to-back launches over enough
+    weight copies (>= 512 MB in all) that no launch finds its matrix in the MALL."""
     size = n * (k // 128) * 18
     ncopy = max(2, -(-512 * 2 ** 20 // size))
     base = S.make_q1(n, k, seed=77, device="cuda")
     mats = [base] + [base.clone() for _ in range(ncopy - 1)]
-    x = S.make_x(1, k, seed=78, device="cuda")[0]
-    y = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    x = S.make_x(rows, k, seed=78, device="cuda")
+    y = torch.empty(rows, n, dtype=torch.bfloat16, device="cuda")
     for i in range(10):
-        B.lowbit_gemv(mats[i % ncopy], x, y, n, k)
+        B.lowbit_gemv(mats[i % ncopy], x, y, n, k, rows)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for i in range(steps):
-        B.lowbit_gemv(mats[i % ncopy], x, y, n, k)
+        B.lowbit_gemv(mats[i % ncopy], x, y, n, k, rows)
     t1.record()
     torch.cuda.synchronize()
     us = t0.elapsed_time(t1) * 1e3 / steps
-    gbs = lowbit_bytes(n, k) / (us * 1e-6) / 1e9
+    nbytes = lowbit_bytes(n, k) + (rows - 1) * (k + n) * 2
+    gbs = nbytes / (us * 1e-6) / 1e9
     del mats
-    # VALU floor: one fp32 lane-op per weight at 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
+    # VALU floor at one row: one fp32 lane-op per weight at 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
     valu_us = n * k / VALU_LANE_OPS * 1e6
-    return dict(n=n, k=k, us=round(us, 2), gbs=round(gbs, 1), frac=round(gbs / PEAK_GBS, 4),
-                bytes=lowbit_bytes(n, k), copies=ncopy,
-                valu_floor_us=round(valu_us, 2), valu_frac=round(valu_us / us, 4))
+    out = dict(n=n, k=k, rows=rows, us=round(us, 2), gbs=round(gbs, 1),
+               frac=round(gbs / PEAK_GBS, 4), bytes=nbytes, copies=ncopy)
+    if rows == 1:
+        out.update(valu_floor_us=round(valu_us, 2), valu_frac=round(valu_us / us, 4))
+    return out
 
 
 def cpu_model():
@@ -537,6 +540,9 @@ def main():
             log(f"timing lowbit_gemv {name} [{n}, {k}]")
             lowbit[name] = time_lowbit(torch, B, S, n, k, steps=max(args.steps, 50))
             log(f"  {lowbit[name]}")
+            lowbit[name + "_8rows"] = time_lowbit(torch, B, S, n, k, steps=max(args.steps, 50),
+                                                  rows=8)
+            log(f"  8 rows: {lowbit[name + '_8rows']}")
         head = {}
         for rows in (1, 8):
             n, k = LM_HEAD_FP8
