@@ -85,7 +85,8 @@ def test_tiny_mxfp4_dedup_off_is_bitwise_equal(tiny4):
     assert torch.equal(on.view(torch.int16), off.view(torch.int16))
 
 
-@pytest.mark.parametrize("rows,mode", [(1, "indep"), (8, "indep"), (8, "corr")])
+@pytest.mark.parametrize("rows,mode", [(1, "indep"), (2, "corr"), (4, "indep"), (6, "corr"),
+                                       (8, "indep"), (8, "corr")])
 def test_glm_mxfp4_parity(glm4, rows, mode):
     _say(f"glm mxfp4 rows={rows} mode={mode}")
     x = S.make_x(rows, glm4.hidden, seed=4200 + 10 * rows + (mode == "corr"), mode=mode)
