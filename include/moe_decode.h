@@ -210,8 +210,10 @@ const char* moe_status_string(moe_status s);
  *   y[n] = bf16( sum_g d[n,g] * sum_{k in g} sign[n,k] * x[k] ),
  * x used as bf16 directly, fp32 accumulation.  w->k a multiple of 128 (at
  * most 16384); w->codes points to the [N, K/128, 18] blocks (device);
- * w->scales is unused (the scales are in the blocks).  rows must be 1 (the
- * reference path is batch 1).  x bf16 [K], y bf16 [N].
+ * w->scales is unused (the scales are in the blocks).  rows 1..8 (the
+ * page's path was batch 1; several rows need K a multiple of 256 and are
+ * computed together, each row as its batch-1 definition).  x bf16 [rows, K],
+ * y bf16 [rows, N], both 16-byte aligned.
  *
  * MOE_FMT_FP8_E4M3_B128 -- FP8 weights with one fp32 scale per 128x128 block,
  * for the tail's LM-head GEMV after the last layer (#85 Mod. row 24: the tail
