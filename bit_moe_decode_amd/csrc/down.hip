@@ -7,13 +7,13 @@
 // bytes with one fp32 scale per 1x128 block, quantised once per (row, pick)
 // and expert.  Mod. rows 18 and 21: 16-byte, nontemporal weight loads.
 //
-// moe_down_kernel: block = WPB waves = 16 * WPB output rows of one expert (the
-// shared expert's blocks first, then those of each of the step's possible
-// routed groups; blocks of groups past the step's D exit at once).  Many
-// small blocks let the hardware dispatcher even out the load per CU: WPB = 2
-// for FP8 steps of one or two rows, where 64-row blocks would leave some CUs
-// with a block more than others (a CU streams at most about 1/256 of the
-// chip's bandwidth), else 4.
+// moe_down_kernel: block = WPB waves of T 16-row tiles each = 16 * WPB * T
+// output rows of one expert (the shared expert's blocks first, then those of
+// each of the step's possible routed groups; blocks of groups past the step's
+// D exit at once).  Many small blocks let the hardware dispatcher even out the
+// load per CU: WPB = 2, T = 1 for FP8 steps of one or two rows, where larger
+// blocks would leave some CUs with a block more than others (a CU streams at
+// most about 1/256 of the chip's bandwidth); else WPB = 4.
 //
 // FP8 experts.  The block first puts the first K blocks of its weight stream
 // in flight, then quantises the fp32 mid of each of its columns (one per row
@@ -22,10 +22,11 @@
 // all-zero block giving s = 0 and zero codes.  Every block of an expert does
 // this the same way, so all use the same bytes; the first block also stores
 // them as the step's midq / midqs.  A wave then owns 16 output rows over the
-// whole K: for each 128-wide K block it loads its 16 weight rows
-// row-contiguously, re-lays them through LDS into MFMA operand order and runs
-// one 16x16x128 FP8 MFMA against the mid codes, scaled by weight scale x mid
-// scale and accumulated in fp32.  It stores y[row, pick][h]; every
+// whole K (from 3 rows, two tiles of 16: each read of the mid codes from LDS
+// then serves 32 rows): for each 128-wide K block it loads its weight rows
+// row-contiguously, re-lays each tile through LDS into MFMA operand order and
+// runs one 16x16x128 FP8 MFMA per tile against the mid codes, scaled by weight
+// scale x mid scale and accumulated in fp32.  It stores y[row, pick][h]; every
 // (row, pick) belongs to exactly one expert of the step, so no two writes
 // collide.
 //
@@ -45,9 +46,10 @@
 
 namespace moe {
 
+template <int TF>
 struct DnStage {
-  u32x4 w0, w1;
-  float sd;
+  u32x4 w0[TF], w1[TF];  // rows l/8 and 8 + l/8 of each 16-row tile
+  float sd;              // weight block scale (the tiles share a 128-row block)
 };
 
 // Dynamic LDS of the down kernel: mid codes of each column (row stride
@@ -248,8 +250,11 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
 
   // ---- the block's expert and rows (MXFP4 routed blocks: T4 times the rows
   // of an FP8 block)
+  // FP8 waves take TF 16-row tiles (T4 in FP8 layers; the shared expert of
+  // an MXFP4 layer keeps one)
+  constexpr int TF = RF == kFmtFp8 ? T4 : 1;
   const int per = H / (16 * WPB);
-  const int nb_sh = d.Is > 0 ? per : 0;
+  const int nb_sh = d.Is > 0 ? per / TF : 0;
   int b = blockIdx.x, g = -1, nrows, e;
   uint64_t rows8 = 0, picks8 = 0;
   if (b < nb_sh) {
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
     e = -1;
   } else {
     b -= nb_sh;
-    const int perg = RF == kFmtMxfp4 ? per / T4 : per;
+    const int perg = per / T4;
     g = b / perg;
     b -= g * perg;
     // one round of independent loads; the table of a group past D is stale
@@ -291,12 +296,12 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
     return;
   }
   const int cc = col < nrows ? col : 0;  // columns past the rows reuse column 0
-  const int h0 = b * 16 * WPB + wv * 16;
+  const int h0 = (b * WPB + wv) * 16 * TF;
 
   const uint8_t* wb = e < 0 ? w.sd_c : w.down_c + (size_t)e * H * I;
   const float* sb =
       e < 0 ? w.sd_s : reinterpret_cast<const float*>(w.down_s) + (size_t)e * (H / 128) * nkb;
-  // lane l loads rows h0 + l/8 and h0 + 8 + l/8, 16-byte chunk l%8
+  // lane l loads rows h0 + 16t + l/8 and h0 + 16t + 8 + l/8 of tile t, 16-byte chunk l%8
   const uint8_t* pw = wb + (size_t)(h0 + (lane >> 3)) * I + (lane & 7) * 16;
   const size_t r8 = (size_t)8 * I;
   const float* psd = sb + (size_t)(h0 / 128) * nkb;
@@ -306,26 +311,41 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
   const uint8_t* pm = s_q + cc * dn_code_stride(I) + (lane >> 4) * 32;
   const float* psm = s_qs + cc * nkb;
 
-  auto issue = [&](DnStage& s, int k) {
+  auto issue = [&](DnStage<TF>& s, int k) {
     const size_t o = (size_t)k * 128;
-    s.w0 = ld_nt16(pw + o);
-    s.w1 = ld_nt16(pw + r8 + o);
+#pragma unroll
+    for (int t = 0; t < TF; t++) {
+      s.w0[t] = ld_nt16(pw + (size_t)t * 2 * r8 + o);
+      s.w1[t] = ld_nt16(pw + (size_t)t * 2 * r8 + r8 + o);
+    }
     s.sd = psd[k];
   };
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  auto consume = [&](DnStage& s, int k) {
-    tile_put(tile, lane, s.w0, s.w1);
-    asm volatile("" ::: "memory");
+  float acc[TF][4];
+#pragma unroll
+  for (int t = 0; t < TF; t++)
+#pragma unroll
+    for (int v = 0; v < 4; v++) acc[t][v] = 0.f;
+  auto consume = [&](DnStage<TF>& s, int k) {
+    v8i a[TF];  // each tile re-laid through the wave's LDS tile in turn
+#pragma unroll
+    for (int t = 0; t < TF; t++) {
+      tile_put(tile, lane, s.w0[t], s.w1[t]);
+      asm volatile("" ::: "memory");
+      a[t] = tile_get(tile, lane);
+      asm volatile("" ::: "memory");
+    }
     const u32x4 m0 = ld16(pm + k * 128), m1 = ld16(pm + k * 128 + 16);
-    const v4f c = mfma_fp8(tile_get(tile, lane), cat8(m0, m1));
-    asm volatile("" ::: "memory");
     const float f = s.sd * psm[k];
 #pragma unroll
-    for (int v = 0; v < 4; v++) acc[v] = fmaf(c[v], f, acc[v]);
+    for (int t = 0; t < TF; t++) {
+      const v4f c = mfma_fp8(a[t], cat8(m0, m1));
+#pragma unroll
+      for (int v = 0; v < 4; v++) acc[t][v] = fmaf(c[v], f, acc[t][v]);
+    }
   };
   // ring of P K blocks (P divides nkb): every issued load is used.  The first
   // P are in flight while the block quantises mid.
-  DnStage st[P];
+  DnStage<TF> st[P];
 #pragma unroll
   for (int p = 0; p < P; p++) issue(st[p], p);
   dn_quant_mid(ws, d, nrows, cols, b == 0, s_q, s_qs);
@@ -339,10 +359,14 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
   }
 #pragma unroll
   for (int p = 0; p < P; p++) consume(st[p], nkb - P + p);
-  pin4(acc);  // the MFMAs run with every lane, before the divergent store
-  if (col < nrows)
-    *reinterpret_cast<v4f*>(ws.ypart + (size_t)cols.u(col) * H + h0 + 4 * (lane >> 4)) =
-        v4f{acc[0], acc[1], acc[2], acc[3]};
+#pragma unroll
+  for (int t = 0; t < TF; t++) pin4(acc[t]);  // the MFMAs run with every lane, before the divergent store
+  if (col < nrows) {
+#pragma unroll
+    for (int t = 0; t < TF; t++)
+      *reinterpret_cast<v4f*>(ws.ypart + (size_t)cols.u(col) * H + h0 + 16 * t + 4 * (lane >> 4)) =
+          v4f{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
+  }
 }
 
 // out[r][h] for 4 consecutive h per thread.
@@ -388,27 +412,31 @@ static hipError_t launch_one(int max_groups, size_t lds, const Weights& w, const
   const hipError_t e =
       ensure_dyn_lds(reinterpret_cast<const void*>(&moe_down_kernel<RF, P, WPB, T4>), lds, raised);
   if (e != hipSuccess) return e;
+  constexpr int TF = RF == kFmtFp8 ? T4 : 1;  // tiles of the FP8 (shared and routed) waves
   const int per = d.H / (16 * WPB);
-  const dim3 grid(per * (d.Is > 0 ? 1 : 0) +
-                  (RF == kFmtMxfp4 ? per / T4 : per) * max_groups);
+  const dim3 grid((d.Is > 0 ? per / TF : 0) + (per / T4) * max_groups);
   hipLaunchKernelGGL((moe_down_kernel<RF, P, WPB, T4>), grid, dim3(64 * WPB), lds, stream, w, ws,
                      d);
   return hipGetLastError();
 }
 
-// Blocks of 2 waves (32 output rows) for FP8 steps of one or two rows, whose
-// few experts otherwise leave some CUs a block more than others; 4 waves
-// (64 rows) otherwise.  MXFP4 routed waves take 2 tiles of 16 rows from
-// kDn4TwoTileRows rows up (the mid operand's LDS reads then serve 32 rows),
-// else 1 (more blocks for the few experts of small steps); measured: 2 tiles
-// are faster from 6 rows, slower at 4 and 5.
+// FP8: blocks of 2 waves of one tile (32 output rows) for steps of one or two
+// rows, whose few experts otherwise leave some CUs a block more than others;
+// else 4 waves of two tiles (128 rows; measured against one tile, same ring:
+// 150.5 -> 149.9, 190.3 -> 188.9, 269.1 -> 266.8 and 339.9 -> 337.2 us per
+// GLM step at 3, 4, 6 and 8 rows; half the ring with two tiles was between).
+// MXFP4 routed waves take 2 tiles of 16 rows from kDn4TwoTileRows rows up
+// (the mid operand's LDS reads then serve 32 rows), else 1 (more blocks for
+// the few experts of small steps); measured: 2 tiles are faster from 6 rows,
+// slower at 4 and 5.
 constexpr int kDn4TwoTileRows = 6;
+
 template <int RF, int P>
 static hipError_t launch_wpb(int max_groups, size_t lds, const Weights& w, const Ws& ws,
                              const Dims& d, hipStream_t stream) {
   if constexpr (RF == kFmtFp8)
     return d.rows <= 2 ? launch_one<RF, P, 2, 1>(max_groups, lds, w, ws, d, stream)
-                       : launch_one<RF, P, 4, 1>(max_groups, lds, w, ws, d, stream);
+                       : launch_one<RF, P, 4, 2>(max_groups, lds, w, ws, d, stream);
   else
     return d.rows >= kDn4TwoTileRows
                ? launch_one<RF, P, 4, 2>(max_groups, lds, w, ws, d, stream)
