@@ -552,6 +552,30 @@ int orc_gemv_fp8(const uint8_t* codes, const float* scales, const uint16_t* x, i
   return ORC_OK;
 }
 
+/* The same tail GEMV over bf16 weights (READING: the #85 page's tail names no
+ * weight format; an LM head kept in bf16 beside FP8 experts is the other
+ * plain reading).  Inputs are bf16 rows used as they are.
+ *   y[r][n] = sum_k dec(W[n][k]) * x[r][k]
+ * accumulated in double (each product of two bf16 is exact in double); y16 =
+ * bf16 RNE of y.  W: [n][k] bf16 bits; x: [rows][k] bf16 bits.  No grid is
+ * imposed on n and k here; the device form has its own. */
+int orc_gemv_bf16(const uint16_t* w, const uint16_t* x, int rows, int n, int k, int nthreads,
+                  uint16_t* y16, double* y) {
+  if (rows < 0 || n < 0 || k <= 0) return ORC_ERR;
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+  for (int row = 0; row < n; row++) {
+    for (int r = 0; r < rows; r++) {
+      double acc = 0.0;
+      for (int kk = 0; kk < k; kk++)
+        acc += orc_dec_bf16(w[(size_t)row * k + kk]) * orc_dec_bf16(x[(size_t)r * k + kk]);
+      if (y) y[(size_t)r * n + row] = acc;
+      if (y16) y16[(size_t)r * n + row] = orc_round_bf16(acc);
+    }
+  }
+  return ORC_OK;
+}
+
 /* ---------------------------------------------- array forms for the tests */
 
 void orc_dec_e4m3_n(const uint8_t* c, int n, double* v) {

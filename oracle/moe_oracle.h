@@ -115,6 +115,10 @@ int orc_lowbit_gemv_q1(const uint8_t* blocks, const uint16_t* x, int n, int k, i
 int orc_gemv_fp8(const uint8_t* codes, const float* scales, const uint16_t* x, int rows, int n,
                  int k, int nthreads, uint16_t* y16, double* y);
 
+/* bf16 weights [n][k], bf16 input rows */
+int orc_gemv_bf16(const uint16_t* w, const uint16_t* x, int rows, int n, int k, int nthreads,
+                  uint16_t* y16, double* y);
+
 #ifdef __cplusplus
 }
 #endif

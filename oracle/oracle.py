@@ -285,3 +285,20 @@ def gemv_fp8(codes, scales, x, nthreads=1):
     if rc != 0:
         raise ValueError("orc_gemv_fp8 failed")
     return y, yf
+
+
+def gemv_bf16(w, x, nthreads=1):
+    """w uint16 [n, k] (bf16 bits), x uint16 [rows, k] (bf16 bits) ->
+    (y uint16 [rows, n] bf16, y_f64 [rows, n])."""
+    ww = np.ascontiguousarray(w, dtype=np.uint16)
+    xx = np.ascontiguousarray(np.atleast_2d(x), dtype=np.uint16)
+    rows, k = xx.shape
+    n = ww.shape[0]
+    assert ww.shape == (n, k)
+    y = np.zeros((rows, n), np.uint16)
+    yf = np.zeros((rows, n), np.float64)
+    rc = lib().orc_gemv_bf16(_p(ww), _p(xx), ctypes.c_int(rows), ctypes.c_int(n),
+                             ctypes.c_int(k), ctypes.c_int(nthreads), _p(y), _p(yf))
+    if rc != 0:
+        raise ValueError("orc_gemv_bf16 failed")
+    return y, yf
