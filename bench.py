@@ -287,13 +287,17 @@ TP_SHARES = (("tp8_inter256", 256), ("tp4_inter512", 512))
 
 LOWBIT_SHAPES = (("mlp_up_gate", 9728, 2560), ("mlp_down", 2560, 9728), ("lm_head", 151936, 2560))
 
-# The tail's LM-head GEMV in FP8 (lowbit_gemv's FP8 form): the vocabulary of the
-# 1-bit LM head above over the GLM hidden size.
+# The tail's LM-head GEMV in FP8 and in bf16 (lowbit_gemv's FP8 and bf16
+# forms): the vocabulary of the 1-bit LM head above over the GLM hidden size.
 LM_HEAD_FP8 = (151936, 6144)
 
 
 def gemv_fp8_bytes(n, k, rows):
     return n * k + (n // 128) * (k // 128) * 4 + rows * k * 2 + rows * n * 2
+
+
+def gemv_bf16_bytes(n, k, rows):
+    return n * k * 2 + rows * k * 2 + rows * n * 2
 
 
 def time_gemv_fp8(torch, B, S, n, k, rows, steps):
@@ -321,6 +325,34 @@ def time_gemv_fp8(torch, B, S, n, k, rows, steps):
     nbytes = gemv_fp8_bytes(n, k, rows)
     gbs = nbytes / (us * 1e-6) / 1e9
     del mats, codes, scales
+    torch.cuda.empty_cache()
+    return dict(n=n, k=k, rows=rows, us=round(us, 2), gbs=round(gbs, 1),
+                frac=round(gbs / PEAK_GBS, 4), bytes=nbytes)
+
+
+def time_gemv_bf16(torch, B, S, n, k, rows, steps):
+    """lowbit_gemv's bf16 form: back-to-back launches alternating over two
+    weight copies (3.7 GB in all, past the MALL)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(81)
+    mats = [(torch.randn(n, k, generator=g, device="cuda") * 0.05).to(torch.bfloat16)
+            for _ in range(2)]
+    x = S.make_x(rows, k, seed=82, device="cuda")
+    y = torch.empty(rows, n, dtype=torch.bfloat16, device="cuda")
+    for i in range(10):
+        B.gemv_bf16(mats[i % 2], x, y, n, k, rows)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        B.gemv_bf16(mats[i % 2], x, y, n, k, rows)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / steps
+    nbytes = gemv_bf16_bytes(n, k, rows)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del mats
     torch.cuda.empty_cache()
     return dict(n=n, k=k, rows=rows, us=round(us, 2), gbs=round(gbs, 1),
                 frac=round(gbs / PEAK_GBS, 4), bytes=nbytes)
@@ -533,7 +565,7 @@ def main():
             torch.cuda.empty_cache()
 
     lowbit = None
-    head = None
+    head = head_bf = None
     if not args.no_lowbit:
         lowbit = {}
         for name, n, k in LOWBIT_SHAPES:
@@ -543,12 +575,18 @@ def main():
             lowbit[name + "_8rows"] = time_lowbit(torch, B, S, n, k, steps=max(args.steps, 50),
                                                   rows=8)
             log(f"  8 rows: {lowbit[name + '_8rows']}")
-        head = {}
+        head, head_bf = {}, {}
         for rows in (1, 8):
             n, k = LM_HEAD_FP8
             log(f"timing lowbit_gemv FP8 LM head [{n}, {k}] rows={rows}")
             head[str(rows)] = time_gemv_fp8(torch, B, S, n, k, rows, steps=max(args.steps, 50))
             log(f"  {head[str(rows)]}")
+        for rows in (1, 8):
+            n, k = LM_HEAD_FP8
+            log(f"timing lowbit_gemv bf16 LM head [{n}, {k}] rows={rows}")
+            head_bf[str(rows)] = time_gemv_bf16(torch, B, S, n, k, rows,
+                                                steps=max(args.steps, 50))
+            log(f"  {head_bf[str(rows)]}")
 
     line = {
         "metric": METRIC,
@@ -600,6 +638,7 @@ def main():
         "tp_share": tp,
         "lowbit_gemv": lowbit,
         "lm_head_fp8": head,
+        "lm_head_bf16": head_bf,
     }
     print(json.dumps(line), flush=True)
 

@@ -16,6 +16,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEV
 FMT_FP8 = 1
 FMT_MXFP4 = 2
 FMT_Q1 = 3
+FMT_BF16 = 4
 ACT_FP8, ACT_BF16 = 0, 1  # moe_afmt
 F_NO_DEDUP = 1 << 1
 N_KERNELS = 5
@@ -225,6 +226,19 @@ def gemv_fp8(codes, scales, x, y, n, k, rows=1, stream=None):
 def gemv_fp8_status(codes, scales, x, y, n, k, rows=1, stream=None):
     m = LowbitMatrix(FMT_FP8, int(n), int(k), codes.data_ptr() if codes is not None else None,
                      scales.data_ptr() if scales is not None else None)
+    return lib().lowbit_gemv(ctypes.byref(m), _ptr(x), int(rows), _ptr(y), _stream(stream))
+
+
+def gemv_bf16(w, x, y, n, k, rows=1, stream=None):
+    """lowbit_gemv with bf16 weights: w bf16 [n, k], x bf16 [rows, k], y bf16
+    [rows, n] (device tensors)."""
+    st = gemv_bf16_status(w, x, y, n, k, rows, stream)
+    if st != MOE_OK:
+        raise MoeError(st, "lowbit_gemv")
+
+
+def gemv_bf16_status(w, x, y, n, k, rows=1, stream=None):
+    m = LowbitMatrix(FMT_BF16, int(n), int(k), w.data_ptr() if w is not None else None, None)
     return lib().lowbit_gemv(ctypes.byref(m), _ptr(x), int(rows), _ptr(y), _stream(stream))
 
 

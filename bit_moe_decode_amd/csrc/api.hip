@@ -21,6 +21,8 @@ hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* 
                             int n, int k, hipStream_t stream);
 hipError_t launch_gemv_fp8(const uint8_t* codes, const float* scales, const uint16_t* x,
                            uint16_t* y, int rows, int n, int k, hipStream_t stream);
+hipError_t launch_gemv_bf16(const uint16_t* w, const uint16_t* x, uint16_t* y, int rows, int n,
+                            int k, hipStream_t stream);
 
 __global__ void moe_fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
@@ -357,6 +359,23 @@ moe_status lowbit_gemv(const lowbit_matrix* w, const uint16_t* x, int32_t rows, 
       return MOE_ERR_INVALID_ARG;
     if (launch_gemv_fp8(static_cast<const uint8_t*>(w->codes), static_cast<const float*>(w->scales),
                         x, y, rows, w->n, w->k, stream) != hipSuccess)
+      return MOE_ERR_DEVICE;
+    return MOE_OK;
+  }
+  if (w->fmt == MOE_FMT_BF16) {
+    // bf16 weights, 1 to 8 bf16 input rows
+    if (w->n < 0 || w->k <= 0) return MOE_ERR_INVALID_ARG;
+    if (w->n % 128 || w->k % 64) return MOE_ERR_UNSUPPORTED;
+    if (rows < 0) return MOE_ERR_INVALID_ARG;
+    if (rows == 0 || w->n == 0) return MOE_OK;
+    if (rows > 8) return MOE_ERR_UNSUPPORTED;
+    if (!w->codes || !x || !y || !aligned16(w->codes) || !aligned16(x) || ((uintptr_t)y & 1u))
+      return MOE_ERR_INVALID_ARG;
+    const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
+    if (xa < ya + (size_t)rows * w->n * 2 && ya < xa + (size_t)rows * w->k * 2)
+      return MOE_ERR_INVALID_ARG;
+    if (launch_gemv_bf16(static_cast<const uint16_t*>(w->codes), x, y, rows, w->n, w->k,
+                         stream) != hipSuccess)
       return MOE_ERR_DEVICE;
     return MOE_OK;
   }

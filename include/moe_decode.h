@@ -70,7 +70,10 @@ typedef enum {
    * (little-endian) then 16 bytes of sign bits; bit i of byte b is element
    * 8b+i; bit 1 means -d, bit 0 means +d (1-Bit Turbo, Q1_0_G128).
    * lowbit_gemv only. */
-  MOE_FMT_Q1_G128 = 3
+  MOE_FMT_Q1_G128 = 3,
+  /* bf16 weights [N, K], no scales.  lowbit_gemv only (the tail's LM head
+   * kept in bf16). */
+  MOE_FMT_BF16 = 4
 } moe_wfmt;
 
 /* The experts' input (the up/gate activation). */
@@ -204,7 +207,7 @@ void moe_decode_destroy(moe_decode_ctx* ctx);
 
 const char* moe_status_string(moe_status s);
 
-/* Dense decode GEMV, in one of two weight formats.
+/* Dense decode GEMV, in one of three weight formats.
  *
  * MOE_FMT_Q1_G128 -- 1-bit group-128 weights (1-Bit Turbo, Q1_0_G128):
  *   y[n] = bf16( sum_g d[n,g] * sum_{k in g} sign[n,k] * x[k] ),
@@ -224,11 +227,18 @@ const char* moe_status_string(moe_status s);
  * w->scales float [N/128, K/128]; rows 1..8; x bf16 [rows, K] (16-byte
  * aligned), y bf16 [rows, N].
  *
- * Both: all pointers are device memory owned by the caller; x and y must not
+ * MOE_FMT_BF16 -- bf16 weights, the same tail GEMV with the LM head kept in
+ * bf16 (#85 Mod. row 24; the page names no weight format for the tail):
+ *   y[r][n] = bf16( sum_k W[n,k] * x[r][k] ),
+ * fp32 accumulation.  w->n a multiple of 128, w->k of 64; w->codes bf16
+ * [N, K] (16-byte aligned); w->scales is unused; rows 1..8; x bf16 [rows, K]
+ * (16-byte aligned), y bf16 [rows, N].
+ *
+ * All forms: all pointers are device memory owned by the caller; x and y must not
  * overlap; rows == 0 or N == 0 is a no-op.  Validation runs before anything
  * is enqueued: a null or misaligned pointer, negative sizes or overlap ->
- * MOE_ERR_INVALID_ARG; an unknown format, sizes off the 128 grid or too many
- * rows -> MOE_ERR_UNSUPPORTED; a launch error -> MOE_ERR_DEVICE. */
+ * MOE_ERR_INVALID_ARG; an unknown format, sizes off the form's grid or too
+ * many rows -> MOE_ERR_UNSUPPORTED; a launch error -> MOE_ERR_DEVICE. */
 typedef struct {
   int32_t fmt, n, k;
   const void* codes;

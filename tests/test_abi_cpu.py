@@ -100,6 +100,18 @@ def test_lowbit_gemv_validation():
     assert call(**dict(fp8, scales=None)) == B.MOE_ERR_INVALID_ARG
     assert call(**dict(fp8, x=(1 << 20) + 8)) == B.MOE_ERR_INVALID_ARG  # misaligned
     assert call(**dict(fp8, y=(1 << 20) + 64)) == B.MOE_ERR_INVALID_ARG  # overlaps x
+    # the bf16 form: N on the 128 grid, K on the 64 grid, 1..8 rows, no scales
+    bf = dict(fmt=B.FMT_BF16, n=128, k=64, x=1 << 20, y=1 << 21)
+    assert call(**dict(bf, n=100)) == B.MOE_ERR_UNSUPPORTED
+    assert call(**dict(bf, k=96)) == B.MOE_ERR_UNSUPPORTED
+    assert call(**dict(bf, rows=9)) == B.MOE_ERR_UNSUPPORTED
+    assert call(**dict(bf, rows=0)) == B.MOE_OK
+    assert call(**dict(bf, codes=None)) == B.MOE_ERR_INVALID_ARG
+    assert call(**dict(bf, codes=4096 + 8)) == B.MOE_ERR_INVALID_ARG  # misaligned weights
+    assert call(**dict(bf, x=(1 << 20) + 8)) == B.MOE_ERR_INVALID_ARG  # misaligned x
+    assert call(**dict(bf, y=(1 << 21) + 1)) == B.MOE_ERR_INVALID_ARG  # odd y
+    assert call(**dict(bf, y=(1 << 20) + 64)) == B.MOE_ERR_INVALID_ARG  # overlaps x
+    assert call(fmt=5) == B.MOE_ERR_UNSUPPORTED
     assert call(rows=0) == B.MOE_OK                    # no-op, nothing launched
     assert call(n=0) == B.MOE_OK
     assert call(codes=None) == B.MOE_ERR_INVALID_ARG
