@@ -149,11 +149,12 @@ def test_step_argument_errors(tiny):
 @pytest.mark.parametrize("shared", [False, True])
 def test_other_intermediate_sizes(inter, shared):
     """Intermediate sizes of 4, 8 and 12 K blocks (ring depths 4, 8 and 4 in
-    down), with and without a shared expert, at one and two rows."""
+    down), with and without a shared expert, at one and two rows (one-tile
+    down waves) and at 3 and 8 rows (two-tile down waves)."""
     shape = dict(hidden=512, inter=inter, n_experts=32, shared_inter=inter if shared else 0,
                  router_std=0.02)
     layer = S.make_layer(shape, seed=3000 + inter + shared, device="cuda")
-    for rows in (1, 2):
+    for rows in (1, 2, 3, 8):
         _say(f"inter={inter} shared={shared} rows={rows}")
         x = S.make_x(rows, layer.hidden, seed=3100 + rows)
         _, _, _, rep = _run(layer, x)
