@@ -2,8 +2,8 @@
 // expert from mid, per (row, pick); then the gate-weighted combine.
 //
 // #85 Mod. row 16: down units take one expert's tile against every row that
-// uses it; a row's output is summed over its units in the one-row form's
-// order, so dedup changes no output bit.  Mod. row 1: down reads mid as FP8
+// uses it, and each row adds its units up in the order a lone row would,
+// so dedup changes no output bit.  Mod. row 1: down reads mid as FP8
 // bytes with one fp32 scale per 1x128 block, quantised once per (row, pick)
 // and expert.  Mod. rows 18 and 21: 16-byte, nontemporal weight loads.
 //

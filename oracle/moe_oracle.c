@@ -298,6 +298,35 @@ static void orc_expert(int fmt, const orc_mat* wg, const orc_mat* wu, const orc_
   free(mhat);
 }
 
+/* The down GEMV of one expert applied to a given mid (#85 Mod. row 16: down
+ * units take an expert's tile against its rows' mid; Mod. row 1: down reads
+ * mid as FP8 codes with one fp32 scale per 1x128 block).  The check of a
+ * device's down outputs calls it on that device's own mid, so that the down
+ * GEMV is judged apart from the up/gate before it:
+ *   y_n = sum_k W[n,k] * mhat_k,
+ * mhat_k = dec(midq[k]) * midqs[k/128] for FP8 experts, and mhat_k = mid32[k]
+ * (the fp32 value itself) for MXFP4 experts, whose mid is not re-quantised.
+ * y_abs_n = sum_k |W[n,k] * mhat_k| sizes rounding bounds.  W is [h_dim,
+ * i_dim] in the expert's format; every sum runs in double in index order. */
+int orc_expert_down(int fmt, const orc_mat* wd, int h_dim, int i_dim, const uint8_t* midq,
+                    const float* midqs, const float* mid32, int nthreads, double* y,
+                    double* y_abs) {
+  if (h_dim <= 0 || i_dim <= 0 || i_dim % 128 || !wd || !wd->codes || !wd->scales || !y)
+    return ORC_ERR;
+  if (fmt == ORC_FMT_FP8 && (!midq || !midqs)) return ORC_ERR;
+  if (fmt == ORC_FMT_MXFP4 && !mid32) return ORC_ERR;
+  if (fmt != ORC_FMT_FP8 && fmt != ORC_FMT_MXFP4) return ORC_ERR;
+  if (fmt == ORC_FMT_FP8 && h_dim % 128) return ORC_ERR;
+  if (nthreads < 1) nthreads = 1;
+  orc_init_luts();
+  double* mhat = (double*)malloc(sizeof(double) * i_dim);
+  for (int k = 0; k < i_dim; k++)
+    mhat[k] = fmt == ORC_FMT_FP8 ? lut_e4m3[midq[k]] * (double)midqs[k / 128] : (double)mid32[k];
+  orc_gemv(fmt, wd, h_dim, i_dim, mhat, y, y_abs, nthreads);
+  free(mhat);
+  return ORC_OK;
+}
+
 /* RMSNorm folded into the router logits for one row (#85 Mod. row 10: the
  * router stores bf16(a * gamma) with the row's sum of squares; the rstd scales
  * the logits).  u = bf16(x * gamma) (the product is exact in double, then one
@@ -352,8 +381,9 @@ int orc_router(int rows, int hidden, int n_experts, float eps, const uint16_t* x
  *     the FP8 activation blocks).  READING: FP8 activations.
  *  4. Each row applies its 8 experts and, if present, the shared expert
  *     (orc_expert).
- *  5. Combine (#85 Mod. row 16: a row's output is summed over its units in the
- *     one-row order): out = bf16(sum_j g_j * y_j + y_shared), j in pick order.
+ *  5. Combine (#85 Mod. row 16: the row's sum over its down units keeps the
+ *     order a single row would use): out = bf16(sum_j g_j * y_j + y_shared),
+ *     j in pick order.
  *     READING: no residual, no routed scaling factor; shared weight 1. */
 int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
                  const uint16_t* router_w, const orc_mat* gate, const orc_mat* up,

@@ -101,6 +101,12 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
                  const orc_mat* sh_down, const float* anchor_z, uint16_t* out,
                  orc_debug* dbg);
 
+/* The down GEMV of one expert on a given mid: FP8 experts take midq codes
+ * [i_dim] with midqs scales [i_dim/128]; MXFP4 experts take mid32 [i_dim]. */
+int orc_expert_down(int fmt, const orc_mat* wd, int h_dim, int i_dim, const uint8_t* midq,
+                    const float* midqs, const float* mid32, int nthreads, double* y,
+                    double* y_abs);
+
 /* array forms, used by the tests */
 void orc_dec_e4m3_n(const uint8_t* c, int n, double* v);
 void orc_dec_bf16_n(const uint16_t* c, int n, double* v);

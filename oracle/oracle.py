@@ -302,3 +302,30 @@ def gemv_bf16(w, x, nthreads=1):
     if rc != 0:
         raise ValueError("orc_gemv_bf16 failed")
     return y, yf
+
+
+def expert_down(fmt, codes, scales, midq=None, midqs=None, mid32=None, nthreads=1):
+    """The down GEMV of one expert on a given mid (orc_expert_down).
+
+    fmt FMT_FP8: codes uint8 [h, i], scales float32 [h/128, i/128], midq uint8
+    [i] and midqs float32 [i/128] (the mid's FP8 codes and block scales).
+    fmt FMT_MXFP4: codes uint8 [h, i/2], scales uint8 E8M0 [h, i/32], mid32
+    float32 [i] (mid itself, not re-quantised).
+    Returns (y float64 [h], y_abs float64 [h]) with y_abs = sum_k |W[n,k] mhat_k|."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    h = c.shape[0]
+    i = c.shape[1] if fmt == FMT_FP8 else 2 * c.shape[1]
+    sc = np.ascontiguousarray(scales, dtype=np.float32 if fmt == FMT_FP8 else np.uint8)
+    q = None if midq is None else np.ascontiguousarray(midq, dtype=np.uint8).ravel()
+    qs = None if midqs is None else np.ascontiguousarray(midqs, dtype=np.float32).ravel()
+    m32 = None if mid32 is None else np.ascontiguousarray(mid32, dtype=np.float32).ravel()
+    for a, n in ((q, i), (qs, i // 128), (m32, i)):
+        assert a is None or a.size == n
+    m = OrcMat(c.ctypes.data, sc.ctypes.data)
+    y = np.zeros(h, np.float64)
+    ya = np.zeros(h, np.float64)
+    rc = lib().orc_expert_down(ctypes.c_int(fmt), ctypes.byref(m), ctypes.c_int(h), ctypes.c_int(i),
+                               _p(q), _p(qs), _p(m32), ctypes.c_int(nthreads), _p(y), _p(ya))
+    if rc != 0:
+        raise ValueError("orc_expert_down failed")
+    return y, ya

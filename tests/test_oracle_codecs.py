@@ -19,7 +19,7 @@ def _facts():
         return json.load(f)
 
 
-# --------------------------------------------------------------- E4M3FN (P1)
+# --------------------------------------------------------------- E4M3FN: every code
 def test_e4m3_all_codes_match_torch():
     codes = np.arange(256, dtype=np.uint8)
     ours = O.dec_e4m3_n(codes)
@@ -39,7 +39,7 @@ def test_e4m3_published_facts():
     assert max(O.dec_e4m3_n(np.arange(0x7F, dtype=np.uint8))) == f["max_finite"]
 
 
-# ------------------------------------------------------- E2M1 / E8M0 (P2)
+# ------------------------------------------------------- E2M1 / E8M0: every code
 def test_e2m1_table():
     f = _facts()["e2m1"]
     mags = [float(v) for v in f["magnitudes"]]
@@ -66,7 +66,7 @@ def test_e8m0_all_codes_match_torch():
     assert np.array_equal(ours[:255], ref[:255])
 
 
-# ------------------------------------------------------------ bf16 / fp16 (P3)
+# ------------------------------------------------------------ bf16 / fp16: every code
 def test_bf16_all_codes_match_torch():
     codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     ours = O.dec_bf16_n(codes)
@@ -122,7 +122,7 @@ def test_round_bf16_identity_and_midpoints():
     assert np.array_equal(got, expect)
 
 
-# -------------------------------------------------------- E4M3 encoder (P6)
+# -------------------------------------------------------- E4M3 encoder: midpoints and sweeps
 def _brute_e4m3(v):
     """Nearest finite E4M3FN value by exhaustive search over torch-decoded
     codes, ties to the code with even mantissa, then v's sign."""

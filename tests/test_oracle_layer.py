@@ -22,7 +22,7 @@ def bf(v):
     return int(b.view(torch.int16).item()) & 0xFFFF
 
 
-# ------------------------------------------------------- hand-worked layer (P7)
+# ------------------------------------------------------- hand-worked layer
 H, I, E, IS = 256, 256, 9, 128
 
 
@@ -196,7 +196,7 @@ def test_hand_worked_layer_mxfp4():
     assert np.allclose(d["out_f64"][0], acc, rtol=1e-12, atol=1e-12 * np.abs(acc).max())
 
 
-# ------------------------------------- independent numpy pipeline (P8, random)
+# ------------------------------------- independent numpy pipeline (random)
 def _np_fp8(codes, scales):
     v = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
     s = np.repeat(np.repeat(scales.astype(np.float64), 128, 0), 128, 1)
@@ -282,7 +282,7 @@ def test_oracle_matches_independent_numpy_pipeline(fmt, act):
     assert np.allclose(d["out_f64"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
-# ---------------------------------------------------------- invariants (P9)
+# ---------------------------------------------------------- invariants
 def test_rows_are_independent_and_permutation_equivariant():
     import bit_moe_decode_amd.synth as S
     layer = S.make_layer("tiny", seed=1001)
@@ -347,7 +347,7 @@ def test_midq_layout_size_matches_the_pages():
         assert round(total / 1000) == kb, (rows, total)
 
 
-# ------------------------------------------------------------ 1-bit (P10)
+# ------------------------------------------------------------ 1-bit closed forms
 def _q1_blocks(bits, d16):
     n, groups = d16.shape
     blk = np.zeros((n, groups, 18), np.uint8)
