@@ -54,7 +54,7 @@ class Weights(ctypes.Structure):
 class Debug(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "rstd", "ids", "gates", "n_groups", "grp_expert", "grp_owner", "grp_mask",
-        "grp_slot", "act_q", "act_s", "mid", "midq", "midqs")] + [
+        "grp_slot", "act_q", "act_s", "mid", "midq", "midqs", "y")] + [
         ("max_groups", ctypes.c_int32), ("mid_stride", ctypes.c_int32)]
 
 
@@ -321,6 +321,7 @@ class LayerRunner:
             mid=g(v.mid, R * 9 * st, f32).reshape(R, 9, st)[:rows],
             midq=g(v.midq, R * 9 * st, u8).reshape(R, 9, st)[:rows],
             midqs=g(v.midqs, R * 9 * (st // 128), f32).reshape(R, 9, st // 128)[:rows],
+            y=g(v.y, R * 9 * H, f32).reshape(R, 9, H)[:rows],
         )
         n = d["n_groups"]
         for k in ("grp_expert", "grp_owner", "grp_mask", "grp_slot"):

@@ -290,6 +290,7 @@ moe_status moe_decode_debug_view(const moe_decode_ctx* ctx, moe_decode_debug* v)
   v->mid = w.mid;
   v->midq = w.midq;
   v->midqs = w.midqs;
+  v->y = w.ypart;
   v->max_groups = ctx->plan.groups;
   v->mid_stride = ctx->plan.imax;
   return MOE_OK;

@@ -91,8 +91,8 @@ typedef enum {
 /* flags */
 enum {
   /* Skip the dedup: every (row, pick) streams its expert separately.  For the
-   * bitwise A/B check that dedup changes no output bit (#85 Mod. row 16: each
-   * row's output is summed in the one-row order). */
+   * bitwise A/B check that dedup changes no output bit (#85 Mod. row 16: a
+   * row adds its units up in the order it would alone). */
   MOE_F_NO_DEDUP = 1u << 1
 };
 
@@ -173,6 +173,8 @@ typedef struct {
   const float* mid;          /* [max_rows, 9, mid_stride] fp32, before quantisation */
   const uint8_t* midq;       /* [max_rows, 9, mid_stride] FP8 codes */
   const float* midqs;        /* [max_rows, 9, mid_stride/128] block scales */
+  const float* y;            /* [max_rows, 9, H] fp32 down output per (row, pick), before
+                                the gate-weighted combine; same indexing as mid */
   int32_t max_groups;        /* min(8 * max_rows, E), or 8 * max_rows with MOE_F_NO_DEDUP */
   int32_t mid_stride;        /* max(I, Is) */
 } moe_decode_debug;

@@ -241,33 +241,40 @@ void orc_quant_blocks(const float* v, int n, uint8_t* q, float* s) {
 
 /* y[n] = sum_k W[n,k] * h[k] for one stored matrix, W decoded element by
  * element: FP8 code * fp32 block scale (per 128x128), or E2M1 * 2^(E8M0-127)
- * (per 32 along K, low nibble = even element). */
+ * (per 32 along K, low nibble = even element).  Two optional outputs size
+ * rounding bounds and take no part in y: yabs[n] = sum_k |W[n,k] h[k]|, and
+ * ygmax[n] = the sum, over the groups of 8 consecutive k (k = 8i .. 8i+7), of
+ * the largest |W[n,k] h[k]| in the group. */
 static void orc_gemv(int fmt, const orc_mat* w, int n_out, int k_in, const double* h, double* y,
-                     double* yabs, int nthreads) {
+                     double* yabs, double* ygmax, int nthreads) {
   const uint8_t* codes = w->codes;
 #pragma omp parallel for num_threads(nthreads) schedule(static)
   for (int n = 0; n < n_out; n++) {
-    double acc = 0.0, aabs = 0.0;
-    if (fmt == ORC_FMT_FP8) {
-      const float* sc = (const float*)w->scales;
-      for (int k = 0; k < k_in; k++) {
-        double wv = lut_e4m3[codes[(size_t)n * k_in + k]] *
-                    (double)sc[(size_t)(n / 128) * (k_in / 128) + k / 128];
-        acc += wv * h[k];
-        aabs += fabs(wv * h[k]);
-      }
-    } else {
-      const uint8_t* sc = (const uint8_t*)w->scales;
-      for (int k = 0; k < k_in; k++) {
+    double acc = 0.0, aabs = 0.0, gsum = 0.0, gmax = 0.0;
+    for (int k = 0; k < k_in; k++) {
+      double wv;
+      if (fmt == ORC_FMT_FP8) {
+        const float* sc = (const float*)w->scales;
+        wv = lut_e4m3[codes[(size_t)n * k_in + k]] *
+             (double)sc[(size_t)(n / 128) * (k_in / 128) + k / 128];
+      } else {
+        const uint8_t* sc = (const uint8_t*)w->scales;
         uint8_t byte = codes[(size_t)n * (k_in / 2) + k / 2];
         uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 15);
-        double wv = lut_e2m1[nib] * lut_e8m0[sc[(size_t)n * (k_in / 32) + k / 32]];
-        acc += wv * h[k];
-        aabs += fabs(wv * h[k]);
+        wv = lut_e2m1[nib] * lut_e8m0[sc[(size_t)n * (k_in / 32) + k / 32]];
+      }
+      const double t = wv * h[k];
+      acc += t;
+      aabs += fabs(t);
+      if (fabs(t) > gmax) gmax = fabs(t);
+      if (k % 8 == 7 || k == k_in - 1) {
+        gsum += gmax;
+        gmax = 0.0;
       }
     }
     y[n] = acc;
-    if (yabs) yabs[n] = aabs; /* sum of |terms|: sizes rounding-error bounds */
+    if (yabs) yabs[n] = aabs;
+    if (ygmax) ygmax[n] = gsum;
   }
 }
 
@@ -280,10 +287,11 @@ static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 static void orc_expert(int fmt, const orc_mat* wg, const orc_mat* wu, const orc_mat* wd, int h_dim,
                        int i_dim, const double* hin, int nthreads, double* mid_out,
                        uint8_t* midq_out, float* midqs_out, double* y, double* gate,
-                       double* upv, double* gate_abs, double* up_abs) {
+                       double* upv, double* gate_abs, double* up_abs, double* gate_gmax,
+                       double* up_gmax) {
   double* mhat = (double*)malloc(sizeof(double) * i_dim);
-  orc_gemv(fmt, wg, i_dim, h_dim, hin, gate, gate_abs, nthreads);
-  orc_gemv(fmt, wu, i_dim, h_dim, hin, upv, up_abs, nthreads);
+  orc_gemv(fmt, wg, i_dim, h_dim, hin, gate, gate_abs, gate_gmax, nthreads);
+  orc_gemv(fmt, wu, i_dim, h_dim, hin, upv, up_abs, up_gmax, nthreads);
   for (int n = 0; n < i_dim; n++) mid_out[n] = orc_silu(gate[n]) * upv[n];
   if (fmt == ORC_FMT_FP8) {
     float* mf = (float*)malloc(sizeof(float) * i_dim);
@@ -294,7 +302,7 @@ static void orc_expert(int fmt, const orc_mat* wg, const orc_mat* wu, const orc_
   } else {
     for (int n = 0; n < i_dim; n++) mhat[n] = mid_out[n];
   }
-  orc_gemv(fmt, wd, h_dim, i_dim, mhat, y, NULL, nthreads);
+  orc_gemv(fmt, wd, h_dim, i_dim, mhat, y, NULL, NULL, nthreads);
   free(mhat);
 }
 
@@ -306,11 +314,12 @@ static void orc_expert(int fmt, const orc_mat* wg, const orc_mat* wu, const orc_
  *   y_n = sum_k W[n,k] * mhat_k,
  * mhat_k = dec(midq[k]) * midqs[k/128] for FP8 experts, and mhat_k = mid32[k]
  * (the fp32 value itself) for MXFP4 experts, whose mid is not re-quantised.
- * y_abs_n = sum_k |W[n,k] * mhat_k| sizes rounding bounds.  W is [h_dim,
+ * y_abs_n = sum_k |W[n,k] * mhat_k| and y_gmax (the per-group maxima of
+ * orc_gemv) size rounding bounds.  W is [h_dim,
  * i_dim] in the expert's format; every sum runs in double in index order. */
 int orc_expert_down(int fmt, const orc_mat* wd, int h_dim, int i_dim, const uint8_t* midq,
                     const float* midqs, const float* mid32, int nthreads, double* y,
-                    double* y_abs) {
+                    double* y_abs, double* y_gmax) {
   if (h_dim <= 0 || i_dim <= 0 || i_dim % 128 || !wd || !wd->codes || !wd->scales || !y)
     return ORC_ERR;
   if (fmt == ORC_FMT_FP8 && (!midq || !midqs)) return ORC_ERR;
@@ -322,7 +331,7 @@ int orc_expert_down(int fmt, const orc_mat* wd, int h_dim, int i_dim, const uint
   double* mhat = (double*)malloc(sizeof(double) * i_dim);
   for (int k = 0; k < i_dim; k++)
     mhat[k] = fmt == ORC_FMT_FP8 ? lut_e4m3[midq[k]] * (double)midqs[k / 128] : (double)mid32[k];
-  orc_gemv(fmt, wd, h_dim, i_dim, mhat, y, y_abs, nthreads);
+  orc_gemv(fmt, wd, h_dim, i_dim, mhat, y, y_abs, y_gmax, nthreads);
   free(mhat);
   return ORC_OK;
 }
@@ -415,6 +424,8 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
   double* uv = (double*)malloc(sizeof(double) * Imax);
   double* ga = (double*)malloc(sizeof(double) * Imax);
   double* ua = (double*)malloc(sizeof(double) * Imax);
+  double* gg = (double*)malloc(sizeof(double) * Imax);
+  double* ug = (double*)malloc(sizeof(double) * Imax);
   uint8_t* mq = (uint8_t*)malloc(Imax);
   float* ms = (float*)malloc(sizeof(float) * (Imax / 128));
   int rc = ORC_OK;
@@ -475,7 +486,7 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
       memset(mq, 0, Imax);
       for (int b = 0; b < Imax / 128; b++) ms[b] = 0.0f;
       orc_expert(fmt, wg, wu, wd, H, idim, hin, nt, midv, mq, ms, ys + (size_t)j * H, gv, uv, ga,
-                 ua);
+                 ua, gg, ug);
       size_t base = ((size_t)r * 9 + j) * Imax;
       for (int n = 0; n < idim; n++) {
         if (dbg->mid) dbg->mid[base + n] = midv[n];
@@ -483,6 +494,8 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
         if (dbg->up) dbg->up[base + n] = uv[n];
         if (dbg->gate_abs) dbg->gate_abs[base + n] = ga[n];
         if (dbg->up_abs) dbg->up_abs[base + n] = ua[n];
+        if (dbg->gate_gmax) dbg->gate_gmax[base + n] = gg[n];
+        if (dbg->up_gmax) dbg->up_gmax[base + n] = ug[n];
       }
       if (dbg->midq) memcpy(dbg->midq + base, mq, idim);
       if (dbg->midqs)
@@ -517,6 +530,8 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
   free(uv);
   free(ga);
   free(ua);
+  free(gg);
+  free(ug);
   free(mq);
   free(ms);
   return rc;

@@ -93,6 +93,9 @@ typedef struct {
   double* up;       /* [R][9][Imax] */
   double* gate_abs; /* [R][9][Imax] sum_k |W_gate[n,k] h_k|: sizes rounding bounds */
   double* up_abs;   /* [R][9][Imax] */
+  double* gate_gmax; /* [R][9][Imax] sum over groups of 8 consecutive k of max |W_gate h|:
+                        sizes the bounds of dot products summed in groups of 8 */
+  double* up_gmax;  /* [R][9][Imax] */
 } orc_debug;
 
 int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
@@ -105,7 +108,7 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
  * [i_dim] with midqs scales [i_dim/128]; MXFP4 experts take mid32 [i_dim]. */
 int orc_expert_down(int fmt, const orc_mat* wd, int h_dim, int i_dim, const uint8_t* midq,
                     const float* midqs, const float* mid32, int nthreads, double* y,
-                    double* y_abs);
+                    double* y_abs, double* y_gmax);
 
 /* array forms, used by the tests */
 void orc_dec_e4m3_n(const uint8_t* c, int n, double* v);

@@ -38,7 +38,7 @@ class OrcCfg(ctypes.Structure):
 class OrcDebug(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "z", "rstd", "u", "ids", "gates", "act_q", "act_s", "mid", "midq", "midqs",
-        "y", "out_f64", "gate", "up", "gate_abs", "up_abs")]
+        "y", "out_f64", "gate", "up", "gate_abs", "up_abs", "gate_gmax", "up_gmax")]
 
 
 def lib():
@@ -229,7 +229,8 @@ def moe_step(cfg, x, gamma, router_w, experts, shared=None, anchor_z=None, nthre
         mid=np.zeros((R, 9, Imax)), midq=np.zeros((R, 9, Imax), np.uint8),
         midqs=np.zeros((R, 9, Imax // 128), np.float32), y=np.zeros((R, 9, H)),
         out_f64=np.zeros((R, H)), gate=np.zeros((R, 9, Imax)), up=np.zeros((R, 9, Imax)),
-        gate_abs=np.zeros((R, 9, Imax)), up_abs=np.zeros((R, 9, Imax)))
+        gate_abs=np.zeros((R, 9, Imax)), up_abs=np.zeros((R, 9, Imax)),
+        gate_gmax=np.zeros((R, 9, Imax)), up_gmax=np.zeros((R, 9, Imax)))
     d = OrcDebug(**{k: v.ctypes.data for k, v in dbg.items()})
     rc = lib().orc_moe_step(ctypes.byref(c), _p(x), _p(gamma), _p(router_w), G, U, D,
                             psg, psu, psd, _p(az), _p(out), ctypes.byref(d))
@@ -311,7 +312,9 @@ def expert_down(fmt, codes, scales, midq=None, midqs=None, mid32=None, nthreads=
     [i] and midqs float32 [i/128] (the mid's FP8 codes and block scales).
     fmt FMT_MXFP4: codes uint8 [h, i/2], scales uint8 E8M0 [h, i/32], mid32
     float32 [i] (mid itself, not re-quantised).
-    Returns (y float64 [h], y_abs float64 [h]) with y_abs = sum_k |W[n,k] mhat_k|."""
+    Returns (y float64 [h], y_abs float64 [h], y_gmax float64 [h]) with y_abs =
+    sum_k |W[n,k] mhat_k| and y_gmax = the sum over groups of 8 consecutive k of
+    the largest |W[n,k] mhat_k| of the group."""
     c = np.ascontiguousarray(codes, dtype=np.uint8)
     h = c.shape[0]
     i = c.shape[1] if fmt == FMT_FP8 else 2 * c.shape[1]
@@ -324,8 +327,10 @@ def expert_down(fmt, codes, scales, midq=None, midqs=None, mid32=None, nthreads=
     m = OrcMat(c.ctypes.data, sc.ctypes.data)
     y = np.zeros(h, np.float64)
     ya = np.zeros(h, np.float64)
+    yg = np.zeros(h, np.float64)
     rc = lib().orc_expert_down(ctypes.c_int(fmt), ctypes.byref(m), ctypes.c_int(h), ctypes.c_int(i),
-                               _p(q), _p(qs), _p(m32), ctypes.c_int(nthreads), _p(y), _p(ya))
+                               _p(q), _p(qs), _p(m32), ctypes.c_int(nthreads), _p(y), _p(ya),
+                               _p(yg))
     if rc != 0:
         raise ValueError("orc_expert_down failed")
-    return y, ya
+    return y, ya, yg

@@ -113,11 +113,16 @@ def test_tiny_tied_logits_go_to_lower_id():
         w[b] = w[a]
     x = S.make_x(4, 256, seed=2500)
     _, _, gpu, _ = _run(layer, x)
+    both = 0
     for r in range(4):
         ids = list(gpu["ids"][r])
         for a, b in ((3, 17), (5, 6), (20, 31), (0, 9)):
+            assert gpu["logits"][r][a] == gpu["logits"][r][b]
+            assert not (b in ids and a not in ids), (r, a, b, ids)  # the higher ID never alone
             if a in ids and b in ids:
-                assert ids.index(a) < ids.index(b)
+                assert ids.index(a) + 1 == ids.index(b)
+                both += 1
+    assert both > 0, "no duplicated pair was picked together: the order was never compared"
 
 
 def test_zero_rows_is_a_noop(tiny):
@@ -197,6 +202,22 @@ def test_glm_parity(glm, rows, mode):
     x = S.make_x(rows, glm.hidden, seed=3000 + 10 * rows + (mode == "corr"), mode=mode)
     _, _, gpu, rep = _run(glm, x, cache=glm.extra.setdefault("host", {}))
     _say(rep)
+
+
+def test_glm_zero_row_and_zero_block(glm):
+    """At GLM scale, 8 rows: row 0 all zero (every logit +0, picks 0..7,
+    activation, mid and output zero), row 1 with one zero 128-block."""
+    x = S.make_x(8, glm.hidden, seed=3300)
+    x[0] = 0
+    x[1, 1024:1152] = 0
+    _say("glm zero row and zero block, 8 rows")
+    _, out, gpu, rep = _run(glm, x, cache=glm.extra.setdefault("host", {}))
+    _say(rep)
+    assert list(gpu["ids"][0]) == list(range(8))
+    assert not gpu["act_q"][0].any() and not gpu["act_s"][0].any()
+    assert gpu["act_s"][1, 8] == 0 and not gpu["act_q"][1, 1024:1152].any()
+    assert not gpu["midqs"][0].any() and not gpu["y"][0].any()
+    assert not out[0].float().abs().sum().item()
 
 
 @pytest.mark.parametrize("rows", [1, 4, 8])

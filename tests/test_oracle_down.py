@@ -21,11 +21,13 @@ def test_fp8_all_one_codes_closed_form():
     t = np.array([1 / 2, -3 / 4, 5 / 8], F32)
     codes = np.full((256, 384), 0x38, np.uint8)
     midq = np.full(384, 0x38, np.uint8)
-    y, ya = O.expert_down(O.FMT_FP8, codes, S, midq=midq, midqs=t)
+    y, ya, yg = O.expert_down(O.FMT_FP8, codes, S, midq=midq, midqs=t)
     blk = 128 * (S.astype(float) @ t.astype(float))
     blk_abs = 128 * (np.abs(S.astype(float)) @ np.abs(t.astype(float)))
     assert np.array_equal(y, np.repeat(blk, 128))
     assert np.array_equal(ya, np.repeat(blk_abs, 128))
+    # every term of a group of 8 is equal: the group maxima sum to y_abs / 8
+    assert np.array_equal(yg, np.repeat(blk_abs, 128) / 8)
     # the transposed reading of the scale grid would give other values
     assert not np.allclose(blk, 128 * (S.astype(float)[:, ::-1] @ t.astype(float)))
 
@@ -41,11 +43,12 @@ def test_fp8_single_mid_code():
         midq = np.zeros(256, np.uint8)
         midq[k0] = 0xC4
         midqs = np.array([0.25, 0.25], F32)
-        y, ya = O.expert_down(O.FMT_FP8, codes, S, midq=midq, midqs=midqs)
+        y, ya, yg = O.expert_down(O.FMT_FP8, codes, S, midq=midq, midqs=midqs)
         w = torch.from_numpy(codes[:, k0].copy()).view(torch.float8_e4m3fn).double().numpy()
         expect = w * np.repeat(S[:, k0 // 128].astype(float), 128) * (-3.0 * 0.25)
         assert np.array_equal(y, expect)
         assert np.array_equal(ya, np.abs(expect))
+        assert np.array_equal(yg, np.abs(expect))  # one nonzero term
 
 
 def test_mxfp4_exponent_extremes_and_negative_zero():
@@ -65,7 +68,7 @@ def test_mxfp4_exponent_extremes_and_negative_zero():
         e8[2 * i + 1] = [c, c, c, 254][: I // 32] if c != 254 else c
     cg = np.array([0.5, 2.0, -0.25, 8.0], F32)
     mid = np.repeat(cg, 32)
-    y, ya = O.expert_down(O.FMT_MXFP4, packed, e8, mid32=mid)
+    y, ya, _ = O.expert_down(O.FMT_MXFP4, packed, e8, mid32=mid)
     count = np.array([32, 16, 32, 0], float)
     expect = np.array([sum(2.0 ** (int(e8[h, g]) - 127) * float(cg[g]) * count[g]
                            for g in range(4)) for h in range(H)])
@@ -84,20 +87,25 @@ def test_against_independent_numpy_pipeline():
     midq = rng.integers(0, 256, 512).astype(np.uint8)
     midq[(midq & 0x7F) == 0x7F] = 0x11
     midqs = (rng.random(4) * 1e-3).astype(F32)
-    y, ya = O.expert_down(O.FMT_FP8, codes, S, midq=midq, midqs=midqs, nthreads=4)
+    y, ya, yg = O.expert_down(O.FMT_FP8, codes, S, midq=midq, midqs=midqs, nthreads=4)
     mhat = torch.from_numpy(midq).view(torch.float8_e4m3fn).double().numpy() * np.repeat(
         midqs.astype(float), 128)
     W = _np_fp8(codes, S)
     assert np.allclose(y, W @ mhat, rtol=0, atol=1e-13 * ya.max())
     assert np.allclose(ya, np.abs(W) @ np.abs(mhat), rtol=1e-13, atol=0)
+    gm = np.abs(W * mhat[None, :]).reshape(W.shape[0], -1, 8).max(axis=2).sum(axis=1)
+    assert np.allclose(yg, gm, rtol=1e-13, atol=0)
+    assert (yg <= ya).all() and (8 * yg >= ya).all()
     # MXFP4: random nibbles (-0 included), E8M0 around 127, fp32 mid
     packed = rng.integers(0, 256, (256, 256)).astype(np.uint8)
     e8 = rng.integers(100, 150, (256, 16)).astype(np.uint8)
     mid = rng.standard_normal(512).astype(F32)
-    y, ya = O.expert_down(O.FMT_MXFP4, packed, e8, mid32=mid, nthreads=4)
+    y, ya, yg = O.expert_down(O.FMT_MXFP4, packed, e8, mid32=mid, nthreads=4)
     W = _np_mxfp4(packed, e8)
     assert np.allclose(y, W @ mid.astype(float), rtol=0, atol=1e-13 * ya.max())
     assert np.allclose(ya, np.abs(W) @ np.abs(mid.astype(float)), rtol=1e-13, atol=0)
+    gm = np.abs(W * mid.astype(float)[None, :]).reshape(W.shape[0], -1, 8).max(axis=2).sum(axis=1)
+    assert np.allclose(yg, gm, rtol=1e-13, atol=0)
 
 
 @pytest.mark.parametrize("fmt", [O.FMT_FP8, O.FMT_MXFP4])
@@ -114,10 +122,10 @@ def test_agrees_with_the_step_oracle(fmt):
             e = int(d["ids"][r, j])
             m = [t.numpy() for t in layer.routed.expert(e)]
             if fmt == O.FMT_FP8:
-                y, _ = O.expert_down(fmt, m[4], m[5], midq=d["midq"][r, j, :layer.inter],
-                                     midqs=d["midqs"][r, j, :layer.inter // 128])
+                y, _, _ = O.expert_down(fmt, m[4], m[5], midq=d["midq"][r, j, :layer.inter],
+                                        midqs=d["midqs"][r, j, :layer.inter // 128])
             else:
-                y, _ = O.expert_down(fmt, m[4], m[5], mid32=d["mid"][r, j, :layer.inter])
+                y, _, _ = O.expert_down(fmt, m[4], m[5], mid32=d["mid"][r, j, :layer.inter])
                 # the step keeps MXFP4 mid in double; the fp32 copy differs by its rounding
                 yd = _np_mxfp4(m[4], m[5]) @ d["mid"][r, j, :layer.inter]
                 assert np.allclose(y, yd, rtol=0, atol=1e-6 * np.abs(yd).max())

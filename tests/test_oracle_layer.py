@@ -132,6 +132,9 @@ def test_hand_worked_layer_fp8():
         for mats, key in ((a, "gate_abs"), (b, "up_abs")):
             blk = 128 * A * cf["rstd"] * (np.abs(mats[e][:, 0]) + 2 * np.abs(mats[e][:, 1]))
             assert np.allclose(d[key][0, j, :I], np.repeat(blk, 128), rtol=1e-13, atol=0)
+            # constant terms within each group of 8: the group maxima are 1/8 of that
+            gkey = key.replace("_abs", "_gmax")
+            assert np.allclose(d[gkey][0, j, :I], np.repeat(blk, 128) / 8, rtol=1e-13, atol=0)
     assert np.allclose(d["out_f64"][0], cf["out"], rtol=1e-13, atol=0)
     assert np.array_equal(out[0], O.round_bf16_n(d["out_f64"][0]))
 
@@ -280,6 +283,18 @@ def test_oracle_matches_independent_numpy_pipeline(fmt, act):
     out, d = _run_oracle(layer, x, act_fmt=act)
     ref = _np_step(layer, x, fmt, act)
     assert np.allclose(d["out_f64"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # the group-of-8 maxima of the gate terms, from the same decoders
+    dec = _np_fp8 if fmt == O.FMT_FP8 else _np_mxfp4
+    r, j = 1, 3
+    e = int(d["ids"][r, j])
+    m = [t.numpy() for t in layer.routed.expert(e)]
+    Wg = dec(m[0], m[1])
+    if act == O.ACT_BF16:
+        h = O.dec_bf16_n(d["u"][r]) * d["rstd"][r]
+    else:
+        h = O.dec_e4m3_n(d["act_q"][r]) * np.repeat(d["act_s"][r].astype(float), 128) * d["rstd"][r]
+    gm = np.abs(Wg * h[None, :]).reshape(Wg.shape[0], -1, 8).max(axis=2).sum(axis=1)
+    assert np.allclose(d["gate_gmax"][r, j, :layer.inter], gm, rtol=1e-12, atol=0)
 
 
 # ---------------------------------------------------------- invariants
