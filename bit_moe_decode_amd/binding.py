@@ -82,6 +82,10 @@ def lib():
         L.moe_decode_step.restype = ctypes.c_int
         L.moe_decode_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                       ctypes.POINTER(Weights), ctypes.c_void_p, ctypes.c_void_p]
+        L.moe_decode_step_noalloc.restype = ctypes.c_int
+        L.moe_decode_step_noalloc.argtypes = [ctypes.POINTER(Config), ctypes.c_void_p,
+                                              ctypes.c_int32, ctypes.POINTER(Weights),
+                                              ctypes.c_void_p, ctypes.c_void_p]
         L.moe_decode_debug_view.restype = ctypes.c_int
         L.moe_decode_debug_view.argtypes = [ctypes.c_void_p, ctypes.POINTER(Debug)]
         L.moe_decode_set_timing.restype = ctypes.c_int
@@ -192,6 +196,16 @@ class Context:
             self.close()
         except Exception:
             pass
+
+
+NOALLOC_MAX_WORKSPACE = 8 << 20  # MOE_DECODE_NOALLOC_MAX_WORKSPACE
+
+
+def step_noalloc_status(cfg: Config, x, rows, weights: Weights, out, stream=None):
+    """moe_decode_step_noalloc: the step with the library's static device
+    scratch instead of a context's workspace; returns the status."""
+    return lib().moe_decode_step_noalloc(ctypes.byref(cfg), _ptr(x), int(rows),
+                                         ctypes.byref(weights), _ptr(out), _stream(stream))
 
 
 def make_weights(gamma, router_w, routed, shared=None) -> Weights:

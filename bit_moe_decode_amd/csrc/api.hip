@@ -3,6 +3,7 @@
 // host-only and run before anything is enqueued.
 #include "moe_decode.h"
 
+#include <mutex>
 #include <new>
 
 #include "device_common.h"
@@ -32,6 +33,14 @@ __global__ void moe_fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
 }  // namespace moe
 
 using namespace moe;
+
+// Device scratch of moe_decode_step_noalloc: the workspace of a step that
+// brings none.  One copy per GPU the library runs on, held until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device
+// array: the device address comes from hipGetSymbolAddress, once per device
+// (scratch_on_device below), and only that address is handed to kernels.
+constexpr size_t kScratchBytes = MOE_DECODE_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -114,6 +123,30 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The kernels' view of a workspace laid out by `p` from base address `b`.
+Ws make_view(char* b, const Plan& p) {
+  Ws v;
+  v.logits = reinterpret_cast<float*>(b + p.off_logits);
+  v.rstd = reinterpret_cast<float*>(b + p.off_rstd);
+  v.ids = reinterpret_cast<int32_t*>(b + p.off_ids);
+  v.gates = reinterpret_cast<float*>(b + p.off_gates);
+  v.n_groups = reinterpret_cast<int32_t*>(b + p.off_ngroups);
+  v.grp_expert = reinterpret_cast<int32_t*>(b + p.off_gexpert);
+  v.grp_owner = reinterpret_cast<uint8_t*>(b + p.off_gowner);
+  v.grp_mask = reinterpret_cast<uint8_t*>(b + p.off_gmask);
+  v.grp_slot = reinterpret_cast<uint8_t*>(b + p.off_gslot);
+  v.grp_rows = reinterpret_cast<uint8_t*>(b + p.off_grows);
+  v.grp_nrows = reinterpret_cast<uint8_t*>(b + p.off_gnrows);
+  v.act_q = reinterpret_cast<uint8_t*>(b + p.off_actq);
+  v.act_s = reinterpret_cast<float*>(b + p.off_acts);
+  v.mid = reinterpret_cast<float*>(b + p.off_mid);
+  v.midq = reinterpret_cast<uint8_t*>(b + p.off_midq);
+  v.midqs = reinterpret_cast<float*>(b + p.off_midqs);
+  v.ypart = reinterpret_cast<float*>(b + p.off_ypart);
+  v.act_u = reinterpret_cast<uint16_t*>(b + p.off_actu);
+  return v;
+}
+
 }  // namespace
 
 struct moe_decode_ctx {
@@ -150,26 +183,7 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
   c->ws = static_cast<char*>(workspace);
   c->timing = false;
   c->last_rows = 0;
-  char* b = c->ws;
-  Ws& v = c->view;
-  v.logits = reinterpret_cast<float*>(b + p.off_logits);
-  v.rstd = reinterpret_cast<float*>(b + p.off_rstd);
-  v.ids = reinterpret_cast<int32_t*>(b + p.off_ids);
-  v.gates = reinterpret_cast<float*>(b + p.off_gates);
-  v.n_groups = reinterpret_cast<int32_t*>(b + p.off_ngroups);
-  v.grp_expert = reinterpret_cast<int32_t*>(b + p.off_gexpert);
-  v.grp_owner = reinterpret_cast<uint8_t*>(b + p.off_gowner);
-  v.grp_mask = reinterpret_cast<uint8_t*>(b + p.off_gmask);
-  v.grp_slot = reinterpret_cast<uint8_t*>(b + p.off_gslot);
-  v.grp_rows = reinterpret_cast<uint8_t*>(b + p.off_grows);
-  v.grp_nrows = reinterpret_cast<uint8_t*>(b + p.off_gnrows);
-  v.act_q = reinterpret_cast<uint8_t*>(b + p.off_actq);
-  v.act_s = reinterpret_cast<float*>(b + p.off_acts);
-  v.mid = reinterpret_cast<float*>(b + p.off_mid);
-  v.midq = reinterpret_cast<uint8_t*>(b + p.off_midq);
-  v.midqs = reinterpret_cast<float*>(b + p.off_midqs);
-  v.ypart = reinterpret_cast<float*>(b + p.off_ypart);
-  v.act_u = reinterpret_cast<uint16_t*>(b + p.off_actu);
+  c->view = make_view(c->ws, p);
   // clear the whole workspace once, so that debug views read before the
   // first step are well defined
   const size_t words = p.total / 4;
@@ -185,10 +199,9 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
 
 namespace {
 // Validates the weights and fills the kernels' argument views for a step of
-// `rows` rows on this context.
-moe_status step_args(const moe_decode_ctx* ctx, int rows, const moe_decode_weights* w,
-                     Weights* wtp, Dims* dp) {
-  const Plan& p = ctx->plan;
+// `rows` rows of a layer with config `cfg` and plan `p`.
+moe_status step_args(const moe_decode_config& cfg, const Plan& p, int rows,
+                     const moe_decode_weights* w, Weights* wtp, Dims* dp) {
   if (!w) return MOE_ERR_INVALID_ARG;
   const void* need[] = {w->rms_gamma, w->router_w, w->gate.codes, w->gate.scales, w->up.codes,
                         w->up.scales, w->down.codes, w->down.scales};
@@ -225,9 +238,9 @@ moe_status step_args(const moe_decode_ctx* ctx, int rows, const moe_decode_weigh
   d.max_rows = p.R;
   d.imax = p.imax;
   d.ks = p.ks;
-  d.no_dedup = (ctx->cfg.flags & MOE_F_NO_DEDUP) ? 1 : 0;
-  d.eps = ctx->cfg.rms_eps;
-  d.act_bf16 = ctx->cfg.act_fmt == MOE_ACT_BF16 ? 1 : 0;
+  d.no_dedup = (cfg.flags & MOE_F_NO_DEDUP) ? 1 : 0;
+  d.eps = cfg.rms_eps;
+  d.act_bf16 = cfg.act_fmt == MOE_ACT_BF16 ? 1 : 0;
   return MOE_OK;
 }
 
@@ -235,6 +248,55 @@ moe_status step_args(const moe_decode_ctx* ctx, int rows, const moe_decode_weigh
 int step_groups(const Plan& p, const Dims& d) {
   const int picks = 8 * d.rows;
   return d.no_dedup ? picks : (picks < p.E ? picks : p.E);
+}
+
+// Host checks of a step's x and out (rows >= 1).
+moe_status check_io(const Plan& p, const uint16_t* x, int rows, const moe_decode_weights* w,
+                    const uint16_t* out) {
+  if (!x || !w || !out || !aligned16(x) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)rows * p.H * 2;
+  const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out;
+  if (xa < oa + bytes && oa < xa + bytes) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// The device address of `scratch` on the current device, looked up once per
+// device under a lock and kept.
+moe_status scratch_on_device(char** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static char* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_DEVICE;
+    addr[dev] = static_cast<char*>(p);
+  }
+  *out = addr[dev];
+  return MOE_OK;
+}
+
+// The step's five launches on `stream` over workspace view `v`; with `ev`,
+// an event before the first and after each.
+moe_status enqueue_step(int routed_fmt, const Plan& p, const Ws& v, const uint16_t* x,
+                        const Weights& wt, const Dims& d, uint16_t* out, hipStream_t stream,
+                        hipEvent_t* ev) {
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (launch_router(x, wt, v, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  // routing, with the shared expert's up/gate alongside
+  if (launch_route(wt, v, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  const int groups = step_groups(p, d);
+  if (launch_upgate(routed_fmt, groups, wt, v, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (launch_down(routed_fmt, groups, wt, v, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (launch_combine(v, d, out, stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (ev && hipEventRecord(ev[5], stream) != hipSuccess) return MOE_ERR_DEVICE;
+  return MOE_OK;
 }
 }  // namespace
 
@@ -244,33 +306,36 @@ moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
   const Plan& p = ctx->plan;
   if (rows < 0 || rows > p.R) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;
-  if (!x || !w || !out || !aligned16(x) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
-  const size_t bytes = (size_t)rows * p.H * 2;
-  const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out;
-  if (xa < oa + bytes && oa < xa + bytes) return MOE_ERR_INVALID_ARG;
+  moe_status st = check_io(p, x, rows, w, out);
+  if (st != MOE_OK) return st;
   Weights wt;
   Dims d;
-  const moe_status st = step_args(ctx, rows, w, &wt, &d);
+  st = step_args(ctx->cfg, p, rows, w, &wt, &d);
   if (st != MOE_OK) return st;
   ctx->last_rows = rows;
+  return enqueue_step(ctx->cfg.routed_fmt, p, ctx->view, x, wt, d, out, stream,
+                      ctx->timing ? ctx->events : nullptr);
+}
 
-  hipEvent_t* ev = ctx->timing ? ctx->events : nullptr;
-  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (launch_router(x, wt, ctx->view, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  // routing, with the shared expert's up/gate alongside
-  if (launch_route(wt, ctx->view, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  const int groups = step_groups(p, d);
-  if (launch_upgate(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream) != hipSuccess)
-    return MOE_ERR_DEVICE;
-  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (launch_down(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream) != hipSuccess)
-    return MOE_ERR_DEVICE;
-  if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (launch_combine(ctx->view, d, out, stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (ev && hipEventRecord(ev[5], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  return MOE_OK;
+moe_status moe_decode_step_noalloc(const moe_decode_config* cfg, const uint16_t* x,
+                                   int32_t rows, const moe_decode_weights* w, uint16_t* out,
+                                   hipStream_t stream) {
+  Plan p;
+  moe_status st = plan_config(cfg, &p);
+  if (st != MOE_OK) return st;
+  if (p.total > kScratchBytes) return MOE_ERR_WORKSPACE;
+  if (rows < 0 || rows > p.R) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  st = check_io(p, x, rows, w, out);
+  if (st != MOE_OK) return st;
+  Weights wt;
+  Dims d;
+  st = step_args(*cfg, p, rows, w, &wt, &d);
+  if (st != MOE_OK) return st;
+  char* base = nullptr;
+  st = scratch_on_device(&base);
+  if (st != MOE_OK) return st;
+  return enqueue_step(cfg->routed_fmt, p, make_view(base, p), x, wt, d, out, stream, nullptr);
 }
 
 moe_status moe_decode_debug_view(const moe_decode_ctx* ctx, moe_decode_debug* v) {
@@ -317,7 +382,7 @@ moe_status moe_decode_relaunch(moe_decode_ctx* ctx, int32_t kernel,
   if (ctx->last_rows == 0) return MOE_ERR_INVALID_ARG;
   Weights wt;
   Dims d;
-  const moe_status st = step_args(ctx, ctx->last_rows, w, &wt, &d);
+  const moe_status st = step_args(ctx->cfg, ctx->plan, ctx->last_rows, w, &wt, &d);
   if (st != MOE_OK) return st;
   const int groups = step_groups(ctx->plan, d);
   for (int i = 0; i < reps; i++) {

@@ -154,6 +154,27 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
 moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
                            const moe_decode_weights* w, uint16_t* out, hipStream_t stream);
 
+/* The decode step without a context or workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same validation, kernels and result
+ * as moe_decode_step with a context created from `cfg`, but the step's
+ * intermediates live in a static device array of the library
+ * (MOE_DECODE_NOALLOC_MAX_WORKSPACE bytes, one per GPU, held until the
+ * process ends).  It calls no hipMalloc, hipFree or other allocating routine;
+ * the first call on a device looks up that array's device address.
+ *  cfg  as for moe_decode_init; its workspace (moe_decode_workspace_size) must
+ *       be at most MOE_DECODE_NOALLOC_MAX_WORKSPACE bytes, else
+ *       MOE_ERR_WORKSPACE (a GLM-scale layer at 8 rows needs about 2.6 MB)
+ *  x, rows, w, out, stream  as for moe_decode_step
+ * Every call on one GPU shares that GPU's array, and the array keeps the
+ * last call's intermediates: two calls that overlap on one GPU (other
+ * streams, other threads) race and may corrupt each other's output.  No
+ * debug view, timing or relaunch is available for these steps. */
+#define MOE_DECODE_NOALLOC_MAX_WORKSPACE ((size_t)8 << 20)
+moe_status moe_decode_step_noalloc(const moe_decode_config* cfg, const uint16_t* x,
+                                   int32_t rows, const moe_decode_weights* w, uint16_t* out,
+                                   hipStream_t stream);
+
 /* Device pointers into the workspace holding the last step's intermediates. */
 typedef struct {
   const float* logits;       /* [max_rows, E]: the fp32 values the top-8 compared */
