@@ -237,15 +237,55 @@ static hipError_t lb_nib_launch(const uint8_t* blocks, const uint16_t* x, uint16
 
 // MFMA form, for 1 to 8 input rows (K a multiple of 256): y[r][n] for every
 // input row r at once.  Block = 4 waves = 4/KS slabs of 16 weight rows x KS
-// parts of K (KS = 4, 2 or 1 dividing the chunks of 256 inputs).  A 4 KB LDS
-// table holds, for each byte value b, the 8 bf16 values (bit i of b ? -1 : +1).
-// Per chunk (two groups, 36 bytes a row) lane l holds its row l%16's 9 dwords
-// and, per 32 inputs, looks up the byte of its row at inputs 8(l/16) .. +8 in
-// the table and runs one 16x16x32 bf16 MFMA against the input rows at the same
-// inputs (the MFMA's columns; those past the rows repeat row 0 and are not
-// stored): the products are +-x exactly.  A group's fp32 sum (4 MFMAs) is
-// scaled by its d (fp16) and accumulated; the block adds its K parts in part
-// order through LDS and stores bf16.
+// parts of K (KS = 4, 2 or 1 dividing the chunks of 256 inputs).  Per chunk
+// (two groups, 36 bytes a row) lane l holds its row l%16's 9 dwords and, per
+// 32 inputs, turns the byte of its row at inputs 8(l/16) .. +8 into 8 bf16
+// values +-1 in registers (bf16 1.0 is 0x3F80; bit i of the byte becomes the
+// sign bit of value i) and runs one 16x16x32 bf16 MFMA against the input rows
+// at the same inputs (the MFMA's columns; those past the rows repeat row 0
+// and are not stored): the products are +-x exactly.  A group's fp32 sum (4
+// MFMAs) is scaled by its d (fp16) and accumulated; the block adds its K
+// parts in part order through LDS and stores bf16.
+
+// Sign bits to bf16 +-1 operands.  bf16 1.0 is 0x3F80; bit i of a sign word
+// becomes the sign bit of value i, values paired per dword (value 2p in the
+// low half, 2p+1 in the high half).  For a pair of bits (i, i+1), i even:
+// R = rotl(w, 15) holds bit i+1 at (i+16) mod 32, so Z = the half of w that
+// holds bit i merged with the other half of R holds bit i at i and bit i+1 at
+// i+16 (mod 32), and rotr(Z, i - 15) puts them at bits 15 and 31; a mask and
+// an or with 1.0 in both halves finish the pair.  The three constants come in
+// registers (kernel arguments): gfx950's three-operand instructions take no
+// literal, and with constants in sight the compiler folds the rotations into
+// quarter-rate multiplies.
+struct SignK {
+  uint32_t half;  // 0x0000FFFF
+  uint32_t sign;  // 0x80008000
+  uint32_t one;   // 0x3F803F80
+};
+// Z for the pairs whose low bit lies in the low half of w (lo = true) or in
+// the high half.
+__device__ __forceinline__ uint32_t q1_spread(uint32_t w, bool lo, const SignK& k) {
+  const uint32_t r = __builtin_amdgcn_alignbit(w, w, 17);  // rotl(w, 15)
+  return lo ? ((w & k.half) | (r & ~k.half)) : ((w & ~k.half) | (r & k.half));
+}
+// The 8 values of sign bits i0 .. i0+7 (i0 = 8 * byte) from their Z; `one`
+// is k.one held in a vector register (so that the mask and the or are one
+// v_and_or_b32 with the mask as its scalar operand).
+__device__ __forceinline__ v8bf q1_pairs(uint32_t z, uint32_t i0, const SignK& k, uint32_t one) {
+  uint32_t r[4];
+#pragma unroll
+  for (int p = 0; p < 4; p++)
+    r[p] = (__builtin_amdgcn_alignbit(z, z, (i0 + 2 * p - 15) & 31) & k.sign) | one;
+  return __builtin_bit_cast(v8bf, r);
+}
+// A kernel argument copied into a vector register (a DPP move the compiler
+// does not fold back into a scalar).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xE4, 0xF, 0xF, false);
+}
+
+constexpr SignK kSignK = {0x0000FFFFu, 0x80008000u, 0x3F803F80u};
+
 struct QmStage {
   uint32_t w[9];  // the chunk of the lane's row: d0, 16 bit-bytes, d1, 16 bit-bytes
   u32x4 xb[8];    // the lane's input row at inputs 128h + 32s + 8(l/16) .. +8
@@ -254,22 +294,10 @@ struct QmStage {
 template <int P>
 __global__ __launch_bounds__(256) void lowbit_gemv_q1_mfma_kernel(
     const uint8_t* __restrict__ blocks, const uint16_t* __restrict__ x,
-    uint16_t* __restrict__ y, int rows, int n, int k, int ks) {
-  __shared__ __align__(16) uint32_t s_tab[256][4];  // bf16 +-1 pairs for each byte value
+    uint16_t* __restrict__ y, int rows, int n, int k, int ks, SignK sk) {
   __shared__ __align__(16) float s_part[4][256];    // per wave 16 x 16 sums, column-major
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
-  {
-    uint32_t e[4];
-#pragma unroll
-    for (int p = 0; p < 4; p++) {
-      const uint32_t lo = ((tid >> (2 * p)) & 1) ? 0xBF80u : 0x3F80u;
-      const uint32_t hi = ((tid >> (2 * p + 1)) & 1) ? 0xBF80u : 0x3F80u;
-      e[p] = lo | (hi << 16);
-    }
-    *reinterpret_cast<u32x4*>(s_tab[tid]) = u32x4{e[0], e[1], e[2], e[3]};
-  }
-  __syncthreads();
   const int spb = 4 / ks;
   const int slab = blockIdx.x * spb + wv / ks, kp = wv % ks;
   const int nch = k / 256, nc = nch / ks, c0 = kp * nc;
@@ -277,6 +305,7 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_mfma_kernel(
   const int rowc = row < n ? row : n - 1;  // rows past n decode the last row (not stored)
   const uint32_t* wrow = reinterpret_cast<const uint32_t*>(blocks + (size_t)rowc * 36 * nch);
   const uint16_t* pa = x + (size_t)(col < rows ? col : 0) * k + 8 * g;
+  const uint32_t one = in_vgpr(sk.one);
 
   auto issue = [&](QmStage& st, int c) {
 #pragma unroll
@@ -303,8 +332,8 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_mfma_kernel(
       v4f c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s2 = 0; s2 < 4; s2++) {
-        const uint32_t byte = __builtin_amdgcn_ubfe(u[4 * h + s2], 8 * g, 8);
-        const v8bf a = *reinterpret_cast<const v8bf*>(s_tab[byte]);
+        // byte g of sign word s2: bits 8g .. 8g+7 (low half of the word for g < 2)
+        const v8bf a = q1_pairs(q1_spread(u[4 * h + s2], g < 2, sk), 8 * g, sk, one);
         c = mfma_bf16(a, __builtin_bit_cast(v8bf, st.xb[4 * h + s2]), c);
       }
       // lane l holds weight rows 4(l/16) + v; their d is held by lanes 4(l/16) + v
@@ -338,6 +367,212 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_mfma_kernel(
   }
 }
 
+// Wide MFMA form, for 1 to 8 input rows (K a multiple of 256, the input
+// rows within kQ4XBytes) and many weight rows: a wave owns 64 weight rows
+// (four 16-row tiles) over its part of K, so each read of the input rows
+// serves four MFMAs, and lane l loads the 36 contiguous bytes of row l's
+// chunk (two dwordx4 and a dword) instead of every lane loading its tile
+// row's 9 dwords one at a time.  The block first copies the input rows into
+// LDS (row stride padded by 16 bytes, so the 16 columns of a read fall on
+// different banks).  Per chunk the lane re-aligns its chunk (two groups of 16
+// bit-bytes as 8 dwords; d0 | d1 << 16) into the wave's LDS area, and the
+// tiles read back their rows' sign dwords.  The K order inside a 128-group is
+// permuted so that one sign dword serves a lane for four MFMA steps: lane
+// quarter g (l/16) takes sign dword g of the group (bytes 4g .. 4g+3, inputs
+// 32g .. 32g+31), step s its byte s (inputs 32g + 8s .. +8), and reads the
+// input rows at the same inputs.  A group's fp32 sum is scaled by its d (the
+// d of the lane's 4 result rows: one 16-byte LDS read) and accumulated; K
+// parts are added in part order.
+constexpr int kQ4Stride = 10;           // LDS dwords per row of sign words (8 used)
+constexpr int kQ4XBytes = 48 * 1024;    // the largest rows x K x 2 staged in LDS
+
+struct Q4Stage {
+  uint32_t w[9];  // this lane's row, one chunk: d0, 16 bit-bytes, d1, 16 bit-bytes
+};
+
+template <int P>
+__global__ __launch_bounds__(256) void lowbit_gemv_q1_mfma4_kernel(
+    const uint8_t* __restrict__ blocks, const uint16_t* __restrict__ x,
+    uint16_t* __restrict__ y, int rows, int n, int k, int ks, SignK sk) {
+  constexpr int T = 4;
+  extern __shared__ __align__(16) uint8_t q4_dyn[];           // input rows, [rows][k + 8] bf16
+  __shared__ __align__(16) uint32_t s_u[4][64 * kQ4Stride];  // per wave: sign dwords by row
+  __shared__ __align__(16) uint32_t s_d[4][64];               // per wave: d0 | d1 << 16 by row
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int xs = k + 8;  // LDS row stride of the input rows (elements)
+  uint16_t* sx = reinterpret_cast<uint16_t*>(q4_dyn);
+  for (int i = tid; i < rows * (k / 8); i += 256) {
+    const int r = i / (k / 8), e = 8 * (i - r * (k / 8));
+    *reinterpret_cast<u32x4*>(sx + r * xs + e) = ld16(x + (size_t)r * k + e);
+  }
+  const int spb = 4 / ks;
+  const int slab = blockIdx.x * spb + wv / ks, kp = wv % ks;
+  const int nch = k / 256, nc = nch / ks, c0 = kp * nc;
+  const int lrow = slab * 64 + lane;
+  const int rowc = lrow < n ? lrow : n - 1;  // rows past n decode the last row (not stored)
+  const uint32_t* wrow = reinterpret_cast<const uint32_t*>(blocks + (size_t)rowc * 36 * nch);
+  const uint16_t* pa = sx + (col < rows ? col : 0) * xs + 32 * g;
+  const uint32_t one = in_vgpr(sk.one);
+  uint32_t* su = s_u[wv];
+  uint32_t* sd = s_d[wv];
+  __syncthreads();
+
+  auto issue = [&](Q4Stage& st, int c) {
+    const uint32_t* src = wrow + 9 * c;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(src);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(src + 4);
+    st.w[0] = a[0]; st.w[1] = a[1]; st.w[2] = a[2]; st.w[3] = a[3];
+    st.w[4] = b[0]; st.w[5] = b[1]; st.w[6] = b[2]; st.w[7] = b[3];
+    st.w[8] = src[8];
+  };
+  float acc[T][4];
+#pragma unroll
+  for (int t = 0; t < T; t++)
+#pragma unroll
+    for (int v = 0; v < 4; v++) acc[t][v] = 0.f;
+  auto consume = [&](Q4Stage& st, int c) {
+    // this lane's chunk re-aligned into the wave's LDS area
+    uint32_t* dst = su + lane * kQ4Stride;
+#pragma unroll
+    for (int q = 0; q < 4; q += 2) {
+      uint2 p0, p1;
+      p0.x = __builtin_amdgcn_alignbyte(st.w[q + 1], st.w[q], 2);
+      p0.y = __builtin_amdgcn_alignbyte(st.w[q + 2], st.w[q + 1], 2);
+      p1.x = st.w[5 + q];
+      p1.y = st.w[6 + q];
+      *reinterpret_cast<uint2*>(dst + q) = p0;
+      *reinterpret_cast<uint2*>(dst + 4 + q) = p1;
+    }
+    sd[lane] = (st.w[0] & 0xFFFFu) | (st.w[4] & 0xFFFF0000u);
+    asm volatile("" ::: "memory");
+    u32x4 dd[T];
+#pragma unroll
+    for (int t = 0; t < T; t++) dd[t] = *reinterpret_cast<const u32x4*>(sd + 16 * t + 4 * g);
+    // per group: the four tiles' MFMA chains interleaved, their results
+    // read after all of them
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      v4f cv[T];
+      uint32_t z[T][2];  // spread of the sign word's low and high halves
+#pragma unroll
+      for (int t = 0; t < T; t++) {
+        const uint32_t uw = su[(16 * t + col) * kQ4Stride + g + 4 * h];
+        z[t][0] = q1_spread(uw, true, sk);
+        z[t][1] = q1_spread(uw, false, sk);
+        cv[t] = v4f{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 4; s2++) {
+        const v8bf b = *reinterpret_cast<const v8bf*>(pa + c * 256 + 128 * h + 8 * s2);
+#pragma unroll
+        for (int t = 0; t < T; t++) {
+          // byte s2 of the sign word: bits 8 s2 .. 8 s2 + 7
+          cv[t] = mfma_bf16(q1_pairs(z[t][s2 >> 1], 8 * s2, sk, one), b, cv[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < T; t++)
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+          acc[t][v] = fmaf(cv[t][v], lb_f16(h ? (dd[t][v] >> 16) : (dd[t][v] & 0xFFFFu)), acc[t][v]);
+    }
+    asm volatile("" ::: "memory");
+  };
+  // ring of P chunks (P divides the part's chunks: every load is used)
+  Q4Stage st[P];
+#pragma unroll
+  for (int p = 0; p < P; p++) issue(st[p], c0 + p);
+  for (int i0 = 0; i0 < nc - P; i0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+      consume(st[p], c0 + i0 + p);
+      issue(st[p], c0 + i0 + P + p);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; p++) consume(st[p], c0 + nc - P + p);
+#pragma unroll
+  for (int t = 0; t < T; t++) pin4(acc[t]);  // the MFMAs run with every lane, before any divergent use
+
+  // K-part sums per wave and tile, column-major, over the input rows' LDS
+  // once every wave is done with them (rows * (k + 8) * 2 >= 16 KB: k >= 1024)
+  __syncthreads();
+  float(*s_part)[T][256] = reinterpret_cast<float(*)[T][256]>(q4_dyn);
+#pragma unroll
+  for (int t = 0; t < T; t++)
+    *reinterpret_cast<v4f*>(&s_part[wv][t][col * 16 + 4 * g]) =
+        v4f{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
+  __syncthreads();
+  const int cc = tid >> 4, i = tid & 15;  // input row cc, weight row i of each tile
+  if (cc >= rows) return;
+  for (int s2 = 0; s2 < spb; s2++) {
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+      float v = s_part[s2 * ks][t][cc * 16 + i];
+      for (int q = 1; q < ks; q++) v += s_part[s2 * ks + q][t][cc * 16 + i];
+      const int rr = (blockIdx.x * spb + s2) * 64 + 16 * t + i;
+      if (rr < n) y[(size_t)cc * n + rr] = f32_to_bf16(v);
+    }
+  }
+}
+
+// The wide form's launch: K parts the fewest of 1, 2, 4 dividing the chunks
+// that gives at least 4096 waves, else the most that divide; ring depth the
+// largest divisor of a part's chunks up to 8 (a whole part of 8 chunks or
+// fewer is loaded at once).
+template <int P>
+static void lb_mfma4_one(dim3 grid, size_t lds, const uint8_t* blocks, const uint16_t* x,
+                         uint16_t* y, int rows, int n, int k, int ks, hipStream_t stream) {
+  hipLaunchKernelGGL(lowbit_gemv_q1_mfma4_kernel<P>, grid, dim3(256), lds, stream, blocks, x, y,
+                     rows, n, k, ks, kSignK);
+}
+template <int P>
+static hipError_t lb_mfma4_lds(size_t lds) {
+  static size_t raised[kLdsDevices] = {};
+  return ensure_dyn_lds(reinterpret_cast<const void*>(lowbit_gemv_q1_mfma4_kernel<P>), lds, raised);
+}
+static hipError_t lb_mfma4_launch(const uint8_t* blocks, const uint16_t* x, uint16_t* y,
+                                  int rows, int n, int k, hipStream_t stream) {
+  const int nch = k / 256, slabs = (n + 63) / 64;
+  int ks = 1;
+  for (int c : {1, 2, 4}) {
+    if (nch % c) continue;
+    ks = c;
+    if (slabs * c >= 4096) break;
+  }
+  const int nc = nch / ks;
+  int p = 1;
+  for (int d = 8; d >= 1; d--)
+    if (nc % d == 0) {
+      p = d;
+      break;
+    }
+  const int spb = 4 / ks;
+  size_t lds = (size_t)rows * (k + 8) * 2;
+  if (lds < 4 * 4 * 256 * 4) lds = 4 * 4 * 256 * 4;  // the K-part sums reuse it
+  const dim3 grid((slabs + spb - 1) / spb);
+  hipError_t e = hipSuccess;
+  switch (p) {
+#define Q4_CASE(P)                                                          \
+  case P:                                                                   \
+    e = lb_mfma4_lds<P>(lds);                                               \
+    if (e == hipSuccess) lb_mfma4_one<P>(grid, lds, blocks, x, y, rows, n, k, ks, stream); \
+    break;
+    Q4_CASE(8)
+    Q4_CASE(7)
+    Q4_CASE(6)
+    Q4_CASE(5)
+    Q4_CASE(4)
+    Q4_CASE(3)
+    Q4_CASE(2)
+    Q4_CASE(1)
+#undef Q4_CASE
+  }
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
 // The MFMA form's launch: K parts the fewest of 1, 2, 4 dividing the chunks
 // that gives at least 512 blocks, else the most that divide (more parts, more
 // blocks); ring depth 2 where it divides a part's chunks, else 1.
@@ -357,16 +592,24 @@ static hipError_t lb_mfma_launch(const uint8_t* blocks, const uint16_t* x, uint1
   const dim3 grid((slabs + spb - 1) / spb);
   if ((nch / ks) % 2 == 0)
     hipLaunchKernelGGL(lowbit_gemv_q1_mfma_kernel<2>, grid, dim3(256), 0, stream, blocks, x, y,
-                       rows, n, k, ks);
+                       rows, n, k, ks, kSignK);
   else
     hipLaunchKernelGGL(lowbit_gemv_q1_mfma_kernel<1>, grid, dim3(256), 0, stream, blocks, x, y,
-                       rows, n, k, ks);
+                       rows, n, k, ks, kSignK);
   return hipGetLastError();
 }
 
+// Weight rows from which several-row calls take the wide form (64 rows a
+// wave): below it there are too few waves to spread over the CUs.
+constexpr int kQ4MinRows = 32768;
+
 hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int rows,
                             int n, int k, hipStream_t stream) {
-  if (rows > 1) return lb_mfma_launch(blocks, x, y, rows, n, k, stream);  // K % 256 == 0
+  if (rows > 1) {  // K % 256 == 0
+    if (n >= kQ4MinRows && (size_t)rows * (k + 8) * 2 <= kQ4XBytes)
+      return lb_mfma4_launch(blocks, x, y, rows, n, k, stream);
+    return lb_mfma_launch(blocks, x, y, rows, n, k, stream);
+  }
   // the nibble-table form: rows per block RB the largest of 128, 64, 32 that
   // gives 2048 blocks, else the largest that gives 256, else 16; chunks per
   // thread and round M the fewest (up to 5) that take all of K in one round,
