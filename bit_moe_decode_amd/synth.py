@@ -11,6 +11,7 @@ Canonical layouts (all row-major, stacked experts expert-major):
   FP8 matrix [N, K]:   codes uint8 [N, K], scales float32 [N/128, K/128]
   MXFP4 matrix [N, K]: codes uint8 [N, K/2] (element 2i in the low nibble),
                        scales uint8 E8M0 [N, K/32]
+  Q1 routed matrix [N, K]: blocks uint8 [N, K/128, 18] (as below), no scales
   Q1 matrix [N, K]:    uint8 [N, K/128, 18] = fp16 d (little-endian) + 16 bytes
                        of sign bits, bit i of byte b is element 8b+i, 1 = minus
 
@@ -22,7 +23,9 @@ synthetic stand-ins for real weights, which are not available):
          of intermediate 2048, router ~ N(0, 0.01)
   x ~ N(0, 1); RMSNorm gamma ~ U(0.8, 1.2); eps 1e-6; expert weights drawn
   from N(0, 1) and encoded per block (FP8: scale amax/448 per 128x128;
-  MXFP4: E8M0 exponent floor(log2 amax) - 2 per 32 along K).
+  MXFP4: E8M0 exponent floor(log2 amax) - 2 per 32 along K).  Routed experts
+  may instead be 1-bit (Q1_0_G128): bits Bernoulli(0.5) and group scales
+  |N(0, 0.02)| in fp16, as the 1-bit GEMV's workload.
 """
 from dataclasses import dataclass, field
 from typing import Optional
@@ -36,6 +39,8 @@ SHAPES = {
 
 FMT_FP8 = 1
 FMT_MXFP4 = 2
+FMT_Q1 = 3
+Q1_D_STD = 0.02  # 1-bit group scales |N(0, 0.02)| (the 1-Bit Turbo workload's)
 
 _E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 
@@ -99,9 +104,11 @@ class ExpertWeights:
     down: tuple
 
     def expert(self, e: int):
-        """Expert e's (gate codes, gate scales, up codes, up scales, down codes, down scales)."""
-        return (self.gate[0][e], self.gate[1][e], self.up[0][e], self.up[1][e],
-                self.down[0][e], self.down[1][e])
+        """Expert e's (gate codes, gate scales, up codes, up scales, down codes,
+        down scales); the scales are None for 1-bit matrices."""
+        sc = lambda m: None if m[1] is None else m[1][e]
+        return (self.gate[0][e], sc(self.gate), self.up[0][e], sc(self.up),
+                self.down[0][e], sc(self.down))
 
 
 @dataclass
@@ -127,14 +134,36 @@ def _encode(fmt, w):
     return encode_fp8_blocks(w) if fmt == FMT_FP8 else encode_mxfp4(w)
 
 
+def q1_blocks(bits: torch.Tensor, d16: torch.Tensor) -> torch.Tensor:
+    """Q1 blocks uint8 [n, groups, 18] from sign bytes uint8 [n, groups, 16]
+    and fp16 scales [n, groups] (d little-endian, then the sign bytes)."""
+    n, groups = d16.shape
+    blk = torch.empty(n, groups, 18, dtype=torch.uint8, device=bits.device)
+    dv = d16.view(torch.int16).to(torch.int32) & 0xFFFF
+    blk[..., 0] = (dv & 0xFF).to(torch.uint8)
+    blk[..., 1] = (dv >> 8).to(torch.uint8)
+    blk[..., 2:] = bits.to(torch.uint8)
+    return blk.contiguous()
+
+
+def _q1_matrix(n, k, gen, device):
+    groups = k // 128
+    d = (torch.randn(n, groups, generator=gen, device=device) * Q1_D_STD).abs().to(torch.float16)
+    bits = torch.randint(0, 256, (n, groups, 16), generator=gen, device=device, dtype=torch.int32)
+    return q1_blocks(bits, d)
+
+
 def _stack(fmt, n_exp, n, k, gen, device):
     codes, scales = [], []
     for _ in range(n_exp):
+        if fmt == FMT_Q1:
+            codes.append(_q1_matrix(n, k, gen, device))
+            continue
         w = torch.randn(n, k, generator=gen, device=device, dtype=torch.float32)
         c, s = _encode(fmt, w)
         codes.append(c)
         scales.append(s)
-    return torch.stack(codes), torch.stack(scales)
+    return torch.stack(codes), (torch.stack(scales) if scales else None)
 
 
 def make_layer(shape="tiny", routed_fmt: int = FMT_FP8, seed: int = 1000,
@@ -176,13 +205,4 @@ def make_x(rows: int, hidden: int, seed: int, mode: str = "indep", device="cpu")
 def make_q1(n: int, k: int, seed: int, device="cpu") -> torch.Tensor:
     """1-bit group-128 matrix: uint8 [n, k/128, 18]; bits Bernoulli(0.5),
     group scale |N(0, 0.02)| stored as fp16 (little-endian)."""
-    gen = _gen(seed, device)
-    groups = k // 128
-    d = (torch.randn(n, groups, generator=gen, device=device) * 0.02).abs().to(torch.float16)
-    bits = torch.randint(0, 256, (n, groups, 16), generator=gen, device=device, dtype=torch.int32)
-    blk = torch.empty(n, groups, 18, dtype=torch.uint8, device=device)
-    dv = d.view(torch.int16).to(torch.int32) & 0xFFFF
-    blk[..., 0] = (dv & 0xFF).to(torch.uint8)
-    blk[..., 1] = (dv >> 8).to(torch.uint8)
-    blk[..., 2:] = bits.to(torch.uint8)
-    return blk.contiguous()
+    return _q1_matrix(n, k, _gen(seed, device), device)

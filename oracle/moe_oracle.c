@@ -240,41 +240,58 @@ void orc_quant_blocks(const float* v, int n, uint8_t* q, float* s) {
 }
 
 /* y[n] = sum_k W[n,k] * h[k] for one stored matrix, W decoded element by
- * element: FP8 code * fp32 block scale (per 128x128), or E2M1 * 2^(E8M0-127)
- * (per 32 along K, low nibble = even element).  Two optional outputs size
+ * element: FP8 code * fp32 block scale (per 128x128), E2M1 * 2^(E8M0-127)
+ * (per 32 along K, low nibble = even element), or +-d for 1-bit group-128
+ * weights (1-Bit Turbo, Q1_0_G128).  Two optional outputs size
  * rounding bounds and take no part in y: yabs[n] = sum_k |W[n,k] h[k]|, and
  * ygmax[n] = the sum, over the groups of 8 consecutive k (k = 8i .. 8i+7), of
  * the largest |W[n,k] h[k]| in the group. */
 static void orc_gemv(int fmt, const orc_mat* w, int n_out, int k_in, const double* h, double* y,
                      double* yabs, double* ygmax, int nthreads) {
   const uint8_t* codes = w->codes;
-#pragma omp parallel for num_threads(nthreads) schedule(static)
-  for (int n = 0; n < n_out; n++) {
-    double acc = 0.0, aabs = 0.0, gsum = 0.0, gmax = 0.0;
-    for (int k = 0; k < k_in; k++) {
-      double wv;
+#pragma omp parallel num_threads(nthreads)
+  {
+    double* wrow = (double*)malloc(sizeof(double) * k_in); /* row n of W, decoded */
+#pragma omp for schedule(static)
+    for (int n = 0; n < n_out; n++) {
       if (fmt == ORC_FMT_FP8) {
         const float* sc = (const float*)w->scales;
-        wv = lut_e4m3[codes[(size_t)n * k_in + k]] *
-             (double)sc[(size_t)(n / 128) * (k_in / 128) + k / 128];
-      } else {
+        for (int k = 0; k < k_in; k++)
+          wrow[k] = lut_e4m3[codes[(size_t)n * k_in + k]] *
+                    (double)sc[(size_t)(n / 128) * (k_in / 128) + k / 128];
+      } else if (fmt == ORC_FMT_MXFP4) {
         const uint8_t* sc = (const uint8_t*)w->scales;
-        uint8_t byte = codes[(size_t)n * (k_in / 2) + k / 2];
-        uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 15);
-        wv = lut_e2m1[nib] * lut_e8m0[sc[(size_t)n * (k_in / 32) + k / 32]];
+        for (int k = 0; k < k_in; k++) {
+          uint8_t byte = codes[(size_t)n * (k_in / 2) + k / 2];
+          uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 15);
+          wrow[k] = lut_e2m1[nib] * lut_e8m0[sc[(size_t)n * (k_in / 32) + k / 32]];
+        }
+      } else {
+        /* Q1_0_G128: an 18-byte block per 128 along K, fp16 d then 16 bytes
+         * of sign bits, bit k%8 of byte (k%128)/8; 1 means -d */
+        for (int k = 0; k < k_in; k++) {
+          const uint8_t* blk = codes + ((size_t)n * (k_in / 128) + k / 128) * 18;
+          const double d = orc_dec_fp16((uint16_t)(blk[0] | (blk[1] << 8)));
+          const int bit = (blk[2 + (k % 128) / 8] >> (k % 8)) & 1;
+          wrow[k] = bit ? -d : d;
+        }
       }
-      const double t = wv * h[k];
-      acc += t;
-      aabs += fabs(t);
-      if (fabs(t) > gmax) gmax = fabs(t);
-      if (k % 8 == 7 || k == k_in - 1) {
-        gsum += gmax;
-        gmax = 0.0;
+      double acc = 0.0, aabs = 0.0, gsum = 0.0, gmax = 0.0;
+      for (int k = 0; k < k_in; k++) {
+        const double t = wrow[k] * h[k];
+        acc += t;
+        aabs += fabs(t);
+        if (fabs(t) > gmax) gmax = fabs(t);
+        if (k % 8 == 7 || k == k_in - 1) {
+          gsum += gmax;
+          gmax = 0.0;
+        }
       }
+      y[n] = acc;
+      if (yabs) yabs[n] = aabs;
+      if (ygmax) ygmax[n] = gsum;
     }
-    y[n] = acc;
-    if (yabs) yabs[n] = aabs;
-    if (ygmax) ygmax[n] = gsum;
+    free(wrow);
   }
 }
 
@@ -283,7 +300,10 @@ static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 /* One expert applied to one row: up/gate, SiLU*gate, mid re-quantised to FP8
  * per 1x128 block for FP8 experts, then down (#85 Mod. rows 1, 16).
  * READING: mid = silu(gate) * up; MXFP4 experts keep mid unquantised (#85 Mod.
- * row 1: "MXFP4 experts keep their path", which read mid as f32). */
+ * row 1: the MXFP4 experts' path is left as it was, and it read mid as f32).
+ * READING: 1-bit (Q1_0_G128) routed experts re-quantise mid to FP8 per 1x128
+ * block like FP8 experts: the rule stated for the step in general, with no
+ * exception on the pages for 1-bit weights. */
 static void orc_expert(int fmt, const orc_mat* wg, const orc_mat* wu, const orc_mat* wd, int h_dim,
                        int i_dim, const double* hin, int nthreads, double* mid_out,
                        uint8_t* midq_out, float* midqs_out, double* y, double* gate,
@@ -293,7 +313,7 @@ static void orc_expert(int fmt, const orc_mat* wg, const orc_mat* wu, const orc_
   orc_gemv(fmt, wg, i_dim, h_dim, hin, gate, gate_abs, gate_gmax, nthreads);
   orc_gemv(fmt, wu, i_dim, h_dim, hin, upv, up_abs, up_gmax, nthreads);
   for (int n = 0; n < i_dim; n++) mid_out[n] = orc_silu(gate[n]) * upv[n];
-  if (fmt == ORC_FMT_FP8) {
+  if (fmt == ORC_FMT_FP8 || fmt == ORC_FMT_Q1) {
     float* mf = (float*)malloc(sizeof(float) * i_dim);
     for (int n = 0; n < i_dim; n++) mf[n] = (float)mid_out[n];
     orc_quant_blocks(mf, i_dim, midq_out, midqs_out);
@@ -312,25 +332,26 @@ static void orc_expert(int fmt, const orc_mat* wg, const orc_mat* wu, const orc_
  * device's down outputs calls it on that device's own mid, so that the down
  * GEMV is judged apart from the up/gate before it:
  *   y_n = sum_k W[n,k] * mhat_k,
- * mhat_k = dec(midq[k]) * midqs[k/128] for FP8 experts, and mhat_k = mid32[k]
- * (the fp32 value itself) for MXFP4 experts, whose mid is not re-quantised.
+ * mhat_k = dec(midq[k]) * midqs[k/128] for FP8 and 1-bit experts, and
+ * mhat_k = mid32[k] (the fp32 value itself) for MXFP4 experts, whose mid is
+ * not re-quantised.  W's scales are unused for 1-bit experts (in the blocks).
  * y_abs_n = sum_k |W[n,k] * mhat_k| and y_gmax (the per-group maxima of
  * orc_gemv) size rounding bounds.  W is [h_dim,
  * i_dim] in the expert's format; every sum runs in double in index order. */
 int orc_expert_down(int fmt, const orc_mat* wd, int h_dim, int i_dim, const uint8_t* midq,
                     const float* midqs, const float* mid32, int nthreads, double* y,
                     double* y_abs, double* y_gmax) {
-  if (h_dim <= 0 || i_dim <= 0 || i_dim % 128 || !wd || !wd->codes || !wd->scales || !y)
-    return ORC_ERR;
-  if (fmt == ORC_FMT_FP8 && (!midq || !midqs)) return ORC_ERR;
+  if (h_dim <= 0 || i_dim <= 0 || i_dim % 128 || !wd || !wd->codes || !y) return ORC_ERR;
+  if ((fmt == ORC_FMT_FP8 || fmt == ORC_FMT_Q1) && (!midq || !midqs)) return ORC_ERR;
   if (fmt == ORC_FMT_MXFP4 && !mid32) return ORC_ERR;
-  if (fmt != ORC_FMT_FP8 && fmt != ORC_FMT_MXFP4) return ORC_ERR;
+  if (fmt != ORC_FMT_FP8 && fmt != ORC_FMT_MXFP4 && fmt != ORC_FMT_Q1) return ORC_ERR;
   if (fmt == ORC_FMT_FP8 && h_dim % 128) return ORC_ERR;
+  if (fmt != ORC_FMT_Q1 && !wd->scales) return ORC_ERR; /* 1-bit: the scales are in the blocks */
   if (nthreads < 1) nthreads = 1;
   orc_init_luts();
   double* mhat = (double*)malloc(sizeof(double) * i_dim);
   for (int k = 0; k < i_dim; k++)
-    mhat[k] = fmt == ORC_FMT_FP8 ? lut_e4m3[midq[k]] * (double)midqs[k / 128] : (double)mid32[k];
+    mhat[k] = fmt == ORC_FMT_MXFP4 ? (double)mid32[k] : lut_e4m3[midq[k]] * (double)midqs[k / 128];
   orc_gemv(fmt, wd, h_dim, i_dim, mhat, y, y_abs, y_gmax, nthreads);
   free(mhat);
   return ORC_OK;
@@ -404,7 +425,9 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
   const int nt = cfg->nthreads > 0 ? cfg->nthreads : 1;
   const int Imax = Is > I ? Is : I;
   if (R < 1 || R > 8 || H % 128 || I % 128 || Is % 128 || E < 8 || Is < 0) return ORC_ERR;
-  if (cfg->routed_fmt != ORC_FMT_FP8 && cfg->routed_fmt != ORC_FMT_MXFP4) return ORC_ERR;
+  if (cfg->routed_fmt != ORC_FMT_FP8 && cfg->routed_fmt != ORC_FMT_MXFP4 &&
+      cfg->routed_fmt != ORC_FMT_Q1)
+    return ORC_ERR;
   if (cfg->act_fmt != ORC_ACT_FP8 && cfg->act_fmt != ORC_ACT_BF16) return ORC_ERR;
   if (Is > 0 && (!sh_gate || !sh_up || !sh_down)) return ORC_ERR;
   orc_init_luts();
@@ -479,7 +502,8 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
         fmt = ORC_FMT_FP8;
         idim = Is;
       }
-      if (!wg->codes || !wu->codes || !wd->codes || !wg->scales || !wu->scales || !wd->scales) {
+      if (!wg->codes || !wu->codes || !wd->codes ||
+          (fmt != ORC_FMT_Q1 && (!wg->scales || !wu->scales || !wd->scales))) {
         rc = ORC_ERR;
         break;
       }

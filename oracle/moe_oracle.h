@@ -34,6 +34,7 @@ extern "C" {
 
 #define ORC_FMT_FP8 1   /* E4M3FN codes, one fp32 scale per 128x128 block  */
 #define ORC_FMT_MXFP4 2 /* E2M1 codes, 2 per byte (low nibble first), E8M0 per 32 along K */
+#define ORC_FMT_Q1 3    /* 1-bit group-128: [N][K/128] blocks of 18 bytes, fp16 d + 16 sign bytes */
 /* Expert inputs: FP8 E4M3 per 1x128 block of u (#85 Mod. row 10, the default),
  * or u itself (bf16) -- an option for comparing what the FP8 blocks cost. */
 #define ORC_ACT_FP8 0
@@ -62,14 +63,14 @@ int orc_router(int rows, int hidden, int n_experts, float eps, const uint16_t* x
 
 /* One weight matrix [N, K] in a low-bit format. */
 typedef struct {
-  const uint8_t* codes; /* FP8: [N][K];  MXFP4: [N][K/2] */
-  const void* scales;   /* FP8: float [N/128][K/128];  MXFP4: uint8 E8M0 [N][K/32] */
+  const uint8_t* codes; /* FP8: [N][K];  MXFP4: [N][K/2];  Q1: [N][K/128][18] */
+  const void* scales;   /* FP8: float [N/128][K/128];  MXFP4: uint8 E8M0 [N][K/32];  Q1: unused */
 } orc_mat;
 
 typedef struct {
   int32_t hidden, inter, n_experts, shared_inter, rows;
   float rms_eps;
-  int32_t routed_fmt; /* ORC_FMT_FP8 or ORC_FMT_MXFP4; the shared expert is always FP8 */
+  int32_t routed_fmt; /* ORC_FMT_FP8, ORC_FMT_MXFP4 or ORC_FMT_Q1; the shared expert is FP8 */
   int32_t nthreads;
   int32_t act_fmt;    /* ORC_ACT_FP8 or ORC_ACT_BF16 */
 } orc_cfg;
@@ -104,8 +105,8 @@ int orc_moe_step(const orc_cfg* cfg, const uint16_t* x, const uint16_t* gamma,
                  const orc_mat* sh_down, const float* anchor_z, uint16_t* out,
                  orc_debug* dbg);
 
-/* The down GEMV of one expert on a given mid: FP8 experts take midq codes
- * [i_dim] with midqs scales [i_dim/128]; MXFP4 experts take mid32 [i_dim]. */
+/* The down GEMV of one expert on a given mid: FP8 and 1-bit experts take midq
+ * codes [i_dim] with midqs scales [i_dim/128]; MXFP4 experts take mid32. */
 int orc_expert_down(int fmt, const orc_mat* wd, int h_dim, int i_dim, const uint8_t* midq,
                     const float* midqs, const float* mid32, int nthreads, double* y,
                     double* y_abs, double* y_gmax);

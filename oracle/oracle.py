@@ -18,6 +18,7 @@ _LIB = None
 
 FMT_FP8 = 1
 FMT_MXFP4 = 2
+FMT_Q1 = 3  # 1-bit group-128 routed experts: [N, K/128, 18] blocks, no separate scales
 ACT_FP8, ACT_BF16 = 0, 1  # the experts' input: FP8 blocks of u (default) or u itself
 
 
@@ -187,7 +188,8 @@ def moe_step(cfg, x, gamma, router_w, experts, shared=None, anchor_z=None, nthre
          (act_fmt ACT_FP8, the default, or ACT_BF16: u itself as the experts' input)
     x: uint16 [R, H] bf16 codes; gamma: uint16 [H]; router_w: uint16 [E, H]
     experts: dict expert_id -> (gate_codes, gate_scales, up_codes, up_scales,
-             down_codes, down_scales); only experts that are picked are needed.
+             down_codes, down_scales); only experts that are picked are needed
+             (1-bit experts: the blocks as codes, scales None).
     shared: the same 6-tuple for the shared expert (FP8) or None.
     anchor_z: float32 [R, E] logits that decide the selection, or None.
     Returns (out uint16 [R, H], debug dict of numpy arrays).
@@ -201,8 +203,11 @@ def moe_step(cfg, x, gamma, router_w, experts, shared=None, anchor_z=None, nthre
 
     def mat(codes, scales):
         codes = np.ascontiguousarray(codes)
+        keep.append(codes)
+        if scales is None:
+            return OrcMat(codes.ctypes.data, None)
         scales = np.ascontiguousarray(scales)
-        keep.extend([codes, scales])
+        keep.append(scales)
         return OrcMat(codes.ctypes.data, scales.ctypes.data)
 
     G = (OrcMat * E)()
@@ -312,19 +317,23 @@ def expert_down(fmt, codes, scales, midq=None, midqs=None, mid32=None, nthreads=
     [i] and midqs float32 [i/128] (the mid's FP8 codes and block scales).
     fmt FMT_MXFP4: codes uint8 [h, i/2], scales uint8 E8M0 [h, i/32], mid32
     float32 [i] (mid itself, not re-quantised).
+    fmt FMT_Q1: codes uint8 [h, i/128, 18] blocks, scales None, midq/midqs as
+    for FP8.
     Returns (y float64 [h], y_abs float64 [h], y_gmax float64 [h]) with y_abs =
     sum_k |W[n,k] mhat_k| and y_gmax = the sum over groups of 8 consecutive k of
     the largest |W[n,k] mhat_k| of the group."""
     c = np.ascontiguousarray(codes, dtype=np.uint8)
     h = c.shape[0]
-    i = c.shape[1] if fmt == FMT_FP8 else 2 * c.shape[1]
-    sc = np.ascontiguousarray(scales, dtype=np.float32 if fmt == FMT_FP8 else np.uint8)
+    i = {FMT_FP8: lambda: c.shape[1], FMT_MXFP4: lambda: 2 * c.shape[1],
+         FMT_Q1: lambda: 128 * c.shape[1]}[fmt]()
+    sc = None if fmt == FMT_Q1 else np.ascontiguousarray(
+        scales, dtype=np.float32 if fmt == FMT_FP8 else np.uint8)
     q = None if midq is None else np.ascontiguousarray(midq, dtype=np.uint8).ravel()
     qs = None if midqs is None else np.ascontiguousarray(midqs, dtype=np.float32).ravel()
     m32 = None if mid32 is None else np.ascontiguousarray(mid32, dtype=np.float32).ravel()
     for a, n in ((q, i), (qs, i // 128), (m32, i)):
         assert a is None or a.size == n
-    m = OrcMat(c.ctypes.data, sc.ctypes.data)
+    m = OrcMat(c.ctypes.data, None if sc is None else sc.ctypes.data)
     y = np.zeros(h, np.float64)
     ya = np.zeros(h, np.float64)
     yg = np.zeros(h, np.float64)

@@ -14,7 +14,7 @@ def np_u16(t):
 
 
 def expert_host(layer, e):
-    return tuple(t.cpu().numpy() for t in layer.routed.expert(int(e)))
+    return tuple(None if t is None else t.cpu().numpy() for t in layer.routed.expert(int(e)))
 
 
 def shared_host(layer):

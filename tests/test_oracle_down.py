@@ -139,3 +139,18 @@ def test_rejects_missing_inputs():
         O.expert_down(O.FMT_FP8, codes, np.ones((1, 1), F32))
     with pytest.raises(ValueError):
         O.expert_down(O.FMT_MXFP4, codes[:, :64], np.zeros((128, 4), np.uint8))
+
+
+def test_q1_down_closed_form():
+    """1-bit down: signs + except row block 1 (all -), group scale d[h/128][g],
+    mid codes all 1.0 with block scales t: y_h = +-128 sum_g d[h/128][g] t[g]."""
+    from tests.test_oracle_layer import _q1_const
+    D = np.array([[1 / 16, 3 / 64], [5 / 32, 1 / 128]])
+    t = np.array([0.5, -0.25], F32)
+    blk = np.concatenate([_q1_const(128, 256, D[:1]), _q1_const(128, 256, D[1:], minus=True)])
+    midq = np.full(256, 0x38, np.uint8)
+    y, ya, yg = O.expert_down(O.FMT_Q1, blk, None, midq=midq, midqs=t)
+    expect = np.concatenate([np.full(128, 128 * (D[0] @ t)), np.full(128, -128 * (D[1] @ t))])
+    assert np.array_equal(y, expect)
+    assert np.array_equal(ya, np.concatenate([np.full(128, 128 * (np.abs(D[0]) @ np.abs(t))),
+                                              np.full(128, 128 * (np.abs(D[1]) @ np.abs(t)))]))

@@ -260,7 +260,8 @@ def _np_step(layer, x, routed_fmt, act_fmt=0):
 def _run_oracle(layer, x, act_fmt=0, **kw):
     import bit_moe_decode_amd.synth as S
     xb = S.bf16_bits(x).numpy().view(np.uint16)
-    experts = {e: tuple(t.numpy() for t in layer.routed.expert(e)) for e in range(layer.n_experts)}
+    experts = {e: tuple(None if t is None else t.numpy() for t in layer.routed.expert(e))
+               for e in range(layer.n_experts)}
     shared = tuple(t.numpy() for t in layer.shared.expert(0)) if layer.shared is not None else None
     cfg = dict(hidden=layer.hidden, inter=layer.inter, n_experts=layer.n_experts,
                shared_inter=layer.shared_inter, rows=x.shape[0], rms_eps=layer.rms_eps,
@@ -426,3 +427,96 @@ def test_q1_block_size_matches_the_pages():
         facts = json.load(f)["q1_size"]
     bpw = facts["file_mb"] * 1e6 * 8 / (facts["params_b"] * 1e9)
     assert abs(bpw - 18 * 8 / 128) < 0.03
+
+
+# ------------------------------------------- 1-bit (Q1_0_G128) routed experts
+def _q1_const(n, k, d_blocks, minus=False):
+    """Q1 matrix [n, k] with every sign + (or every sign -) and group scale
+    d_blocks[n // 128][g] (fp16-exact values)."""
+    groups = k // 128
+    d = np.repeat(np.asarray(d_blocks, np.float64), 128, axis=0)[:n, :groups].astype(np.float16)
+    assert np.array_equal(d.astype(np.float64), np.repeat(np.asarray(d_blocks), 128, axis=0)[:n])
+    blk = np.zeros((n, groups, 18), np.uint8)
+    dv = d.view(np.uint16)
+    blk[..., 0] = dv & 0xFF
+    blk[..., 1] = dv >> 8
+    blk[..., 2:] = 0xFF if minus else 0
+    return blk
+
+
+def test_hand_worked_layer_q1():
+    """1-bit routed experts whose signs are all + and whose group scales d are
+    the FP8 hand-worked layer's block scales: each matrix equals that layer's
+    (every FP8 code there is 1.0), so the step reproduces its closed form --
+    mid re-quantised to FP8 per 1x128 block as for FP8 experts.  Flipping
+    every sign bit of one expert's down matrix negates its output."""
+    x, gamma, w = _hand_inputs()
+    a, b, c, _, _, _ = _hand_scales()
+    _, shared = _hand_layer_fp8()
+    experts = {e: (_q1_const(I, H, a[e]), None, _q1_const(I, H, b[e]), None,
+                   _q1_const(H, I, c[e]), None) for e in range(E)}
+    cfg = dict(hidden=H, inter=I, n_experts=E, shared_inter=IS, rows=1, rms_eps=1e-6,
+               routed_fmt=O.FMT_Q1)
+    out, d = O.moe_step(cfg, x, gamma, w, experts, shared)
+    cf = _closed_form_fp8()
+    assert list(d["ids"][0]) == cf["ids"]
+    for j in range(8):
+        mid, sm, y = cf["ys"][j]
+        assert np.allclose(d["mid"][0, j, :I], np.repeat(mid, 128), rtol=1e-13, atol=0)
+        assert np.array_equal(d["midqs"][0, j, :2], sm.astype(F32))
+        assert np.allclose(d["y"][0, j], np.repeat(y, 128), rtol=1e-13, atol=0)
+    assert np.allclose(d["out_f64"][0], cf["out"], rtol=1e-13, atol=0)
+    e0 = cf["ids"][0]
+    flipped = dict(experts)
+    flipped[e0] = experts[e0][:4] + (_q1_const(H, I, c[e0], minus=True), None)
+    _, d2 = O.moe_step(cfg, x, gamma, w, flipped, shared)
+    assert np.array_equal(d2["y"][0, 0], -d["y"][0, 0])
+    assert np.array_equal(d2["y"][0, 1:], d["y"][0, 1:])
+
+
+def _np_q1(blocks):
+    """Independent decode of Q1 blocks [n, g, 18]: d * (1 - 2 bit)."""
+    n, groups, _ = blocks.shape
+    d = blocks[..., :2].copy().view(np.float16)[..., 0].astype(np.float64)
+    bits = np.unpackbits(blocks[..., 2:], axis=-1, bitorder="little").astype(np.float64)
+    return (d[..., None] * (1.0 - 2.0 * bits)).reshape(n, groups * 128)
+
+
+def test_oracle_q1_layer_matches_independent_numpy_pipeline():
+    import bit_moe_decode_amd.synth as S
+    shape = dict(hidden=256, inter=256, n_experts=32, shared_inter=256, router_std=0.02)
+    layer = S.make_layer(shape, routed_fmt=S.FMT_Q1, seed=1020)
+    x = S.make_x(3, 256, seed=2020)
+    out, d = _run_oracle(layer, x)
+    xv = x.double().numpy()
+    gam = layer.gamma.double().numpy()
+    wr = layer.router_w.double().numpy()
+    for r in range(3):
+        rstd = 1 / np.sqrt((xv[r] ** 2).sum() / 256 + float(F32(1e-6)))
+        u = torch.from_numpy(xv[r] * gam).to(torch.float32).to(torch.bfloat16).double().numpy()
+        z = rstd * (wr @ u)
+        ids = np.lexsort((np.arange(z.size), -z))[:8]
+        assert list(ids) == list(d["ids"][r])
+        g = np.exp(z[ids] - z[ids].max())
+        g /= g.sum()
+        ub = u.reshape(-1, 128)
+        s = (np.abs(ub).max(axis=1).astype(F32) / F32(448)).astype(F32)
+        q = torch.from_numpy((ub.astype(F32) / s[:, None]).astype(F32)).to(torch.float8_e4m3fn)
+        h = (q.double().numpy() * s[:, None]).ravel() * rstd
+
+        def ffn(m, q1):
+            if q1:
+                Wg, Wu, Wd = _np_q1(m[0]), _np_q1(m[2]), _np_q1(m[4])
+            else:
+                Wg, Wu, Wd = _np_fp8(m[0], m[1]), _np_fp8(m[2], m[3]), _np_fp8(m[4], m[5])
+            gt, up = Wg @ h, Wu @ h
+            mid = (gt / (1 + np.exp(-gt)) * up).astype(F32).reshape(-1, 128)
+            sm = (np.abs(mid).max(axis=1) / F32(448)).astype(F32)
+            mq = torch.from_numpy((mid / sm[:, None]).astype(F32)).to(torch.float8_e4m3fn)
+            return Wd @ (mq.double().numpy() * sm[:, None]).ravel()
+
+        ref = sum(g[j] * ffn([None if t is None else t.numpy()
+                              for t in layer.routed.expert(int(e))], True)
+                  for j, e in enumerate(ids))
+        ref = ref + ffn([t.numpy() for t in layer.shared.expert(0)], False)
+        assert np.allclose(d["out_f64"][r], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
