@@ -215,7 +215,7 @@ def make_weights(gamma, router_w, routed, shared=None) -> Weights:
     w.rms_gamma = gamma.data_ptr()
     w.router_w = router_w.data_ptr()
     for name, (c, s) in zip(("gate", "up", "down"), routed):
-        setattr(w, name, Tensor(c.data_ptr(), s.data_ptr()))
+        setattr(w, name, Tensor(c.data_ptr(), None if s is None else s.data_ptr()))
     if shared is not None:
         for name, (c, s) in zip(("sh_gate", "sh_up", "sh_down"), shared):
             setattr(w, name, Tensor(c.data_ptr(), s.data_ptr()))

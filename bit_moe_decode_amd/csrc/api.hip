@@ -66,7 +66,14 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   if (c->shared_inter != 0 && c->shared_inter != c->inter) return MOE_ERR_UNSUPPORTED;
   if (!is_mult(c->n_experts, 16) || c->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
   if (c->max_rows < 1 || c->max_rows > 8) return MOE_ERR_INVALID_ARG;
-  if (c->routed_fmt != MOE_FMT_FP8_E4M3_B128 && c->routed_fmt != MOE_FMT_MXFP4)
+  if (c->routed_fmt != MOE_FMT_FP8_E4M3_B128 && c->routed_fmt != MOE_FMT_MXFP4 &&
+      c->routed_fmt != MOE_FMT_Q1_G128)
+    return MOE_ERR_UNSUPPORTED;
+  // 1-bit routed experts: up/gate items of 4 groups (hidden % 512), down rows
+  // of whole 36-byte chunks loaded at once (inter % 256, at most 4096), FP8
+  // activations (their MFMA is FP8 x FP8)
+  if (c->routed_fmt == MOE_FMT_Q1_G128 &&
+      (c->hidden % 512 || c->inter % 256 || c->inter > 4096 || c->act_fmt != MOE_ACT_FP8_B128))
     return MOE_ERR_UNSUPPORTED;
   // MXFP4 up/gate items are two K blocks wide; the down GEMV keeps its
   // columns' mid split into bf16 hi + lo in LDS (4 bytes an element, up to 8
@@ -203,10 +210,14 @@ namespace {
 moe_status step_args(const moe_decode_config& cfg, const Plan& p, int rows,
                      const moe_decode_weights* w, Weights* wtp, Dims* dp) {
   if (!w) return MOE_ERR_INVALID_ARG;
-  const void* need[] = {w->rms_gamma, w->router_w, w->gate.codes, w->gate.scales, w->up.codes,
-                        w->up.scales, w->down.codes, w->down.scales};
+  const void* need[] = {w->rms_gamma, w->router_w, w->gate.codes, w->up.codes, w->down.codes};
   for (const void* q : need)
     if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (cfg.routed_fmt != MOE_FMT_Q1_G128) {  // 1-bit blocks hold their own scales
+    const void* sc[] = {w->gate.scales, w->up.scales, w->down.scales};
+    for (const void* q : sc)
+      if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  }
   if (p.Is > 0) {
     const void* sh[] = {w->sh_gate.codes, w->sh_gate.scales, w->sh_up.codes,
                         w->sh_up.scales, w->sh_down.codes, w->sh_down.scales};
@@ -241,6 +252,10 @@ moe_status step_args(const moe_decode_config& cfg, const Plan& p, int rows,
   d.no_dedup = (cfg.flags & MOE_F_NO_DEDUP) ? 1 : 0;
   d.eps = cfg.rms_eps;
   d.act_bf16 = cfg.act_fmt == MOE_ACT_BF16 ? 1 : 0;
+  d.q1k[0] = 0x0000FFFFu;  // 1-bit operand constants (see q1_fp8_operand)
+  d.q1k[1] = 0x00800080u;
+  d.q1k[2] = 0x80008000u;
+  d.q1k[3] = 0x38383838u;
   return MOE_OK;
 }
 

@@ -37,7 +37,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kMaxRows = 8;
 
-enum : int { kFmtFp8 = 1, kFmtMxfp4 = 2 };
+enum : int { kFmtFp8 = 1, kFmtMxfp4 = 2, kFmtQ1 = 3 };
 
 // Everything a step keeps in the caller's workspace (device pointers).
 struct Ws {
@@ -71,6 +71,9 @@ struct Dims {
   int no_dedup;        // 1: one group per (row, pick)
   int act_bf16;        // 1: the experts take u (bf16), not FP8 activation blocks
   float eps;
+  // 1-bit expert operand constants (0x0000FFFF, 0x00800080, 0x80008000,
+  // 0x38383838), passed in so that they sit in registers: see q1_fp8_operand
+  uint32_t q1k[4];
 };
 
 struct Weights {
@@ -244,6 +247,60 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(uint2 c) {
 
 __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- 1-bit (Q1_0_G128) weights as FP8 MFMA operands.
+// A group of 128 weights is an fp16 d and 16 sign bytes; weight k of the
+// group is -d when bit k%8 of byte k/8 is set, else +d.  Two groups (36
+// bytes) make a dword-aligned chunk.  The FP8 MFMA takes the weights as E4M3
+// +-1 (0x38 / 0xB8) and the group's sum is scaled by d afterwards.
+//
+// Lane l's A operand of a 16x16x128 MFMA is 32 weights of its row, 4 to a
+// dword: the 32 sign bits w of sign dword l/16 of the group.  Dword j (weights
+// 4j .. 4j+3) needs bit 4j+i at bit 8i+7 over 0x38 in every byte.  With
+// R = rotl(w, 14) holding bit i+2 at i+16 (mod 32), Z = the half of w that
+// holds bits 4j .. 4j+3 merged with the other half of R holds bit i at i and
+// bit i+2 at i+16, so rotr(Z, 4j-7) puts bits 4j and 4j+2 at 7 and 23 and
+// rotr(Z, 4j-14) puts bits 4j+1 and 4j+3 at 15 and 31.  The masks and 1.0
+// come in registers (Dims::q1k: gfx950's three-operand instructions take no
+// literal, and with the constants in sight the compiler folds the rotations
+// into quarter-rate multiplies); `one` is q1k[3] in a vector register.
+__device__ __forceinline__ uint32_t q1_in_vgpr(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xE4, 0xF, 0xF, false);
+}
+__device__ __forceinline__ v8i q1_fp8_operand(uint32_t w, const uint32_t* k, uint32_t one) {
+  const uint32_t r = __builtin_amdgcn_alignbit(w, w, 18);  // rotl(w, 14)
+  const uint32_t zl = (w & k[0]) | (r & ~k[0]);              // bits 0..15 and their +2 partners
+  const uint32_t zh = (w & ~k[0]) | (r & k[0]);              // bits 16..31
+  v8i a;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const uint32_t z = j < 4 ? zl : zh;
+    const uint32_t t = (__builtin_amdgcn_alignbit(z, z, (4 * j - 7) & 31) & k[1]) | one;
+    a[j] = (int)((__builtin_amdgcn_alignbit(z, z, (4 * j - 14) & 31) & k[2]) | t);
+  }
+  return a;
+}
+
+// One 36-byte chunk (9 dwords, as loaded) re-aligned: the 16 sign bytes of
+// each group as 4 dwords (u[0..3] group 0, which starts 2 bytes in, u[4..7]
+// group 1), and both groups' fp16 d as one dword (d0 | d1 << 16).
+__device__ __forceinline__ void q1_chunk_split(const uint32_t* w, uint32_t* u, uint32_t* dd) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    u[q] = __builtin_amdgcn_alignbyte(w[q + 1], w[q], 2);
+    u[4 + q] = w[5 + q];
+  }
+  *dd = (w[0] & 0xFFFFu) | (w[4] & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ float q1_d(uint32_t dd, int h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(h ? (dd >> 16) : (dd & 0xFFFFu)));
+}
+
+// Nontemporal 4-byte load for weights read once per step.
+__device__ __forceinline__ uint32_t ld_nt4(const uint32_t* p) {
+  return __builtin_nontemporal_load(p);
 }
 
 }  // namespace moe

@@ -238,6 +238,70 @@ __device__ __forceinline__ void dn4_split_mid(const Ws& ws, const Dims& d, int n
   }
 }
 
+// The 1-bit down GEMV of one wave: output rows h0 .. h0 + 16 of routed expert
+// e over the whole K (I <= 4096: up to 4 items of 4 chunks), against the
+// block's FP8 mid codes in LDS (pm: the lane's column at inputs 32(l/16) ..,
+// psm: that column's block scales).  Item i = chunks 4i .. 4i+3 of every row:
+// lane l loads chunk 4i + l%4 of row h0 + l/4 (9 dwords, nontemporal; lanes
+// past the row's chunks load chunk 0 and do not use it), all items at once,
+// before the block quantises mid.  Per item the chunks are re-aligned into the
+// wave's LDS tile; per group the lane reads sign dword l/16 of its MFMA row
+// l%16, builds E4M3 +-1 operands and runs one FP8 MFMA against the mid codes;
+// each row's sum is scaled by its group d and the mid block scale.
+struct DnQ1Items {
+  uint32_t w[4][9];
+};
+__device__ __forceinline__ void down_q1_issue(const Weights& w, const Dims& d, int e, int h0,
+                                              DnQ1Items& it) {
+  const int lane = threadIdx.x & 63, I = d.I;
+  const size_t rb = (size_t)18 * (I / 128);
+  const int nchunk = I / 256;
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(
+      w.down_c + ((size_t)e * d.H + h0 + (lane >> 2)) * rb);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    if (4 * i < nchunk) {  // wave-uniform
+      const int c = 4 * i + (lane & 3);
+      const uint32_t* p = row + 9 * (c < nchunk ? c : 0);
+#pragma unroll
+      for (int q = 0; q < 9; q++) it.w[i][q] = ld_nt4(p + q);
+    }
+  }
+}
+__device__ __forceinline__ void down_q1_consume(const Dims& d, const DnQ1Items& it,
+                                                uint32_t* lds, const uint8_t* pm,
+                                                const float* psm, float* acc) {
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+  const int lrow = lane >> 2, lq = lane & 3;
+  const int nchunk = d.I / 256;
+  const uint32_t one = q1_in_vgpr(d.q1k[3]);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    if (4 * i >= nchunk) break;  // wave-uniform
+    uint32_t u[8], dd;
+    q1_chunk_split(it.w[i], u, &dd);
+#pragma unroll
+    for (int q = 0; q < 8; q++) lds[(lq * 8 + q) * 16 + lrow] = u[q];
+    lds[512 + lq * 16 + lrow] = dd;
+    asm volatile("" ::: "memory");
+    const int nc = nchunk - 4 * i < 4 ? nchunk - 4 * i : 4;
+    for (int q = 0; q < nc; q++) {
+      const u32x4 dv = *reinterpret_cast<const u32x4*>(lds + 512 + q * 16 + 4 * g);
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int kb = 2 * (4 * i + q) + h;  // group = mid block
+        const uint32_t ws = lds[(q * 8 + 4 * h + g) * 16 + col];
+        const v4f c = mfma_fp8(q1_fp8_operand(ws, d.q1k, one),
+                               cat8(ld16(pm + kb * 128), ld16(pm + kb * 128 + 16)));
+        const float sm = psm[kb];
+#pragma unroll
+        for (int v = 0; v < 4; v++) acc[v] = fmaf(c[v], q1_d(dv[v], h) * sm, acc[v]);
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+}
+
 template <int RF, int P, int WPB, int T4>
 __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Dims d) {
   __shared__ __align__(16) uint8_t s_tile[WPB][kTileBytes];
@@ -293,6 +357,26 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
         *reinterpret_cast<v4f*>(ws.ypart + (size_t)cols.u(col) * H + h0 + 16 * t +
                                 4 * (lane >> 4)) = v4f{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
     }
+    return;
+  }
+  if (RF == kFmtQ1 && g >= 0) {
+    // 1-bit routed expert: all its weight items in flight while the block
+    // quantises mid into LDS, then one 16-row tile a wave
+    const int h0 = (b * WPB + wv) * 16;
+    DnQ1Items it;
+    down_q1_issue(w, d, e, h0, it);
+    uint8_t* s_q = dyn;
+    float* s_qs = reinterpret_cast<float*>(dyn + (size_t)d.rows * dn_code_stride(I));
+    dn_quant_mid(ws, d, nrows, cols, b == 0, s_q, s_qs);
+    __syncthreads();
+    const int cq = col < nrows ? col : 0;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    down_q1_consume(d, it, reinterpret_cast<uint32_t*>(s_tile[wv]),
+                    s_q + cq * dn_code_stride(I) + (lane >> 4) * 32, s_qs + cq * nkb, acc);
+    pin4(acc);  // the MFMAs run with every lane, before the divergent store
+    if (col < nrows)
+      *reinterpret_cast<v4f*>(ws.ypart + (size_t)cols.u(col) * H + h0 + 4 * (lane >> 4)) =
+          v4f{acc[0], acc[1], acc[2], acc[3]};
     return;
   }
   const int cc = col < nrows ? col : 0;  // columns past the rows reuse column 0
@@ -434,7 +518,9 @@ constexpr int kDn4TwoTileRows = 6;
 template <int RF, int P>
 static hipError_t launch_wpb(int max_groups, size_t lds, const Weights& w, const Ws& ws,
                              const Dims& d, hipStream_t stream) {
-  if constexpr (RF == kFmtFp8)
+  if constexpr (RF == kFmtQ1)  // 1-bit routed experts: one 16-row tile a wave
+    return launch_one<RF, P, 4, 1>(max_groups, lds, w, ws, d, stream);
+  else if constexpr (RF == kFmtFp8)
     return d.rows <= 2 ? launch_one<RF, P, 2, 1>(max_groups, lds, w, ws, d, stream)
                        : launch_one<RF, P, 4, 2>(max_groups, lds, w, ws, d, stream);
   else
@@ -460,6 +546,7 @@ hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws,
   if (rfmt == kFmtMxfp4 && dn4_lds_bytes(d.rows, d.I) > lds) lds = dn4_lds_bytes(d.rows, d.I);
   if (rfmt == kFmtFp8) return launch_rf<kFmtFp8>(max_groups, lds, w, ws, d, stream);
   if (rfmt == kFmtMxfp4) return launch_rf<kFmtMxfp4>(max_groups, lds, w, ws, d, stream);
+  if (rfmt == kFmtQ1) return launch_rf<kFmtQ1>(max_groups, lds, w, ws, d, stream);
   return hipErrorInvalidValue;
 }
 

@@ -294,6 +294,92 @@ __device__ __forceinline__ void ug_fp4(const Weights& w, const Ws& ws, const Dim
   for (int p = 0; p < P; p++) consume(st[p]);
 }
 
+// 1-bit weights (Q1_0_G128): groups kb0 .. kb0 + nk of the slab (nk a
+// multiple of 4, kb0 even).  An item is 4 groups = 2 chunks of 36 bytes per
+// row: lane l loads chunk l%2 of row (l%32)/2 of gate (l < 32) or up, 9
+// dwords, row-contiguous and nontemporal, and re-aligns it into the wave's
+// LDS area (sign dwords and d by chunk, dword and row); then per group the
+// lane reads the sign dword l/16 of its MFMA row l%16 for gate and up, builds
+// E4M3 +-1 operands from it and runs one FP8 MFMA per matrix against the
+// using rows' activation codes; each row's sum is scaled by its group d and
+// the activation block scale and accumulated.
+struct UgStageQ1 {
+  uint32_t w[9];  // the lane's chunk
+  u32x4 a[4][2];  // activation codes of the item's 4 groups (operand order)
+  float sa[4];
+};
+template <int P>
+__device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims& d, UgJob j,
+                                      int kb0, int nk, uint32_t* lds, int lane, float* accg,
+                                      float* accu) {
+  const int H = d.H, nkbh = H / 128;
+  const size_t rb = (size_t)18 * nkbh;  // bytes per row
+  const size_t ebytes = (size_t)d.I * rb;
+  const int m = lane >> 5, lrow = (lane & 31) >> 1, lq = lane & 1;
+  const int col = lane & 15, g = lane >> 4;
+  const uint8_t* base = (m ? w.up_c : w.gate_c) + (size_t)j.e * ebytes;
+  const uint32_t* src =
+      reinterpret_cast<const uint32_t*>(base + (size_t)(j.n0 + lrow) * rb) + 9 * (kb0 / 2 + lq);
+  const uint8_t* pa = ws.act_q + (size_t)j.row * H + (lane >> 4) * 32 + (size_t)kb0 * 128;
+  const float* psa = ws.act_s + (size_t)j.row * nkbh + kb0;
+  const uint32_t one = q1_in_vgpr(d.q1k[3]);
+
+  auto issue = [&](UgStageQ1& st, int it) {
+    const uint32_t* p = src + 18 * it;
+#pragma unroll
+    for (int i = 0; i < 9; i++) st.w[i] = ld_nt4(p + i);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const size_t o = (size_t)(4 * it + q) * 128;
+      st.a[q][0] = ld16(pa + o);
+      st.a[q][1] = ld16(pa + o + 16);
+      st.sa[q] = psa[4 * it + q];
+    }
+  };
+  auto consume = [&](UgStageQ1& st) {
+    uint32_t u[8], dd;
+    q1_chunk_split(st.w, u, &dd);
+    const int area = (m * 2 + lq);
+#pragma unroll
+    for (int i = 0; i < 8; i++) lds[(area * 8 + i) * 16 + lrow] = u[i];
+    lds[512 + area * 16 + lrow] = dd;
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const u32x4 dg = *reinterpret_cast<const u32x4*>(lds + 512 + (0 * 2 + q) * 16 + 4 * g);
+      const u32x4 du = *reinterpret_cast<const u32x4*>(lds + 512 + (1 * 2 + q) * 16 + 4 * g);
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int gi = 2 * q + h;  // group of the item
+        const uint32_t wg = lds[((0 * 2 + q) * 8 + 4 * h + g) * 16 + col];
+        const uint32_t wu = lds[((1 * 2 + q) * 8 + 4 * h + g) * 16 + col];
+        const v8i bv = cat8(st.a[gi][0], st.a[gi][1]);
+        const v4f cg = mfma_fp8(q1_fp8_operand(wg, d.q1k, one), bv);
+        const v4f cu = mfma_fp8(q1_fp8_operand(wu, d.q1k, one), bv);
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          accg[v] = fmaf(cg[v], q1_d(dg[v], h) * st.sa[gi], accg[v]);
+          accu[v] = fmaf(cu[v], q1_d(du[v], h) * st.sa[gi], accu[v]);
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+  };
+  const int ni = nk / 4;
+  UgStageQ1 st[P];
+#pragma unroll
+  for (int p = 0; p < P; p++) issue(st[p], p);
+  for (int k0 = 0; k0 < ni - P; k0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+      consume(st[p]);
+      issue(st[p], k0 + P + p);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; p++) consume(st[p]);
+}
+
 typedef uint8_t UgTiles[4][2][kTileBytes];  // per wave: gate and up weight tiles
 
 // Up/gate block number `blk` of the numbering above (the shared expert's
@@ -338,6 +424,10 @@ __device__ __forceinline__ void upgate_block(const Weights& w, const Ws& ws, con
   } else if (RF == kFmtMxfp4 && e >= 0) {
     const int ni = d.H / 256 / KS;  // items of two K blocks per part
     ug_fp4<P4>(w, ws, d, j, kp * ni, ni, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
+  } else if (RF == kFmtQ1 && e >= 0) {
+    const int nk = d.H / 128 / KS;  // groups per part, a multiple of 4
+    ug_q1<P4>(w, ws, d, j, kp * nk, nk, reinterpret_cast<uint32_t*>(s_tile[wv][0]), lane, accg,
+              accu);
   } else {
     const int nk = d.H / 128 / KS;
     ug_fp8<P>(w, ws, d, j, kp * nk, nk, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
@@ -414,7 +504,10 @@ static int ring_depth4(int ni) { return ni % 3 == 0 ? 3 : (ni % 2 == 0 ? 2 : 1);
 // K parts of the up/gate slabs: the largest of 4, 2, 1 dividing H/128, or
 // H/256 when routed experts are MXFP4 (their items are two K blocks).
 int upgate_k_parts(int hidden, int routed_fmt) {
-  const int n = routed_fmt == kFmtMxfp4 ? hidden / 256 : hidden / 128;
+  // parts hold whole items: K blocks (FP8), pairs of them (MXFP4), or 4-group
+  // items (1-bit experts: hidden a multiple of 512)
+  const int n = routed_fmt == kFmtMxfp4 ? hidden / 256
+                                          : (routed_fmt == kFmtQ1 ? hidden / 512 : hidden / 128);
   return n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1);
 }
 
@@ -460,6 +553,14 @@ hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& w
       case 4: launch_p4<kFmtMxfp4, 4>(p4, grid, base, w, ws, d, stream); break;
       case 2: launch_p4<kFmtMxfp4, 2>(p4, grid, base, w, ws, d, stream); break;
       default: launch_p4<kFmtMxfp4, 1>(p4, grid, base, w, ws, d, stream); break;
+    }
+  } else if (rfmt == kFmtQ1) {
+    // 1-bit items (4 groups) in flight: the largest of 3, 2, 1 dividing a part's items
+    const int pq = ring_depth4(d.H / 512 / d.ks);
+    switch (p) {
+      case 4: launch_p4<kFmtQ1, 4>(pq, grid, base, w, ws, d, stream); break;
+      case 2: launch_p4<kFmtQ1, 2>(pq, grid, base, w, ws, d, stream); break;
+      default: launch_p4<kFmtQ1, 1>(pq, grid, base, w, ws, d, stream); break;
     }
   } else {
     return hipErrorInvalidValue;

@@ -69,7 +69,10 @@ typedef enum {
   /* 1-bit group-128: [N, K/128] blocks of 18 bytes, an fp16 scale d
    * (little-endian) then 16 bytes of sign bits; bit i of byte b is element
    * 8b+i; bit 1 means -d, bit 0 means +d (1-Bit Turbo, Q1_0_G128).
-   * lowbit_gemv only. */
+   * lowbit_gemv, and routed experts of the decode step: their scales
+   * pointers are unused (may be NULL), their mid is re-quantised to FP8 per
+   * 1x128 block as for FP8 experts; needs hidden % 512 == 0, inter % 256 ==
+   * 0, inter <= 4096 and FP8 activations. */
   MOE_FMT_Q1_G128 = 3,
   /* bf16 weights [N, K], no scales.  lowbit_gemv only (the tail's LM head
    * kept in bf16). */
@@ -104,7 +107,7 @@ typedef struct {
   int32_t shared_inter; /* I of the shared expert: 0 for none, else equal to inter */
   int32_t max_rows;     /* 1..8: the widest step this context will run */
   float rms_eps;        /* RMSNorm epsilon */
-  int32_t routed_fmt;   /* MOE_FMT_FP8_E4M3_B128 or MOE_FMT_MXFP4 */
+  int32_t routed_fmt;   /* MOE_FMT_FP8_E4M3_B128, MOE_FMT_MXFP4 or MOE_FMT_Q1_G128 */
   int32_t shared_fmt;   /* MOE_FMT_FP8_E4M3_B128 */
   uint32_t flags;       /* MOE_F_* */
   int32_t act_fmt;      /* moe_afmt: MOE_ACT_FP8_B128 (0) or MOE_ACT_BF16 */

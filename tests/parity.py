@@ -128,14 +128,14 @@ def down_bound(fmt, inter):
     """(a, b): the device's down GEMV on its own mid is within a * y_gmax +
     b * y_abs of the exact sum (y_abs = sum_k |W[n,k] mhat_k|, y_gmax = the
     sum over groups of 8 consecutive k of the largest such term), from its
-    arithmetic.  FP8: per 128-wide K block one scaled FP8 MFMA (the model
-    above), the weight-scale x mid-scale product rounded once, and inter/128
-    fused multiply-adds into the fp32 accumulator: (inter/128 + 4) * 2^-24
-    more.  MXFP4: the weights converted to bf16 exactly (an E2M1 value times a
+    arithmetic.  FP8 (and 1-bit, whose weights enter as E4M3 +-1): per
+    128-wide K block one scaled FP8 MFMA (the model above), the weight-scale
+    (or group d) x mid-scale product rounded once, and inter/128 fused
+    multiply-adds into the fp32 accumulator: (inter/128 + 4) * 2^-24 more.  MXFP4: the weights converted to bf16 exactly (an E2M1 value times a
     power of two), mid split into bf16 hi + lo (|mid - hi - lo| <= 2^-18
     |mid|), and 2 * inter exact fp32 products summed through the bf16 MFMA
     chain, bounded as a sequential fp32 sum with truncation."""
-    if fmt == O.FMT_FP8:
+    if fmt in (O.FMT_FP8, O.FMT_Q1):  # 1-bit: +-1 E4M3 weights, then d x mid scale
         return MFMA8_GROUP, MFMA8_SUMS + (inter // 128 + 4) * U32
     return 0.0, 2 * inter * 2.0 ** -23 + 2.0 ** -17
 
@@ -182,7 +182,8 @@ def compare(layer, x, gpu, out_gpu, ref_out, ref, check_mid_codes=True):
         else:
             g = slot - 1
             users = [(r, int(t["slot"][g][r])) for r in range(R) if t["slot"][g][r] != 0xFF]
-            width, fp8 = layer.inter, layer.routed_fmt == O.FMT_FP8
+            # 1-bit experts' mid is FP8 like FP8 experts'
+            width, fp8 = layer.inter, layer.routed_fmt in (O.FMT_FP8, O.FMT_Q1)
         for r, j in users:
             mg = gpu["mid"][r, j, :width].astype(np.float64)
             mo = ref["mid"][r, j, :width]
@@ -253,7 +254,7 @@ def compare(layer, x, gpu, out_gpu, ref_out, ref, check_mid_codes=True):
                 mats = host[int(t["expert"][g])]
             ba, bb = down_bound(fmt, width)
             for r, j in users:
-                if fmt == O.FMT_FP8:
+                if fmt in (O.FMT_FP8, O.FMT_Q1):
                     yref, yabs, ygm = O.expert_down(fmt, mats[4], mats[5],
                                                     midq=gpu["midq"][r, j, :width],
                                                     midqs=gpu["midqs"][r, j, :width // 128],

@@ -27,6 +27,11 @@ def cfg(**kw):
     return B.Config(*base.values())
 
 
+def test_one_bit_routed_experts_are_supported():
+    assert B.workspace_size(cfg(routed_fmt=B.FMT_Q1)) == B.workspace_size(cfg())
+    assert B.workspace_size(cfg(routed_fmt=B.FMT_Q1, hidden=512, inter=256, shared_inter=0)) > 0
+
+
 def test_workspace_size_supported_shapes():
     n8 = B.workspace_size(cfg())
     n1 = B.workspace_size(cfg(max_rows=1))
@@ -40,7 +45,12 @@ def test_workspace_size_supported_shapes():
 
 @pytest.mark.parametrize("kw", [dict(top_k=4), dict(hidden=6100), dict(inter=100),
                                 dict(n_experts=24), dict(n_experts=2048), dict(shared_inter=64),
-                                dict(routed_fmt=B.FMT_Q1), dict(shared_fmt=B.FMT_MXFP4),
+                                dict(routed_fmt=B.FMT_BF16), dict(shared_fmt=B.FMT_MXFP4),
+                                dict(routed_fmt=B.FMT_Q1, act_fmt=B.ACT_BF16),
+                                dict(routed_fmt=B.FMT_Q1, hidden=6400),
+                                dict(routed_fmt=B.FMT_Q1, inter=4352, shared_inter=4352),
+                                dict(routed_fmt=B.FMT_Q1, inter=384, shared_inter=384),
+                                dict(shared_fmt=B.FMT_Q1),
                                 dict(routed_fmt=B.FMT_MXFP4, inter=4224, shared_inter=4224),
                                 dict(flags=1 << 7), dict(hidden=32768), dict(max_rows=9),
                                 dict(max_rows=0), dict(act_fmt=2), dict(act_fmt=-1),
