@@ -66,8 +66,12 @@ def mxfp4_matrix_bytes(n, k):
     return n * k // 2 + n * (k // 32)
 
 
+def q1_matrix_bytes(n, k):
+    return n * (k // 128) * 18
+
+
 def routed_matrix_bytes(layer, n, k):
-    return mxfp4_matrix_bytes(n, k) if layer.routed_fmt == 2 else fp8_matrix_bytes(n, k)
+    return {2: mxfp4_matrix_bytes, 3: q1_matrix_bytes}.get(layer.routed_fmt, fp8_matrix_bytes)(n, k)
 
 
 def step_bytes(layer, rows, d):
@@ -93,9 +97,11 @@ def layer_copies(S, base, n):
         copies.append(S.Layer(base.shape, base.hidden, base.inter, base.n_experts,
                               base.shared_inter, base.rms_eps, base.gamma.clone(),
                               base.router_w.clone(),
-                              S.ExpertWeights(base.routed.fmt, *[tuple(t.clone() for t in m) for m in
-                                                                 (base.routed.gate, base.routed.up,
-                                                                  base.routed.down)]),
+                              S.ExpertWeights(base.routed.fmt, *[tuple(None if t is None else
+                                                                       t.clone() for t in m)
+                                                                 for m in (base.routed.gate,
+                                                                           base.routed.up,
+                                                                           base.routed.down)]),
                               S.ExpertWeights(base.shared.fmt, *[tuple(t.clone() for t in m) for m in
                                                                  (base.shared.gate, base.shared.up,
                                                                   base.shared.down)])))
@@ -260,7 +266,10 @@ def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base, mode="
     gbytes = sum(step_bytes(layer, rows, dvals[i % POOL]) for i in range(GSTEPS)) / GSTEPS
     graph = dict(us_per_step=graph_ms * 1e3, gbs=gbytes / (graph_ms * 1e-3) / 1e9,
                  distinct_experts=gd)
+    # the protocol's steps cycle the same pool and copies, so the same mean D
+    gbs_proto = nbytes / (proto_ms * 1e-3) / 1e9
     return dict(rows=rows, us_per_step=ms * 1e3, gbs=gbs, frac=gbs / PEAK_GBS, d_mean=d_mean,
+                gbs_protocol=gbs_proto, frac_protocol=gbs_proto / PEAK_GBS,
                 graph=graph, us_per_step_protocol=proto_ms * 1e3, alone_us=alone,
                 upgate_alone_bytes=ug_alone_bytes,
                 bytes_per_step=nbytes,
@@ -270,9 +279,14 @@ def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base, mode="
 
 
 def row_summary(r):
-    """The figures of one time_rows result that go into the JSON line."""
-    return {"us_per_step": round(r["us_per_step"], 2), "gbs": round(r["gbs"], 1),
-            "frac_of_peak": round(r["frac"], 4), "distinct_experts": r["d_mean"],
+    """The figures of one time_rows result that go into the JSON line: µs per
+    step and GB/s by the pages' protocol (mean of 2 rounds of the median of 7
+    trials of 50 steps), and of the plain back-to-back run."""
+    return {"us_per_step": round(r["us_per_step_protocol"], 2),
+            "gbs": round(r["gbs_protocol"], 1), "frac_of_peak": round(r["frac_protocol"], 4),
+            "us_per_step_backtoback": round(r["us_per_step"], 2),
+            "gbs_backtoback": round(r["gbs"], 1),
+            "distinct_experts": r["d_mean"],
             "bytes_per_step": int(r["bytes_per_step"]),
             "kernel_us": {k: round(t, 2) for k, t in r["kernel_us"].items()},
             "kernel_alone_us": {k: round(t, 2) for k, t in r["alone_us"].items()},
@@ -405,53 +419,93 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(torch, layer, res, seconds):
-    from oracle import oracle as O
+def oracle_threads():
+    """Host threads for the oracle: every core this process may run on, but
+    no more than OMP_NUM_THREADS when that is set (the GPU machine sets it to its
+    CPU share per GPU)."""
+    aff = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    return (min(aff, int(omp)) if omp and omp.isdigit() and int(omp) > 0 else aff), aff
+
+
+def oracle_steps(torch, layer, runner, pool, weights, rows, seconds, max_steps, threads, cache):
+    """The oracle (fp64, `threads` OpenMP threads) on full steps of the pool,
+    anchored on the GPU's logits, until `seconds` of oracle time or
+    `max_steps`; each step is also checked against the GPU's output."""
     from tests import parity as P
-    cores = min(16, len(os.sched_getaffinity(0)))
-    runner, pool = res["runner"], res["pool"]
-    cache = {}
     done, t_used, nbytes, errs = 0, 0.0, 0.0, []
-    out = torch.empty(1, layer.hidden, dtype=torch.bfloat16, device="cuda")
-    while done < 64 * POOL and (done == 0 or t_used < seconds):
-        x = pool[done % POOL]
-        runner.ctx.step(x, 1, res["weights"][0], out)
+    out = torch.empty(rows, layer.hidden, dtype=torch.bfloat16, device="cuda")
+    while done < max_steps and (done == 0 or t_used < seconds):
+        x = pool[done % len(pool)]
+        runner.ctx.step(x, rows, weights, out)
         torch.cuda.synchronize()
-        gpu = runner.debug(1)
-        ids = sorted(set(int(e) for e in gpu["ids"].ravel()))
-        for e in ids:
+        gpu = runner.debug(rows)
+        for e in sorted(set(int(e) for e in gpu["ids"].ravel())):
             if e not in cache:
                 cache[e] = P.expert_host(layer, e)
         xc = x.cpu()
         t = time.perf_counter()
-        ref_out, ref = P.oracle_for(layer, xc, gpu["logits"], nthreads=cores, host_cache=cache)
+        ref_out, ref = P.oracle_for(layer, xc, gpu["logits"], nthreads=threads, host_cache=cache)
         t_used += time.perf_counter() - t
-        nbytes += step_bytes(layer, 1, gpu["n_groups"])
-        rep = P.compare(layer, xc, gpu, out, ref_out, ref)
-        errs.append(rep["out_err_rel_max"])
+        nbytes += step_bytes(layer, rows, gpu["n_groups"])
+        errs.append(P.compare(layer, xc, gpu, out, ref_out, ref)["out_err_rel_max"])
         done += 1
-    gbs = nbytes / t_used / 1e9
-    # the same oracle on one thread, over the first few pool entries
-    t1, n1, b1 = 0.0, 0, 0.0
-    while n1 < 4:
-        x = pool[n1 % POOL]
-        runner.ctx.step(x, 1, res["weights"][0], out)
-        torch.cuda.synchronize()
-        gpu = runner.debug(1)
-        xc = x.cpu()
-        t = time.perf_counter()
-        P.oracle_for(layer, xc, gpu["logits"], nthreads=1, host_cache=cache)
-        t1 += time.perf_counter() - t
-        b1 += step_bytes(layer, 1, gpu["n_groups"])
-        n1 += 1
-    single = dict(value=b1 / t1 / 1e9, unit="GB/s", cores=1, ms_per_step=t1 / n1 * 1e3,
-                  sample=f"{n1} full 1-row steps")
-    return dict(value=gbs, unit="GB/s", cores=cores, kind="oracle", cpu_model=cpu_model(),
-                single_thread=single,
-                sample=f"{done} full 1-row GLM-scale steps (router, 8 routed + shared expert, "
-                       f"combine; the {POOL} token rows of the timed pool, cycled) in "
-                       f"{t_used:.1f} s; fp64, {cores} OpenMP threads",
-                ms_per_step=t_used / done * 1e3), max(errs)
+    return dict(ms_per_step=round(t_used / done * 1e3, 2), gbs=round(nbytes / t_used / 1e9, 3),
+                steps=done, out_err_rel_max=max(errs))
+
+
+def oracle_lowbit(S, n, k, threads):
+    """The oracle's 1-bit GEMV at one [n, k] shape, one row."""
+    from oracle import oracle as O
+    blk = S.make_q1(n, k, seed=77).numpy()
+    xb = S.bf16_bits(S.make_x(1, k, seed=78)[0]).numpy().view("uint16")
+    t = time.perf_counter()
+    O.lowbit_gemv_q1(blk, xb, n, k, nthreads=threads)
+    dt = time.perf_counter() - t
+    return dict(ms=round(dt * 1e3, 2), gbs=round(lowbit_bytes(n, k) / dt / 1e9, 3))
+
+
+def cpu_baseline(torch, B, S, layer, results, seconds):
+    """The oracle timed on the host: the headline figure on 1-row GLM-scale
+    steps (about `seconds` of oracle time), then bounded samples at 4 and 8
+    rows, on the tiny layer at 1/4/8 rows and the 1-bit GEMV shapes, plus 4
+    one-row steps on a single thread."""
+    threads, aff = oracle_threads()
+    cache = {}
+    m = results[1]
+    main = oracle_steps(torch, layer, m["runner"], m["pool"], m["weights"][0], 1, seconds,
+                        64 * POOL, threads, cache)
+    per = {"glm_fp8_rows1": main}
+    for rows, secs in ((4, 3.0), (8, 4.0)):
+        if rows in results:
+            r = results[rows]
+            per[f"glm_fp8_rows{rows}"] = oracle_steps(torch, layer, r["runner"], r["pool"],
+                                                     r["weights"][0], rows, secs, 4, threads,
+                                                     cache)
+            log(f"oracle glm rows={rows}: {per[f'glm_fp8_rows{rows}']}")
+    cache.clear()
+    tiny = S.make_layer("tiny", seed=1000, device="cuda")
+    for rows in (1, 4, 8):
+        runner = B.LayerRunner(tiny, rows)
+        pool = [S.make_x(rows, tiny.hidden, seed=7500 + 10 * rows + t).cuda() for t in range(4)]
+        o = oracle_steps(torch, tiny, runner, pool, runner.weights, rows, 0.5, 40, threads, {})
+        per[f"tiny_rows{rows}"] = dict(us_per_step=round(o["ms_per_step"] * 1e3, 1),
+                                       steps=o["steps"], out_err_rel_max=o["out_err_rel_max"])
+    for name, n, k in LOWBIT_SHAPES:
+        per[f"lowbit_{name}"] = oracle_lowbit(S, n, k, threads)
+        log(f"oracle lowbit {name}: {per[f'lowbit_{name}']}")
+    single = oracle_steps(torch, layer, m["runner"], m["pool"], m["weights"][0], 1, 1e9, 4, 1,
+                          cache)
+    return dict(value=main["gbs"], unit="GB/s", cores=threads, kind="oracle",
+                cpu_model=cpu_model(), affinity_cores=aff,
+                omp_num_threads=os.environ.get("OMP_NUM_THREADS"),
+                single_thread=dict(value=single["gbs"], unit="GB/s", cores=1,
+                                   ms_per_step=single["ms_per_step"],
+                                   sample=f"{single['steps']} full 1-row steps"),
+                sample=f"{main['steps']} full 1-row GLM-scale steps (router, 8 routed + shared "
+                       f"expert, combine; the {POOL} token rows of the timed pool, cycled), fp64, "
+                       f"{threads} OpenMP threads",
+                ms_per_step=main["ms_per_step"], per_config=per), main["out_err_rel_max"]
 
 
 def main():
@@ -467,6 +521,8 @@ def main():
     ap.add_argument("--no-mxfp4", action="store_true")
     ap.add_argument("--no-corr", action="store_true")
     ap.add_argument("--no-tp-share", action="store_true")
+    ap.add_argument("--no-tiny", action="store_true")
+    ap.add_argument("--no-q1", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the decode step has no multi-GPU path in this "
@@ -503,12 +559,27 @@ def main():
     for rows in results:
         hot[str(rows)] = round(time_hot(torch, B, S, base, rows, args.steps, 7000 + 100 * rows), 2)
         log(f"hot (one weight copy) rows={rows}: {hot[str(rows)]} us/step")
+    tiny = None
+    if not args.no_tiny:
+        # the tiny layer (hidden 256, 32 experts of 128, no shared expert):
+        # 0.8-3.2 MB a step, cache-resident and latency-bound, so µs only
+        tiny = {}
+        tl = S.make_layer("tiny", seed=1000, device="cuda")
+        for rows in (1, 4, 8):
+            r = time_rows(torch, B, S, tl, [tl], rows, args.steps, args.warmup,
+                          seed_base=7000 + 10 * rows)
+            tiny[str(rows)] = {"us_per_step": round(r["us_per_step_protocol"], 2),
+                               "us_per_step_backtoback": round(r["us_per_step"], 2),
+                               "graph_replay_us_per_step": round(r["graph"]["us_per_step"], 2),
+                               "distinct_experts": r["d_mean"],
+                               "kernel_us": {k: round(t, 2) for k, t in r["kernel_us"].items()}}
+            log(f"tiny rows={rows}: {tiny[str(rows)]}")
     stream_gbs = copy_stream_gbs(torch)
     log(f"copy stream (torch copy of 2 GiB, read + write): {stream_gbs:.0f} GB/s")
     cpu, err = (None, None)
     if not args.no_cpu_baseline and main_rows == 1:
         log("timing the oracle on the host")
-        cpu, err = cpu_baseline(torch, base, m, args.cpu_seconds)
+        cpu, err = cpu_baseline(torch, B, S, base, results, args.cpu_seconds)
     corr = None
     if not args.no_corr:
         # correlated rows (x_i = 0.8 x_0 + 0.6 N(0,1)): rows share experts, the
@@ -534,12 +605,34 @@ def main():
                           seed_base=6000 + 100 * rows)
             log(f"mxfp4 rows={rows}: {r['us_per_step']:.1f} us/step, {r['gbs']:.0f} GB/s "
                 f"({100 * r['frac']:.1f}% of peak), D={r['d_mean']:.1f}, kernels {r['kernel_us']}")
-            mx[str(rows)] = {"us_per_step": round(r["us_per_step"], 2), "gbs": round(r["gbs"], 1),
-                             "frac_of_peak": round(r["frac"], 4), "distinct_experts": r["d_mean"],
-                             "bytes_per_step": int(r["bytes_per_step"]),
-                             "kernel_us": {k: round(t, 2) for k, t in r["kernel_us"].items()},
-                             "graph_replay": {k: round(t, 2) for k, t in r["graph"].items()}}
+            mx[str(rows)] = row_summary(r)
+            if rows == 8 and cpu is not None:
+                threads, _ = oracle_threads()
+                o = oracle_steps(torch, mbase, r["runner"], r["pool"], r["weights"][0], 8, 4.0,
+                                 2, threads, {})
+                cpu["per_config"]["glm_mxfp4_rows8"] = o
+                log(f"oracle mxfp4 rows=8: {o}")
         del mcopies, mbase
+        torch.cuda.empty_cache()
+
+    q1 = None
+    if not args.no_q1:
+        # 1-bit (Q1_0_G128) routed experts, FP8 shared expert: 5.3 MB a routed
+        # expert, so the shared expert and the router are most of a 1-row step
+        log("generating the GLM-scale layer with 1-bit routed experts")
+        copies = None
+        torch.cuda.empty_cache()
+        qbase = S.make_layer("glm", routed_fmt=S.FMT_Q1, seed=1004, device="cuda")
+        qcopies = layer_copies(S, qbase, args.copies)
+        torch.cuda.synchronize()
+        q1 = {}
+        for rows in (1, 8):
+            r = time_rows(torch, B, S, qbase, qcopies, rows, args.steps, args.warmup,
+                          seed_base=6500 + 100 * rows)
+            log(f"q1 rows={rows}: {r['us_per_step']:.1f} us/step, {r['gbs']:.0f} GB/s "
+                f"({100 * r['frac']:.1f}% of peak), D={r['d_mean']:.1f}, kernels {r['kernel_us']}")
+            q1[str(rows)] = row_summary(r)
+        del qcopies, qbase
         torch.cuda.empty_cache()
 
     tp = None
@@ -590,14 +683,17 @@ def main():
 
     line = {
         "metric": METRIC,
-        "value": round(m["gbs"], 1),
+        "value": round(m["gbs_protocol"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(m["us_per_step"] / 1e3, 5),
-        "us_per_step": round(m["us_per_step"], 2),
-        "frac_of_peak": round(m["frac"], 4),
+        "ms_per_step": round(m["us_per_step_protocol"] / 1e3, 5),
+        "us_per_step": round(m["us_per_step_protocol"], 2),
+        "frac_of_peak": round(m["frac_protocol"], 4),
+        "timing": "mean of 2 rounds of the median of 7 trials of 50 back-to-back steps; "
+                  "us_per_step_backtoback = the same steps timed once over --steps",
+        "us_per_step_backtoback": round(m["us_per_step"], 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -620,21 +716,16 @@ def main():
                      "traffic": measured_traffic() if main_rows == 1 else None},
         "cpu_baseline": cpu,
         "oracle_check_out_err_rel_max": err,
-        "by_rows": {str(r): {"us_per_step": round(v["us_per_step"], 2), "gbs": round(v["gbs"], 1),
-                             "frac_of_peak": round(v["frac"], 4), "distinct_experts": v["d_mean"],
-                             "bytes_per_step": int(v["bytes_per_step"]),
-                             "kernel_us": {k: round(t, 2) for k, t in v["kernel_us"].items()},
-                             "upgate_gbs": round(v["upgate_gbs"], 1),
-                             "us_per_step_median7x50_mean2": round(v["us_per_step_protocol"], 2),
-                             "kernel_alone_us": {k: round(t, 2) for k, t in v["alone_us"].items()},
-                             "upgate_alone_gbs": round(v["upgate_alone_bytes"]
-                                                       / (v["alone_us"]["upgate"] * 1e-6) / 1e9, 1),
-                             "graph_replay": {k: round(t, 2) for k, t in v["graph"].items()}}
+        "by_rows": {str(r): dict(row_summary(v),
+                                 upgate_alone_gbs=round(v["upgate_alone_bytes"]
+                                                        / (v["alone_us"]["upgate"] * 1e-6) / 1e9, 1))
                     for r, v in results.items()},
+        "tiny_layer": tiny,
         "hot_us_per_step": hot,
         "copy_stream_gbs": round(stream_gbs, 1),
         "corr_rows": corr,
         "mxfp4_routed": mx,
+        "q1_routed": q1,
         "tp_share": tp,
         "lowbit_gemv": lowbit,
         "lm_head_fp8": head,

@@ -298,9 +298,14 @@ __device__ __forceinline__ float q1_d(uint32_t dd, int h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(h ? (dd >> 16) : (dd & 0xFFFFu)));
 }
 
-// Nontemporal 4-byte load for weights read once per step.
-__device__ __forceinline__ uint32_t ld_nt4(const uint32_t* p) {
-  return __builtin_nontemporal_load(p);
+// A 36-byte chunk (dword-aligned) as two 16-byte and one 4-byte nontemporal
+// loads (the hardware takes 16-byte loads at any dword alignment).
+__device__ __forceinline__ void ld_nt_chunk36(const uint32_t* p, uint32_t* w) {
+  const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 4));
+  w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+  w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
+  w[8] = __builtin_nontemporal_load(p + 8);
 }
 
 }  // namespace moe

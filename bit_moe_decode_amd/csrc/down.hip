@@ -262,9 +262,7 @@ __device__ __forceinline__ void down_q1_issue(const Weights& w, const Dims& d, i
   for (int i = 0; i < 4; i++) {
     if (4 * i < nchunk) {  // wave-uniform
       const int c = 4 * i + (lane & 3);
-      const uint32_t* p = row + 9 * (c < nchunk ? c : 0);
-#pragma unroll
-      for (int q = 0; q < 9; q++) it.w[i][q] = ld_nt4(p + q);
+      ld_nt_chunk36(row + 9 * (c < nchunk ? c : 0), it.w[i]);
     }
   }
 }

@@ -325,9 +325,7 @@ __device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims
   const uint32_t one = q1_in_vgpr(d.q1k[3]);
 
   auto issue = [&](UgStageQ1& st, int it) {
-    const uint32_t* p = src + 18 * it;
-#pragma unroll
-    for (int i = 0; i < 9; i++) st.w[i] = ld_nt4(p + i);
+    ld_nt_chunk36(src + 18 * it, st.w);
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const size_t o = (size_t)(4 * it + q) * 128;

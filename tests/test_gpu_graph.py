@@ -76,6 +76,13 @@ def test_graph_replay_glm_mxfp4():
     _graph_vs_eager(layer, [8, 1], seed=7300)
 
 
+def test_graph_replay_q1_experts():
+    """1-bit routed experts (and the FP8 shared expert) at 1, 4 and 8 rows."""
+    layer = S.make_layer(dict(hidden=1024, inter=512, n_experts=64, shared_inter=512,
+                              router_std=0.02), routed_fmt=S.FMT_Q1, seed=1007, device="cuda")
+    _graph_vs_eager(layer, [8, 1, 4], seed=7300)
+
+
 def test_graph_replay_lowbit_gemv_forms():
     """lowbit_gemv's three forms (1-bit at 1 and 4 rows, FP8 and bf16 at 1 and
     8 rows) captured into one graph: every replay, with eager calls of other
