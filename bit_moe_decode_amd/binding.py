@@ -93,6 +93,11 @@ def lib():
         L.moe_decode_relaunch.restype = ctypes.c_int
         L.moe_decode_relaunch.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(Weights),
                                           ctypes.c_int32, ctypes.c_void_p]
+        L.moe_decode_set_wait.restype = ctypes.c_int
+        L.moe_decode_set_wait.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int32]
+        L.moe_decode_wait_timeouts.restype = ctypes.c_int
+        L.moe_decode_wait_timeouts.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32),
+                                               ctypes.c_void_p]
         L.moe_decode_destroy.restype = None
         L.moe_decode_destroy.argtypes = [ctypes.c_void_p]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -185,6 +190,21 @@ class Context:
         st = self.relaunch_status(kernel, weights, reps, stream)
         if st != MOE_OK:
             raise MoeError(st, "moe_decode_relaunch")
+
+    def set_wait(self, cap_ticks=0, withhold=0):
+        """Cap of the routing launch's waits (100 MHz ticks, 0 = default) and
+        the test-only switch that withholds the routing block's records."""
+        st = lib().moe_decode_set_wait(self.handle, int(cap_ticks), int(withhold))
+        if st != MOE_OK:
+            raise MoeError(st, "moe_decode_set_wait")
+
+    def wait_timeouts(self, stream=None) -> int:
+        """Routed blocks that gave up waiting for their record so far."""
+        n = ctypes.c_uint32()
+        st = lib().moe_decode_wait_timeouts(self.handle, ctypes.byref(n), _stream(stream))
+        if st != MOE_OK:
+            raise MoeError(st, "moe_decode_wait_timeouts")
+        return int(n.value)
 
     def close(self):
         if getattr(self, "handle", None):

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbit_moe_decode.so")
-SOURCES = ["api.hip", "router.hip", "upgate.hip", "down.hip", "lowbit_gemv.hip", "dense_gemv.hip"]
+SOURCES = ["api.hip", "router.hip", "route.hip", "upgate.hip", "down.hip", "lowbit_gemv.hip", "dense_gemv.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

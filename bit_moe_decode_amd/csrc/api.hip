@@ -11,7 +11,9 @@
 namespace moe {
 hipError_t launch_router(const uint16_t* x, const Weights& w, const Ws& ws, const Dims& d,
                          hipStream_t stream);
-hipError_t launch_route(const Weights& w, const Ws& ws, const Dims& d, hipStream_t stream);
+hipError_t launch_route(int rfmt, const Weights& w, const Ws& ws, const Dims& d,
+                        hipStream_t stream);
+bool fused_route(const Dims& d);
 hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& ws,
                          const Dims& d, hipStream_t stream);
 hipError_t launch_down(int rfmt, int max_groups, const Weights& w, const Ws& ws, const Dims& d,
@@ -52,7 +54,7 @@ struct Plan {
   int H, I, E, Is, R, imax, groups, ks;
   size_t off_logits, off_rstd, off_ids, off_gates, off_ngroups, off_gexpert,
       off_gowner, off_gmask, off_gslot, off_grows, off_gnrows, off_actq, off_acts, off_mid,
-      off_midq, off_midqs, off_ypart, off_actu, total;
+      off_midq, off_midqs, off_ypart, off_actu, off_blkrec, off_waitto, total;
 };
 
 bool is_mult(int v, int m) { return v > 0 && v % m == 0; }
@@ -124,6 +126,9 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   p->off_midqs = take(U * (IM / 128) * 4);
   p->off_ypart = take(U * H * 4);
   p->off_actu = take(R * H * 2);
+  // one record per up/gate block of the routing launch: at most Is/16 + G*I/16
+  p->off_blkrec = take((p->Is / 16 + G * (p->I / 16)) * 8);
+  p->off_waitto = take(4);
   p->total = o;
   return MOE_OK;
 }
@@ -151,6 +156,8 @@ Ws make_view(char* b, const Plan& p) {
   v.midqs = reinterpret_cast<float*>(b + p.off_midqs);
   v.ypart = reinterpret_cast<float*>(b + p.off_ypart);
   v.act_u = reinterpret_cast<uint16_t*>(b + p.off_actu);
+  v.blk_rec = reinterpret_cast<uint64_t*>(b + p.off_blkrec);
+  v.wait_timeouts = reinterpret_cast<uint32_t*>(b + p.off_waitto);
   return v;
 }
 
@@ -164,7 +171,13 @@ struct moe_decode_ctx {
   hipEvent_t events[MOE_DECODE_N_KERNELS + 1];
   bool timing;
   int last_rows;  // rows of the last step enqueued, 0 before the first
+  uint32_t wait_ticks;  // cap of the routing launch's waits
+  int withhold;         // 1: the routing block publishes no records
 };
+
+// Default cap of a routed up/gate block's wait for its record: 10 ms of the
+// 100 MHz real-time counter, far beyond the routing's few microseconds.
+constexpr uint32_t kDefaultWaitTicks = 1000000u;
 
 extern "C" {
 
@@ -190,6 +203,8 @@ moe_status moe_decode_init(const moe_decode_config* cfg, void* workspace, size_t
   c->ws = static_cast<char*>(workspace);
   c->timing = false;
   c->last_rows = 0;
+  c->wait_ticks = kDefaultWaitTicks;
+  c->withhold = 0;
   c->view = make_view(c->ws, p);
   // clear the whole workspace once, so that debug views read before the
   // first step are well defined
@@ -252,6 +267,10 @@ moe_status step_args(const moe_decode_config& cfg, const Plan& p, int rows,
   d.no_dedup = (cfg.flags & MOE_F_NO_DEDUP) ? 1 : 0;
   d.eps = cfg.rms_eps;
   d.act_bf16 = cfg.act_fmt == MOE_ACT_BF16 ? 1 : 0;
+  const int picks = 8 * rows;
+  d.groups = d.no_dedup ? picks : (picks < p.E ? picks : p.E);
+  d.wait_ticks = kDefaultWaitTicks;
+  d.withhold = 0;
   d.q1k[0] = 0x0000FFFFu;  // 1-bit operand constants (see q1_fp8_operand)
   d.q1k[1] = 0x00800080u;
   d.q1k[2] = 0x80008000u;
@@ -260,10 +279,6 @@ moe_status step_args(const moe_decode_config& cfg, const Plan& p, int rows,
 }
 
 // Groups a step of `rows` rows can produce: at most 8 * rows (and E with dedup).
-int step_groups(const Plan& p, const Dims& d) {
-  const int picks = 8 * d.rows;
-  return d.no_dedup ? picks : (picks < p.E ? picks : p.E);
-}
 
 // Host checks of a step's x and out (rows >= 1).
 moe_status check_io(const Plan& p, const uint16_t* x, int rows, const moe_decode_weights* w,
@@ -301,13 +316,14 @@ moe_status enqueue_step(int routed_fmt, const Plan& p, const Ws& v, const uint16
   if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (launch_router(x, wt, v, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  // routing, with the shared expert's up/gate alongside
-  if (launch_route(wt, v, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
+  // routing, with the up/gate of the shared and the routed experts alongside
+  // (or the routing alone, then the up/gate)
+  if (launch_route(routed_fmt, wt, v, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  const int groups = step_groups(p, d);
-  if (launch_upgate(routed_fmt, groups, wt, v, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (!fused_route(d) && launch_upgate(routed_fmt, d.groups, wt, v, d, stream) != hipSuccess)
+    return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_ERR_DEVICE;
-  if (launch_down(routed_fmt, groups, wt, v, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
+  if (launch_down(routed_fmt, d.groups, wt, v, d, stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (launch_combine(v, d, out, stream) != hipSuccess) return MOE_ERR_DEVICE;
   if (ev && hipEventRecord(ev[5], stream) != hipSuccess) return MOE_ERR_DEVICE;
@@ -327,6 +343,8 @@ moe_status moe_decode_step(moe_decode_ctx* ctx, const uint16_t* x, int32_t rows,
   Dims d;
   st = step_args(ctx->cfg, p, rows, w, &wt, &d);
   if (st != MOE_OK) return st;
+  d.wait_ticks = ctx->wait_ticks;
+  d.withhold = ctx->withhold;
   ctx->last_rows = rows;
   return enqueue_step(ctx->cfg.routed_fmt, p, ctx->view, x, wt, d, out, stream,
                       ctx->timing ? ctx->events : nullptr);
@@ -399,14 +417,34 @@ moe_status moe_decode_relaunch(moe_decode_ctx* ctx, int32_t kernel,
   Dims d;
   const moe_status st = step_args(ctx->cfg, ctx->plan, ctx->last_rows, w, &wt, &d);
   if (st != MOE_OK) return st;
-  const int groups = step_groups(ctx->plan, d);
+  d.wait_ticks = ctx->wait_ticks;
+  const int rf = ctx->cfg.routed_fmt;
   for (int i = 0; i < reps; i++) {
-    const hipError_t e = kernel == MOE_DECODE_K_UPGATE
-                             ? launch_upgate(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream)
-                             : launch_down(ctx->cfg.routed_fmt, groups, wt, ctx->view, d, stream);
+    hipError_t e;
+    if (kernel == MOE_DECODE_K_DOWN)
+      e = launch_down(rf, d.groups, wt, ctx->view, d, stream);
+    else if (fused_route(d))  // the up/gate runs in the routing launch: relaunch that
+      e = launch_route(rf, wt, ctx->view, d, stream);
+    else
+      e = launch_upgate(rf, d.groups, wt, ctx->view, d, stream);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
   }
   return MOE_OK;
+}
+
+moe_status moe_decode_set_wait(moe_decode_ctx* ctx, uint32_t cap_ticks, int32_t withhold) {
+  if (!ctx || (withhold != 0 && withhold != 1)) return MOE_ERR_INVALID_ARG;
+  ctx->wait_ticks = cap_ticks ? cap_ticks : kDefaultWaitTicks;
+  ctx->withhold = withhold;
+  return MOE_OK;
+}
+
+moe_status moe_decode_wait_timeouts(moe_decode_ctx* ctx, uint32_t* count, hipStream_t stream) {
+  if (!ctx || !count) return MOE_ERR_INVALID_ARG;
+  if (hipMemcpyAsync(count, ctx->view.wait_timeouts, sizeof(uint32_t), hipMemcpyDeviceToHost,
+                     stream) != hipSuccess)
+    return MOE_ERR_DEVICE;
+  return hipStreamSynchronize(stream) == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
 void moe_decode_destroy(moe_decode_ctx* ctx) { delete ctx; }

@@ -60,6 +60,11 @@ struct Ws {
   uint8_t* midq;          // [max_rows * 9][imax]
   float* midqs;           // [max_rows * 9][imax/128]
   float* ypart;           // [max_rows * 9][H] down output per (row, pick)
+  // routing launch: one record per up/gate block (the shared expert's go,
+  // then each routed block's group_record, route.h), cleared by the router
+  // and by the block that reads it
+  uint64_t* blk_rec;      // [Is/16 + G * I/16]
+  uint32_t* wait_timeouts;  // [1] routed blocks that gave up waiting for their record
 };
 
 // Shapes of the step (all multiples as validated on the host).
@@ -70,6 +75,9 @@ struct Dims {
   int ks;              // up/gate K parts (divides H/128)
   int no_dedup;        // 1: one group per (row, pick)
   int act_bf16;        // 1: the experts take u (bf16), not FP8 activation blocks
+  int groups;          // routed groups the up/gate grid covers (8 * rows, or E if fewer)
+  uint32_t wait_ticks; // cap of a routed block's wait for its record (100 MHz ticks)
+  int withhold;        // 1: the routing block publishes no records (failure tests)
   float eps;
   // 1-bit expert operand constants (0x0000FFFF, 0x00800080, 0x80008000,
   // 0x38383838), passed in so that they sit in registers: see q1_fp8_operand

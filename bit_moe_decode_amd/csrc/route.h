@@ -41,23 +41,43 @@ struct RouteSmem {
   uint8_t g_owner[64][2];
   uint8_t g_rows[64][8];
   uint8_t g_nrows[64];
+  uint64_t g_rec[64];  // published record of each group (group_record)
   int n_groups;
 };
 
-// The 8 largest order keys of the logits z[0 .. E) of one row, unordered,
-// with their expert IDs: written to ckey[0 .. 8) and cid[0 .. 8) by the lanes
-// that hold them.  Runs with one full wave; lane l holds experts l, l + 64,
-// ... in KPL = ceil(E / 64) key slots (key 0, below every logit, past E).
+// Record of a routed up/gate block in moe_route_kernel, 64 bits: bit 0 set
+// when published; bits 1-10 the group's expert, 11-14 its number of using
+// rows (0: the step has no such group), 15 + 3c its c-th using row, 39 + 3r
+// the pick that row r of the group made (rows of the group only).  Expert IDs
+// are below 1024 and rows below 8, so the fields hold them whole.
+__device__ __forceinline__ uint64_t group_record(int expert, int nrows, const uint8_t* rows,
+                                                 const uint8_t* slot) {
+  uint64_t rec = 1u | ((uint64_t)expert << 1) | ((uint64_t)nrows << 11);
+  for (int c = 0; c < nrows; c++) {
+    const int r = rows[c];
+    rec |= (uint64_t)r << (15 + 3 * c);
+    rec |= (uint64_t)(slot[r] & 7) << (39 + 3 * r);
+  }
+  return rec;
+}
+
+// Order keys of the logits z[0 .. E) of one row: lane l holds experts l,
+// l + 64, ... in KPL = ceil(E / 64) key slots (key 0, below every logit, past E).
 template <int KPL>
-__device__ __forceinline__ void select8(const float* z, int E, int lane, uint32_t* ckey,
-                                        int* cid) {
-  uint32_t key[KPL];
+__device__ __forceinline__ void load_keys(const float* z, int E, int lane, uint32_t* key) {
 #pragma unroll
   for (int i = 0; i < KPL; i++) {
     const int e = lane + kWave * i;
     const float v = z[e < E ? e : E - 1];  // lanes past E load in bounds
     key[i] = e < E ? topk_vkey(v) : 0u;
   }
+}
+
+// The 8 largest of a row's order keys (load_keys), unordered, with their
+// expert IDs: written to ckey[0 .. 8) and cid[0 .. 8) by the lanes that hold
+// them.  Runs with one full wave.
+template <int KPL>
+__device__ __forceinline__ void select8(const uint32_t* key, int lane, uint32_t* ckey, int* cid) {
 
   // T: the largest t with at least 8 keys >= t (E >= 16 real keys, all >= 1)
   uint32_t t = 0;
@@ -136,14 +156,28 @@ __device__ __forceinline__ void publish_gates(const Ws& ws, int r, const float* 
 // Runs with every thread of the block (it contains block barriers).  Fills
 // `rs` for rows 0..d.rows-1; when `publish`, also writes ids, gates and the
 // group table to the workspace.  KPL = key slots per lane, ceil(E / 64).
+// go > 0 (the routing launch): once row 0's logits are in registers, wave 0
+// publishes the records 0 .. go - 1 of the launch's first up/gate blocks
+// (the shared expert's), which hold back their weight loads until then, so
+// that the logits' loads do not queue behind those streams.
 template <int KPL>
 __device__ __forceinline__ void route_block(const Ws& ws, const Dims& d, RouteSmem& rs,
-                                            bool publish) {
+                                            bool publish, int go = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
   const int R = d.rows, E = d.E;
 
-  for (int r = wv; r < R; r += nw)
-    select8<KPL>(ws.logits + (size_t)r * E, E, lane, rs.ckey[r], rs.cid[r]);
+  for (int r = wv; r < R; r += nw) {
+    uint32_t key[KPL];
+    load_keys<KPL>(ws.logits + (size_t)r * E, E, lane, key);
+    if (go > 0 && r == 0) {
+      // the logits loads have returned (the wait), so the stores come after them
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      for (int i = lane; i < go; i += kWave)
+        __hip_atomic_store(ws.blk_rec + i, (uint64_t)1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    select8<KPL>(key, lane, rs.ckey[r], rs.cid[r]);
+  }
   if (tid < 64) {
     rs.g_mask[tid] = 0u;
 #pragma unroll
@@ -211,6 +245,7 @@ __device__ __forceinline__ void route_block(const Ws& ws, const Dims& d, RouteSm
     for (int r = 0; r < 8; r++)
       if ((m >> r) & 1u) rs.g_rows[tid][n++] = (uint8_t)r;
     rs.g_nrows[tid] = (uint8_t)n;
+    rs.g_rec[tid] = group_record(rs.g_expert[tid], n, rs.g_rows[tid], rs.g_slot[tid]);
     if (publish) {
       ws.grp_expert[tid] = rs.g_expert[tid];
       ws.grp_owner[2 * tid] = rs.g_owner[tid][0];

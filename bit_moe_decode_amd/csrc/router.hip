@@ -4,7 +4,7 @@
 // #85 Mod. row 10: the router multiplies u = bf16(x * gamma) (the product is
 // exact in fp32, rounded once) and scales each row's dots by its rstd; the
 // same u, quantised per 1x128 block, is the activation of the up/gate GEMV,
-// whose results take the rstd afterwards.  moe_route_kernel (upgate.hip) then
+// whose results take the rstd afterwards.  The routing launch (route.hip) then
 // derives the top-8, gates and dedup table from these logits in one block
 // (route.h).
 //
@@ -55,6 +55,11 @@ __global__ __launch_bounds__(1024) void moe_router_kernel(const uint16_t* __rest
   const int q = lane >> 4, s = lane & 15;
   const int H = d.H, E = d.E, nkb = H / 128;
   const int e0 = blockIdx.x * EB;
+
+  // the routing launch's records (route.hip) start unpublished
+  const int nrec = (d.Is + d.groups * d.I) / (16 * (4 / d.ks));
+  for (int t = blockIdx.x * blockDim.x + tid; t < nrec; t += gridDim.x * blockDim.x)
+    ws.blk_rec[t] = 0u;
 
   float dot[EB][R], ss[R];
 #pragma unroll

@@ -1,503 +1,17 @@
-// upgate.hip -- up/gate GEMV of the shared expert and of every distinct
-// routed expert, and mid = silu(gate) * up from it.
-//
-// #85 Mod. row 16: up/gate jobs are tiles of the shared expert and of each
-// distinct expert, with every row that uses the expert as an MFMA column, so
-// an expert's weights stream once however many rows picked it.  Mod. rows 18
-// and 21: weights load 16 bytes a lane and, being read once, nontemporal.
-// Mod. row 1 and the MXFP4 page: routed experts may instead hold MXFP4
-// weights (E2M1 pairs, one E8M0 exponent per 32 inputs); the shared expert
-// stays FP8.
-//
-// Block = 4 waves = 4/ks slabs of 16 intermediate rows x ks parts of K; the
-// blocks are numbered over the shared expert's slabs, then I/16 slabs for each
-// of the step's possible routed groups (blocks of groups past the step's D
-// exit at once).  For steps of up to 4 rows the shared expert's blocks run
-// beside the routing block in moe_route_kernel; the routed ones (and else the
-// shared ones too) in moe_upgate_kernel.
-// Many small blocks let the hardware dispatcher even out the load per CU.
-// A wave loads its 16 weight rows of gate and of up row-contiguously (8 lanes
-// read one row's 128-byte line), re-lays them through LDS into MFMA operand
-// order and runs 16x16x128 MFMAs whose 16 columns are the expert's using rows;
-// the fp32 results are scaled and accumulated.  The block then adds its K-part
-// sums in part order, through LDS, and stores
-//   mid = silu(gate * rstd) * (up * rstd)          (fp32)
-// per (row, pick) of its slabs.  No block waits for another.  The FP8
-// re-quantisation of mid is done by the down kernel, which reads it.
-//
-//  FP8 item = one 128-wide K block: one FP8 x FP8 MFMA per matrix, scaled by
-//    weight block scale x activation block scale.
-//  FP8 item with bf16 activations (MOE_ACT_BF16, u itself as the input): the
-//    K block's codes converted to bf16 exactly, four 16x16x32 bf16 MFMAs per
-//    matrix against u, scaled by the weight block scale.
-//  MXFP4 item = two 128-wide K blocks (a 128-byte line per row): per K block
-//    one scaled FP4 x FP8 MFMA per matrix, the E8M0 exponents entering as the
-//    MFMA's A scales, then the activation block scale.  Operand layout of that
-//    MFMA on gfx950 (established by a device probe): A lane l holds row l%16
-//    and the 32 inputs 32*(l/16) .. +32 of the K block as 16 bytes, low nibble
-//    first, with the E8M0 of those 32 as its scale; B lane l holds column l%16
-//    and the FP8 inputs 16*(l/16) .. +16 and 64 + 16*(l/16) .. +16.
-#include "route.h"
+// upgate.hip -- the up/gate launch of steps whose routing runs alone
+// (moe_route_only_kernel): the shared expert's slabs and every routed
+// group's, which read the published table (the block's code is in upgate.h).
+#include "upgate.h"
 
 namespace moe {
 
-// One K item of one wave: gate and up weight rows (row-contiguous), the using
-// rows' activation codes in operand order and the scales.  Every lane loads
-// (columns past the expert's rows read row 0; their results are never
-// stored), so the ring carries no per-lane condition.
-struct UgStage {
-  u32x4 g0, g1, u0, u1, a0, a1;
-  float sg, su, sa;
-};
-struct UgStage4 {
-  u32x4 g0, g1, u0, u1, a0, a1, a2, a3;  // a0,a1: K block 0; a2,a3: K block 1
-  uint32_t eg0, eg1, eu0, eu1;           // E8M0 of the lane's row, K blocks 0 and 1
-  float sa0, sa1;
-};
-
-// Operand of the scaled MFMA for FP4 A: 16 bytes in the low half.
-__device__ __forceinline__ v8i fp4_operand(const u32x4& v) {
-  v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
-  r[0] = v[0];
-  r[1] = v[1];
-  r[2] = v[2];
-  r[3] = v[3];
-  return r;
-}
-// Row l%16, bytes 64h + 16(l/16) .. +16 of the tile (K block h of the item).
-__device__ __forceinline__ u32x4 tile_get_fp4(const uint8_t* tile, int lane, int h) {
-  return *reinterpret_cast<const u32x4*>(tile + (lane & 15) * kTileStride + 64 * h +
-                                         (lane >> 4) * 16);
-}
-__device__ __forceinline__ v4f mfma_fp4_fp8(const v8i& a, const v8i& b, int scale_a) {
-  v4f z = {0.f, 0.f, 0.f, 0.f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 4, 0, 0, scale_a, 0, 127);
-}
-
-struct UgJob {
-  int e, row, n0;  // expert (-1: shared), activation row of the lane's column, first row
-};
-
-// FP8 weights: K blocks kb0 .. kb0 + nk of the slab.
-template <int P>
-__device__ __forceinline__ void ug_fp8(const Weights& w, const Ws& ws, const Dims& d, UgJob j,
-                                       int kb0, int nk, uint8_t* tg, uint8_t* tu, int lane,
-                                       float* accg, float* accu) {
-  const int H = d.H, nkbh = H / 128;
-  const size_t ebytes = (size_t)d.I * H;
-  const size_t escl = (size_t)(d.I / 128) * nkbh;  // scales per routed expert
-  const uint8_t* bg = j.e < 0 ? w.sg_c : w.gate_c + (size_t)j.e * ebytes;
-  const uint8_t* bu = j.e < 0 ? w.su_c : w.up_c + (size_t)j.e * ebytes;
-  const float* sg =
-      j.e < 0 ? w.sg_s : reinterpret_cast<const float*>(w.gate_s) + (size_t)j.e * escl;
-  const float* su = j.e < 0 ? w.su_s : reinterpret_cast<const float*>(w.up_s) + (size_t)j.e * escl;
-  // lane l loads rows n0 + l/8 and n0 + 8 + l/8, 16-byte chunk l%8
-  const uint8_t* pg = bg + (size_t)(j.n0 + (lane >> 3)) * H + (lane & 7) * 16 + (size_t)kb0 * 128;
-  const uint8_t* pu = bu + (pg - bg);
-  const size_t r8 = (size_t)8 * H;
-  const uint8_t* pa = ws.act_q + (size_t)j.row * H + (lane >> 4) * 32 + (size_t)kb0 * 128;
-  const float* psg = sg + (size_t)(j.n0 / 128) * nkbh + kb0;
-  const float* psu = su + (size_t)(j.n0 / 128) * nkbh + kb0;
-  const float* psa = ws.act_s + (size_t)j.row * nkbh + kb0;
-
-  auto issue = [&](UgStage& st, int k) {
-    const size_t o = (size_t)k * 128;
-    st.g0 = ld_nt16(pg + o);
-    st.g1 = ld_nt16(pg + r8 + o);
-    st.u0 = ld_nt16(pu + o);
-    st.u1 = ld_nt16(pu + r8 + o);
-    st.a0 = ld16(pa + o);
-    st.a1 = ld16(pa + o + 16);
-    st.sg = psg[k];
-    st.su = psu[k];
-    st.sa = psa[k];
-  };
-  auto consume = [&](UgStage& st) {
-    tile_put(tg, lane, st.g0, st.g1);
-    tile_put(tu, lane, st.u0, st.u1);
-    asm volatile("" ::: "memory");
-    const v8i bv = cat8(st.a0, st.a1);
-    const v4f cgv = mfma_fp8(tile_get(tg, lane), bv);
-    const v4f cuv = mfma_fp8(tile_get(tu, lane), bv);
-    asm volatile("" ::: "memory");
-    const float fg = st.sg * st.sa, fu = st.su * st.sa;
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-      accg[v] = fmaf(cgv[v], fg, accg[v]);
-      accu[v] = fmaf(cuv[v], fu, accu[v]);
-    }
-  };
-  // ring of P K blocks (P divides nk): every issued load is used
-  UgStage st[P];
-#pragma unroll
-  for (int p = 0; p < P; p++) issue(st[p], p);
-  for (int k0 = 0; k0 < nk - P; k0 += P) {
-#pragma unroll
-    for (int p = 0; p < P; p++) {
-      consume(st[p]);
-      issue(st[p], k0 + P + p);
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < P; p++) consume(st[p]);
-}
-
-// FP8 weights against bf16 activations (u itself): K blocks kb0 .. kb0 + nk
-// of the slab.  The weight rows are re-laid through LDS as for FP8; then per
-// 32 inputs of the K block, lane l converts the 8 codes of row l%16 at inputs
-// 32s + 8(l/16) .. +8 to bf16 (exact: every E4M3 value is a bf16 value; the
-// conversion's scale is 1) and runs one 16x16x32 bf16 MFMA per matrix against
-// its using row's u at the same inputs; the K block's fp32 result is scaled
-// by the weight block scale (rstd comes in the epilogue).
-struct UgStageB {
-  u32x4 g0, g1, u0, u1, a[4];
-  float sg, su;
-};
-template <int P>
-__device__ __forceinline__ void ug_fp8_bf16a(const Weights& w, const Ws& ws, const Dims& d,
-                                             UgJob j, int kb0, int nk, uint8_t* tg, uint8_t* tu,
-                                             int lane, float* accg, float* accu) {
-  const int H = d.H, nkbh = H / 128;
-  const size_t ebytes = (size_t)d.I * H;
-  const size_t escl = (size_t)(d.I / 128) * nkbh;
-  const uint8_t* bg = j.e < 0 ? w.sg_c : w.gate_c + (size_t)j.e * ebytes;
-  const uint8_t* bu = j.e < 0 ? w.su_c : w.up_c + (size_t)j.e * ebytes;
-  const float* sg =
-      j.e < 0 ? w.sg_s : reinterpret_cast<const float*>(w.gate_s) + (size_t)j.e * escl;
-  const float* su = j.e < 0 ? w.su_s : reinterpret_cast<const float*>(w.up_s) + (size_t)j.e * escl;
-  const uint8_t* pg = bg + (size_t)(j.n0 + (lane >> 3)) * H + (lane & 7) * 16 + (size_t)kb0 * 128;
-  const uint8_t* pu = bu + (pg - bg);
-  const size_t r8 = (size_t)8 * H;
-  // u of the lane's column at inputs 8(l/16) .. +8 of each 32-input step
-  const uint16_t* pa = ws.act_u + (size_t)j.row * H + (lane >> 4) * 8 + (size_t)kb0 * 128;
-  const float* psg = sg + (size_t)(j.n0 / 128) * nkbh + kb0;
-  const float* psu = su + (size_t)(j.n0 / 128) * nkbh + kb0;
-  const int col = lane & 15, g = lane >> 4;
-
-  auto issue = [&](UgStageB& st, int k) {
-    const size_t o = (size_t)k * 128;
-    st.g0 = ld_nt16(pg + o);
-    st.g1 = ld_nt16(pg + r8 + o);
-    st.u0 = ld_nt16(pu + o);
-    st.u1 = ld_nt16(pu + r8 + o);
-#pragma unroll
-    for (int s = 0; s < 4; s++) st.a[s] = ld16(pa + o + 32 * s);
-    st.sg = psg[k];
-    st.su = psu[k];
-  };
-  auto consume = [&](UgStageB& st) {
-    tile_put(tg, lane, st.g0, st.g1);
-    tile_put(tu, lane, st.u0, st.u1);
-    asm volatile("" ::: "memory");
-    v4f cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; s++) {
-      const int off = col * kTileStride + 32 * s + 8 * g;
-      const v8bf ag = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(tg + off));
-      const v8bf au = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(tu + off));
-      const v8bf b = __builtin_bit_cast(v8bf, st.a[s]);
-      cg = mfma_bf16(ag, b, cg);
-      cu = mfma_bf16(au, b, cu);
-    }
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-      accg[v] = fmaf(cg[v], st.sg, accg[v]);
-      accu[v] = fmaf(cu[v], st.su, accu[v]);
-    }
-  };
-  UgStageB st[P];
-#pragma unroll
-  for (int p = 0; p < P; p++) issue(st[p], p);
-  for (int k0 = 0; k0 < nk - P; k0 += P) {
-#pragma unroll
-    for (int p = 0; p < P; p++) {
-      consume(st[p]);
-      issue(st[p], k0 + P + p);
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < P; p++) consume(st[p]);
-}
-
-// MXFP4 weights: items (pairs of K blocks) it0 .. it0 + ni of the slab.
-template <int P>
-__device__ __forceinline__ void ug_fp4(const Weights& w, const Ws& ws, const Dims& d, UgJob j,
-                                       int it0, int ni, uint8_t* tg, uint8_t* tu, int lane,
-                                       float* accg, float* accu) {
-  const int H = d.H, nkbh = H / 128;
-  const size_t rbytes = H / 2;  // one row of codes
-  const size_t ebytes = (size_t)d.I * rbytes, escl = (size_t)d.I * (H / 32);
-  const uint8_t* bg = w.gate_c + (size_t)j.e * ebytes;
-  const uint8_t* bu = w.up_c + (size_t)j.e * ebytes;
-  const uint8_t* eg = reinterpret_cast<const uint8_t*>(w.gate_s) + (size_t)j.e * escl;
-  const uint8_t* eu = reinterpret_cast<const uint8_t*>(w.up_s) + (size_t)j.e * escl;
-  // lane l loads rows n0 + l/8 and n0 + 8 + l/8, 16-byte chunk l%8 of the
-  // item's 128 bytes, and the E8M0 of its MFMA row n0 + l%16 (4 per K block)
-  const uint8_t* pg =
-      bg + (size_t)(j.n0 + (lane >> 3)) * rbytes + (lane & 7) * 16 + (size_t)it0 * 128;
-  const uint8_t* pu = bu + (pg - bg);
-  const size_t r8 = 8 * rbytes;
-  const uint8_t* peg = eg + (size_t)(j.n0 + (lane & 15)) * (H / 32) + (size_t)it0 * 8;
-  const uint8_t* peu = eu + (peg - eg);
-  // activation of K block 2i + h: bytes 16(l/16) .. +16 and 64 + 16(l/16) .. +16
-  const uint8_t* pa = ws.act_q + (size_t)j.row * H + (lane >> 4) * 16 + (size_t)it0 * 256;
-  const float* psa = ws.act_s + (size_t)j.row * nkbh + 2 * it0;
-  const int sh = 8 * (lane >> 4);  // the lane's byte of each E8M0 word
-
-  auto issue = [&](UgStage4& st, int k) {
-    const size_t o = (size_t)k * 128;
-    st.g0 = ld_nt16(pg + o);
-    st.g1 = ld_nt16(pg + r8 + o);
-    st.u0 = ld_nt16(pu + o);
-    st.u1 = ld_nt16(pu + r8 + o);
-    const size_t oa = (size_t)k * 256;
-    st.a0 = ld16(pa + oa);
-    st.a1 = ld16(pa + oa + 64);
-    st.a2 = ld16(pa + oa + 128);
-    st.a3 = ld16(pa + oa + 192);
-    st.eg0 = *reinterpret_cast<const uint32_t*>(peg + 8 * k);
-    st.eg1 = *reinterpret_cast<const uint32_t*>(peg + 8 * k + 4);
-    st.eu0 = *reinterpret_cast<const uint32_t*>(peu + 8 * k);
-    st.eu1 = *reinterpret_cast<const uint32_t*>(peu + 8 * k + 4);
-    st.sa0 = psa[2 * k];
-    st.sa1 = psa[2 * k + 1];
-  };
-  auto consume = [&](UgStage4& st) {
-    tile_put(tg, lane, st.g0, st.g1);
-    tile_put(tu, lane, st.u0, st.u1);
-    asm volatile("" ::: "memory");
-    const v8i b0 = cat8(st.a0, st.a1), b1 = cat8(st.a2, st.a3);
-    const v4f cg0 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tg, lane, 0)), b0, (st.eg0 >> sh) & 0xFF);
-    const v4f cu0 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tu, lane, 0)), b0, (st.eu0 >> sh) & 0xFF);
-    const v4f cg1 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tg, lane, 1)), b1, (st.eg1 >> sh) & 0xFF);
-    const v4f cu1 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tu, lane, 1)), b1, (st.eu1 >> sh) & 0xFF);
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-      accg[v] = fmaf(cg1[v], st.sa1, fmaf(cg0[v], st.sa0, accg[v]));
-      accu[v] = fmaf(cu1[v], st.sa1, fmaf(cu0[v], st.sa0, accu[v]));
-    }
-  };
-  // ring of P items (P divides ni)
-  UgStage4 st[P];
-#pragma unroll
-  for (int p = 0; p < P; p++) issue(st[p], p);
-  for (int k0 = 0; k0 < ni - P; k0 += P) {
-#pragma unroll
-    for (int p = 0; p < P; p++) {
-      consume(st[p]);
-      issue(st[p], k0 + P + p);
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < P; p++) consume(st[p]);
-}
-
-// 1-bit weights (Q1_0_G128): groups kb0 .. kb0 + nk of the slab (nk a
-// multiple of 4, kb0 even).  An item is 4 groups = 2 chunks of 36 bytes per
-// row: lane l loads chunk l%2 of row (l%32)/2 of gate (l < 32) or up, 9
-// dwords, row-contiguous and nontemporal, and re-aligns it into the wave's
-// LDS area (sign dwords and d by chunk, dword and row); then per group the
-// lane reads the sign dword l/16 of its MFMA row l%16 for gate and up, builds
-// E4M3 +-1 operands from it and runs one FP8 MFMA per matrix against the
-// using rows' activation codes; each row's sum is scaled by its group d and
-// the activation block scale and accumulated.
-struct UgStageQ1 {
-  uint32_t w[9];  // the lane's chunk
-  u32x4 a[4][2];  // activation codes of the item's 4 groups (operand order)
-  float sa[4];
-};
-template <int P>
-__device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims& d, UgJob j,
-                                      int kb0, int nk, uint32_t* lds, int lane, float* accg,
-                                      float* accu) {
-  const int H = d.H, nkbh = H / 128;
-  const size_t rb = (size_t)18 * nkbh;  // bytes per row
-  const size_t ebytes = (size_t)d.I * rb;
-  const int m = lane >> 5, lrow = (lane & 31) >> 1, lq = lane & 1;
-  const int col = lane & 15, g = lane >> 4;
-  const uint8_t* base = (m ? w.up_c : w.gate_c) + (size_t)j.e * ebytes;
-  const uint32_t* src =
-      reinterpret_cast<const uint32_t*>(base + (size_t)(j.n0 + lrow) * rb) + 9 * (kb0 / 2 + lq);
-  const uint8_t* pa = ws.act_q + (size_t)j.row * H + (lane >> 4) * 32 + (size_t)kb0 * 128;
-  const float* psa = ws.act_s + (size_t)j.row * nkbh + kb0;
-  const uint32_t one = q1_in_vgpr(d.q1k[3]);
-
-  auto issue = [&](UgStageQ1& st, int it) {
-    ld_nt_chunk36(src + 18 * it, st.w);
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const size_t o = (size_t)(4 * it + q) * 128;
-      st.a[q][0] = ld16(pa + o);
-      st.a[q][1] = ld16(pa + o + 16);
-      st.sa[q] = psa[4 * it + q];
-    }
-  };
-  auto consume = [&](UgStageQ1& st) {
-    uint32_t u[8], dd;
-    q1_chunk_split(st.w, u, &dd);
-    const int area = (m * 2 + lq);
-#pragma unroll
-    for (int i = 0; i < 8; i++) lds[(area * 8 + i) * 16 + lrow] = u[i];
-    lds[512 + area * 16 + lrow] = dd;
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int q = 0; q < 2; q++) {
-      const u32x4 dg = *reinterpret_cast<const u32x4*>(lds + 512 + (0 * 2 + q) * 16 + 4 * g);
-      const u32x4 du = *reinterpret_cast<const u32x4*>(lds + 512 + (1 * 2 + q) * 16 + 4 * g);
-#pragma unroll
-      for (int h = 0; h < 2; h++) {
-        const int gi = 2 * q + h;  // group of the item
-        const uint32_t wg = lds[((0 * 2 + q) * 8 + 4 * h + g) * 16 + col];
-        const uint32_t wu = lds[((1 * 2 + q) * 8 + 4 * h + g) * 16 + col];
-        const v8i bv = cat8(st.a[gi][0], st.a[gi][1]);
-        const v4f cg = mfma_fp8(q1_fp8_operand(wg, d.q1k, one), bv);
-        const v4f cu = mfma_fp8(q1_fp8_operand(wu, d.q1k, one), bv);
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-          accg[v] = fmaf(cg[v], q1_d(dg[v], h) * st.sa[gi], accg[v]);
-          accu[v] = fmaf(cu[v], q1_d(du[v], h) * st.sa[gi], accu[v]);
-        }
-      }
-    }
-    asm volatile("" ::: "memory");
-  };
-  const int ni = nk / 4;
-  UgStageQ1 st[P];
-#pragma unroll
-  for (int p = 0; p < P; p++) issue(st[p], p);
-  for (int k0 = 0; k0 < ni - P; k0 += P) {
-#pragma unroll
-    for (int p = 0; p < P; p++) {
-      consume(st[p]);
-      issue(st[p], k0 + P + p);
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < P; p++) consume(st[p]);
-}
-
-typedef uint8_t UgTiles[4][2][kTileBytes];  // per wave: gate and up weight tiles
-
-// Up/gate block number `blk` of the numbering above (the shared expert's
-// slabs, then those of each routed group), with 256 threads.
+// Up/gate blocks: the shared expert's slabs, then the routed groups'.
 template <int RF, int P, int P4, bool AB>
-__device__ __forceinline__ void upgate_block(const Weights& w, const Ws& ws, const Dims& d,
-                                             int blk, UgTiles& s_tile) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int KS = d.ks;
-  const int spb = 4 / KS;  // slabs per block
-  const int col = lane & 15;
-
-  // ---- the block's expert and slab
-  const int nb_sh = d.Is / (16 * spb);
-  int b = blk, g = -1, nrows, row, e;
-  uint64_t rows8 = 0, picks8 = 0;  // using rows, and the pick of each row (routed)
-  if (b < nb_sh) {
-    nrows = d.rows;
-    row = col < nrows ? col : 0;
-    e = -1;
-  } else {
-    b -= nb_sh;
-    const int per = d.I / (16 * spb);
-    g = b / per;
-    b -= g * per;
-    // one round of independent loads; the table of a group past D is stale
-    // but in bounds, and unused
-    const int D = *ws.n_groups;
-    e = ws.grp_expert[g];
-    nrows = ws.grp_nrows[g];
-    rows8 = *reinterpret_cast<const uint64_t*>(ws.grp_rows + g * 8);
-    picks8 = *reinterpret_cast<const uint64_t*>(ws.grp_slot + g * 8);
-    if (g >= D) return;
-    row = col < nrows ? (int)((rows8 >> (8 * (col & 7))) & 0xFF) : 0;
-  }
-  const int slab = b * spb + wv / KS, kp = wv % KS;
-  const UgJob j{e, row, slab * 16};
-  float accg[4] = {0.f, 0.f, 0.f, 0.f}, accu[4] = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (AB) {  // bf16 activations (FP8 weights only)
-    const int nk = d.H / 128 / KS;
-    ug_fp8_bf16a<P>(w, ws, d, j, kp * nk, nk, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
-  } else if (RF == kFmtMxfp4 && e >= 0) {
-    const int ni = d.H / 256 / KS;  // items of two K blocks per part
-    ug_fp4<P4>(w, ws, d, j, kp * ni, ni, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
-  } else if (RF == kFmtQ1 && e >= 0) {
-    const int nk = d.H / 128 / KS;  // groups per part, a multiple of 4
-    ug_q1<P4>(w, ws, d, j, kp * nk, nk, reinterpret_cast<uint32_t*>(s_tile[wv][0]), lane, accg,
-              accu);
-  } else {
-    const int nk = d.H / 128 / KS;
-    ug_fp8<P>(w, ws, d, j, kp * nk, nk, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
-  }
-  pin4(accg);  // the MFMAs run with every lane, before any divergent use
-  pin4(accu);
-
-  // ---- K parts -> mid.  Each wave parks its 16 x 16 sums of gate and of up
-  // in its own (finished) tile, column-major: element (n, c) at c*16 + n.
-  float* part = reinterpret_cast<float*>(s_tile[wv][0]);
-  *reinterpret_cast<v4f*>(part + col * 16 + 4 * (lane >> 4)) = v4f{accg[0], accg[1], accg[2], accg[3]};
-  *reinterpret_cast<v4f*>(part + 256 + col * 16 + 4 * (lane >> 4)) =
-      v4f{accu[0], accu[1], accu[2], accu[3]};
-  __syncthreads();
-  // thread t: element n = t%16 of column c = t/16, for each slab of the block
-  const int c = tid >> 4, n = tid & 15;
-  if (c >= nrows) return;
-  const int r = g < 0 ? c : (int)((rows8 >> (8 * c)) & 0xFF);
-  const int pick = g < 0 ? 8 : (int)((picks8 >> (8 * r)) & 0xFF);
-  const float rs = ws.rstd[r];
-  float* mrow = ws.mid + (size_t)(r * 9 + pick) * d.imax;
-  for (int s = 0; s < spb; s++) {
-    const float* p0 = reinterpret_cast<const float*>(s_tile[s * KS][0]);
-    float gs = p0[tid], us = p0[256 + tid];
-    for (int q = 1; q < KS; q++) {  // parts in order
-      const float* pq = reinterpret_cast<const float*>(s_tile[s * KS + q][0]);
-      gs += pq[tid];
-      us += pq[256 + tid];
-    }
-    const float gt = gs * rs, ut = us * rs;
-    mrow[(b * spb + s) * 16 + n] = gt / (1.0f + expf(-gt)) * ut;
-  }
-}
-
-// Up/gate blocks base, base + 1, ... (base = 0: the shared expert's slabs and
-// the routed groups'; base = Is/BR: the routed groups' only).
-template <int RF, int P, int P4, bool AB>
-__global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims d, int base) {
+__global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims d) {
   __shared__ __align__(16) UgTiles s_tile;
-  upgate_block<RF, P, P4, AB>(w, ws, d, base + blockIdx.x, s_tile);
+  __shared__ uint64_t s_rec;
+  upgate_block<RF, P, P4, AB, false>(w, ws, d, blockIdx.x, s_tile, &s_rec);
 }
-
-// Steps of up to 4 rows: the step's routing decisions (top-8, gates, dedup
-// table; route.h) in block 0, and the shared expert's up/gate slabs in blocks
-// 1 .. Is/BR.  The shared expert needs only the router's activation blocks and
-// rstd, so its weights stream while the routing, a latency-bound single
-// block, runs.  (With more rows the routing takes longer on 4 waves than the
-// shared expert saves: moe_route_only_kernel on 8 waves, and the shared
-// slabs go with the routed ones.)
-template <int KPL, int P, bool AB>
-__global__ __launch_bounds__(256) void moe_route_kernel(Weights w, Ws ws, Dims d) {
-  __shared__ RouteSmem rs;
-  __shared__ __align__(16) UgTiles s_tile;
-  if (blockIdx.x == 0)
-    route_block<KPL>(ws, d, rs, true);
-  else
-    upgate_block<kFmtFp8, P, 1, AB>(w, ws, d, blockIdx.x - 1, s_tile);
-}
-
-template <int KPL>
-__global__ __launch_bounds__(512) void moe_route_only_kernel(Ws ws, Dims d) {
-  __shared__ RouteSmem rs;
-  route_block<KPL>(ws, d, rs, true);
-}
-
-// Whether the shared expert's up/gate runs in the routing launch.
-bool shared_with_route(const Dims& d) { return d.rows <= 4 && d.Is > 0; }
-
-// Items in flight per wave: the largest of 4, 2, 1 (3, 2, 1 for MXFP4 items)
-// that divides the wave's items.
-static int ring_depth(int nk) { return nk % 4 == 0 ? 4 : (nk % 2 == 0 ? 2 : 1); }
-static int ring_depth4(int ni) { return ni % 3 == 0 ? 3 : (ni % 2 == 0 ? 2 : 1); }
 
 // K parts of the up/gate slabs: the largest of 4, 2, 1 dividing H/128, or
 // H/256 when routed experts are MXFP4 (their items are two K blocks).
@@ -510,94 +24,57 @@ int upgate_k_parts(int hidden, int routed_fmt) {
 }
 
 template <int RF, int P, int P4>
-static void launch_one(dim3 grid, int base, const Weights& w, const Ws& ws, const Dims& d,
+static void launch_one(dim3 grid, const Weights& w, const Ws& ws, const Dims& d,
                        hipStream_t stream) {
   if constexpr (RF == kFmtFp8) {  // bf16 activations: FP8 routed experts only
     if (d.act_bf16) {
       hipLaunchKernelGGL((moe_upgate_kernel<RF, P, P4, true>), grid, dim3(256), 0, stream, w, ws,
-                         d, base);
+                         d);
       return;
     }
   }
-  hipLaunchKernelGGL((moe_upgate_kernel<RF, P, P4, false>), grid, dim3(256), 0, stream, w, ws, d,
-                     base);
+  hipLaunchKernelGGL((moe_upgate_kernel<RF, P, P4, false>), grid, dim3(256), 0, stream, w, ws, d);
 }
 
 template <int RF, int P>
-static void launch_p4(int p4, dim3 grid, int base, const Weights& w, const Ws& ws,
+static void launch_p4(int p4, dim3 grid, const Weights& w, const Ws& ws,
                       const Dims& d, hipStream_t stream) {
   switch (p4) {
-    case 3: launch_one<RF, P, 3>(grid, base, w, ws, d, stream); break;
-    case 2: launch_one<RF, P, 2>(grid, base, w, ws, d, stream); break;
-    default: launch_one<RF, P, 1>(grid, base, w, ws, d, stream); break;
+    case 3: launch_one<RF, P, 3>(grid, w, ws, d, stream); break;
+    case 2: launch_one<RF, P, 2>(grid, w, ws, d, stream); break;
+    default: launch_one<RF, P, 1>(grid, w, ws, d, stream); break;
   }
 }
 
 hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& ws,
                          const Dims& d, hipStream_t stream) {
   const int br = 16 * (4 / d.ks);
-  const int nb_sh = d.Is / br, base = shared_with_route(d) ? nb_sh : 0;
-  const dim3 grid(nb_sh - base + max_groups * (d.I / br));
+  const dim3 grid(d.Is / br + max_groups * (d.I / br));
   const int p = ring_depth(d.H / 128 / d.ks);
   if (rfmt == kFmtFp8) {
     switch (p) {
-      case 4: launch_one<kFmtFp8, 4, 1>(grid, base, w, ws, d, stream); break;
-      case 2: launch_one<kFmtFp8, 2, 1>(grid, base, w, ws, d, stream); break;
-      default: launch_one<kFmtFp8, 1, 1>(grid, base, w, ws, d, stream); break;
+      case 4: launch_one<kFmtFp8, 4, 1>(grid, w, ws, d, stream); break;
+      case 2: launch_one<kFmtFp8, 2, 1>(grid, w, ws, d, stream); break;
+      default: launch_one<kFmtFp8, 1, 1>(grid, w, ws, d, stream); break;
     }
   } else if (rfmt == kFmtMxfp4) {
     const int p4 = ring_depth4(d.H / 256 / d.ks);
     switch (p) {
-      case 4: launch_p4<kFmtMxfp4, 4>(p4, grid, base, w, ws, d, stream); break;
-      case 2: launch_p4<kFmtMxfp4, 2>(p4, grid, base, w, ws, d, stream); break;
-      default: launch_p4<kFmtMxfp4, 1>(p4, grid, base, w, ws, d, stream); break;
+      case 4: launch_p4<kFmtMxfp4, 4>(p4, grid, w, ws, d, stream); break;
+      case 2: launch_p4<kFmtMxfp4, 2>(p4, grid, w, ws, d, stream); break;
+      default: launch_p4<kFmtMxfp4, 1>(p4, grid, w, ws, d, stream); break;
     }
   } else if (rfmt == kFmtQ1) {
     // 1-bit items (4 groups) in flight: the largest of 3, 2, 1 dividing a part's items
     const int pq = ring_depth4(d.H / 512 / d.ks);
     switch (p) {
-      case 4: launch_p4<kFmtQ1, 4>(pq, grid, base, w, ws, d, stream); break;
-      case 2: launch_p4<kFmtQ1, 2>(pq, grid, base, w, ws, d, stream); break;
-      default: launch_p4<kFmtQ1, 1>(pq, grid, base, w, ws, d, stream); break;
+      case 4: launch_p4<kFmtQ1, 4>(pq, grid, w, ws, d, stream); break;
+      case 2: launch_p4<kFmtQ1, 2>(pq, grid, w, ws, d, stream); break;
+      default: launch_p4<kFmtQ1, 1>(pq, grid, w, ws, d, stream); break;
     }
   } else {
     return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-template <int KPL>
-static void launch_route_k(int p, const Weights& w, const Ws& ws, const Dims& d,
-                           hipStream_t stream) {
-  if (!shared_with_route(d)) {
-    hipLaunchKernelGGL((moe_route_only_kernel<KPL>), dim3(1), dim3(512), 0, stream, ws, d);
-    return;
-  }
-  const dim3 grid(1 + d.Is / (16 * (4 / d.ks)));
-  if (d.act_bf16) {
-    switch (p) {
-      case 4: hipLaunchKernelGGL((moe_route_kernel<KPL, 4, true>), grid, dim3(256), 0, stream, w, ws, d); break;
-      case 2: hipLaunchKernelGGL((moe_route_kernel<KPL, 2, true>), grid, dim3(256), 0, stream, w, ws, d); break;
-      default: hipLaunchKernelGGL((moe_route_kernel<KPL, 1, true>), grid, dim3(256), 0, stream, w, ws, d); break;
-    }
-    return;
-  }
-  switch (p) {
-    case 4: hipLaunchKernelGGL((moe_route_kernel<KPL, 4, false>), grid, dim3(256), 0, stream, w, ws, d); break;
-    case 2: hipLaunchKernelGGL((moe_route_kernel<KPL, 2, false>), grid, dim3(256), 0, stream, w, ws, d); break;
-    default: hipLaunchKernelGGL((moe_route_kernel<KPL, 1, false>), grid, dim3(256), 0, stream, w, ws, d); break;
-  }
-}
-
-hipError_t launch_route(const Weights& w, const Ws& ws, const Dims& d, hipStream_t stream) {
-  const int p = ring_depth(d.H / 128 / d.ks);
-  // key slots per lane of the top-8: 4, 8 or 16 (E <= 256, 512, 1024)
-  if (d.E <= 256)
-    launch_route_k<4>(p, w, ws, d, stream);
-  else if (d.E <= 512)
-    launch_route_k<8>(p, w, ws, d, stream);
-  else
-    launch_route_k<16>(p, w, ws, d, stream);
   return hipGetLastError();
 }
 

@@ -209,14 +209,16 @@ moe_status moe_decode_debug_view(const moe_decode_ctx* ctx, moe_decode_debug* vi
  * records events[0] before its first kernel and events[i+1] after kernel i
  * (MOE_DECODE_N_KERNELS kernels), on the step's stream.  The caller owns the
  * events (hipEventCreate) and must keep them alive; pass NULL to stop. */
-#define MOE_DECODE_N_KERNELS 5 /* router, routing (+ the shared expert's up/gate up to 4
-                                  rows), up/gate + mid, down, combine */
+#define MOE_DECODE_N_KERNELS 5 /* router, routing (with the up/gate of the shared and the
+                                  routed experts + mid), up/gate + mid (an empty span when
+                                  the routing launch ran it), down, combine */
 moe_status moe_decode_set_timing(moe_decode_ctx* ctx, hipEvent_t* events);
 
 /* Kernel timing without per-kernel events: enqueues `reps` more launches of
  * one kernel of the last step enqueued on this context (the up/gate or the
- * down GEMV), with that step's row count, routing table and activations in the
- * workspace, and the weights `w` -- which must hold the same experts at
+ * down GEMV), with that step's row count, router logits, routing table and
+ * activations in the workspace, and the weights `w` -- which must hold the
+ * same experts at
  * possibly other addresses, e.g. another copy of the layer, so that repeated
  * launches stream from HBM rather than from a cache.  The relaunched kernel
  * rewrites the same workspace values (mid, or the down outputs); the step's
@@ -224,10 +226,31 @@ moe_status moe_decode_set_timing(moe_decode_ctx* ctx, hipEvent_t* events);
  * launches with its own events).
  * Returns MOE_ERR_INVALID_ARG without a previous step, for another kernel, for
  * reps < 0 or for weights that step validation rejects. */
+/* MOE_DECODE_K_UPGATE relaunches the launch that ran the step's up/gate: the
+ * routing launch, routing included, when the up/gate runs in it. */
 #define MOE_DECODE_K_UPGATE 2
 #define MOE_DECODE_K_DOWN 3
 moe_status moe_decode_relaunch(moe_decode_ctx* ctx, int32_t kernel,
                                const moe_decode_weights* w, int32_t reps, hipStream_t stream);
+
+/* The routing launch's waits (#85 Mod. row 3 and its `poll` section: the
+ * routed experts' weights stream as soon as the routing has chosen them).
+ * In steps of up to 4 rows the up/gate runs in the routing launch, whose
+ * routed up/gate blocks each wait for a record that the routing block
+ * publishes (wider steps run the routing alone and do not wait); a wait gives up after `cap_ticks` of the GPU's
+ * 100 MHz real-time counter (0 restores the default, 10 ms), and a block that
+ * gives up counts itself and skips its work, so that the step's output is then
+ * wrong but every kernel ends.  withhold = 1 makes the routing block publish no
+ * record, so that every routed block gives up: for tests of that path only.
+ * Applies to later steps and relaunches of this context.
+ * Returns MOE_ERR_INVALID_ARG for a null context or withhold not 0 or 1. */
+moe_status moe_decode_set_wait(moe_decode_ctx* ctx, uint32_t cap_ticks, int32_t withhold);
+
+/* The number of routed blocks that gave up waiting, summed over every step and
+ * relaunch of this context's workspace since moe_decode_init (0 when every
+ * routed block got its record).  Reads it on `stream`, after the work enqueued
+ * there, and synchronizes that stream. */
+moe_status moe_decode_wait_timeouts(moe_decode_ctx* ctx, uint32_t* count, hipStream_t stream);
 
 void moe_decode_destroy(moe_decode_ctx* ctx);
 

@@ -14,7 +14,8 @@ def test_library_exports_every_declared_function():
     assert set(names) >= {"moe_decode_init", "moe_decode_step", "lowbit_gemv",
                           "moe_decode_workspace_size", "moe_decode_debug_view",
                           "moe_decode_destroy", "moe_status_string", "moe_decode_set_timing",
-                          "moe_decode_relaunch"}
+                          "moe_decode_relaunch", "moe_decode_set_wait",
+                          "moe_decode_wait_timeouts"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -84,6 +85,9 @@ def test_step_without_context():
     w = B.Weights()
     assert B.lib().moe_decode_step(None, None, 1, ctypes.byref(w), None, None) == B.MOE_ERR_INVALID_ARG
     assert B.lib().moe_decode_debug_view(None, None) == B.MOE_ERR_INVALID_ARG
+    assert B.lib().moe_decode_set_wait(None, 0, 0) == B.MOE_ERR_INVALID_ARG
+    n = ctypes.c_uint32()
+    assert B.lib().moe_decode_wait_timeouts(None, ctypes.byref(n), None) == B.MOE_ERR_INVALID_ARG
     B.lib().moe_decode_destroy(None)
 
 

@@ -50,6 +50,7 @@ def _run(layer, x, max_rows=None, flags=0, cache=None, check_mid_codes=True, act
     ref_out, ref = P.oracle_for(layer, x, gpu["logits"], nthreads=NTHREADS, host_cache=cache,
                                 act_fmt=act_fmt)
     rep = P.compare(layer, x, gpu, out, ref_out, ref, check_mid_codes=check_mid_codes)
+    assert runner.ctx.wait_timeouts() == 0  # every routed block got its record
     return runner, out, gpu, rep
 
 
@@ -295,3 +296,4 @@ def test_relaunch_rewrites_the_same_values(tiny):
     assert runner.ctx.relaunch_status(B.K_UPGATE, wc, 0) == B.MOE_OK
     out2 = runner.run(x)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert runner.ctx.wait_timeouts() == 0
