@@ -7,12 +7,11 @@
 // experts of the step are numbered by first use in slot-major order (slot j of
 // every row before slot j + 1), the owner of a group being that first use.
 //
-// Top-8 by radix select: with lane l holding experts l, l + 64, ... as order
-// keys, the 8th largest key T is built bit by bit from the top, keeping a bit
-// when at least 8 keys are >= the candidate (one ballot per key slot); it
-// stops early once exactly 8 keys reach the candidate.  The picks are the keys
-// above T plus, when several keys equal T, the lowest IDs among them; their
-// order comes from ranking the 8 against each other.
+// Top-8 in 8 rounds on one wave: lane l holds experts l, l + 64, ... as order
+// keys; a round takes the wave's largest remaining key (DPP max) and, among
+// the slots holding it, the lowest expert ID, then clears that slot, so the
+// picks come out in top-8 order.  (A radix select of the 8th largest key, 32
+// ballot rounds, then ranking the 8 picks, took about three times as long.)
 #pragma once
 #include "device_common.h"
 
@@ -31,8 +30,6 @@ __device__ __forceinline__ float topk_vkey_value(uint32_t k) {
 }
 
 struct RouteSmem {
-  uint32_t ckey[kMaxRows][8];  // a row's 8 picks, unordered
-  int cid[kMaxRows][8];
   int ids[kMaxRows][8];        // picks in top-8 order
   float zsel[kMaxRows][8];
   int g_expert[64];
@@ -73,67 +70,34 @@ __device__ __forceinline__ void load_keys(const float* z, int E, int lane, uint3
   }
 }
 
-// The 8 largest of a row's order keys (load_keys), unordered, with their
-// expert IDs: written to ckey[0 .. 8) and cid[0 .. 8) by the lanes that hold
-// them.  Runs with one full wave.
+// The 8 largest of a row's order keys (load_keys) in top-8 order, equal keys
+// by increasing expert ID, as wave-uniform values okey[j], oid[j].  Runs with
+// one full wave; clears the picked slots of `key` (key 0 is below every
+// logit's key, and E >= 16 leaves 8 real keys).
 template <int KPL>
-__device__ __forceinline__ void select8(const uint32_t* key, int lane, uint32_t* ckey, int* cid) {
-
-  // T: the largest t with at least 8 keys >= t (E >= 16 real keys, all >= 1)
-  uint32_t t = 0;
-  int nge = 0;
-  for (int b = 31; b >= 0; b--) {
-    const uint32_t c = t | (1u << b);
-    int cnt = 0;
+__device__ __forceinline__ void top8_sorted(uint32_t* key, int lane, uint32_t* okey, int* oid) {
 #pragma unroll
-    for (int i = 0; i < KPL; i++) cnt += __popcll(__ballot(key[i] >= c));
-    if (cnt >= 8) {
-      t = c;
-      nge = cnt;
-      if (cnt == 8) break;
+  for (int j = 0; j < 8; j++) {
+    uint32_t m = key[0];
+#pragma unroll
+    for (int i = 1; i < KPL; i++) m = max(m, key[i]);
+    const uint32_t M = dpp_umax(m);
+    // the lowest expert ID holding M: the lowest slot, then the lowest lane
+    int id = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; i++) {
+      const uint64_t b = __ballot(key[i] == M);
+      if (b) {
+        id = kWave * i + (int)__builtin_ctzll(b);
+        break;
+      }
     }
-  }
-  // picks: keys above T, then ties at T by increasing expert ID
-  int need = 8;
-  if (nge > 8) {
-    int ngt = 0;
 #pragma unroll
-    for (int i = 0; i < KPL; i++) ngt += __popcll(__ballot(key[i] > t));
-    need = 8 - ngt;
+    for (int i = 0; i < KPL; i++)
+      if (kWave * i + lane == id) key[i] = 0u;
+    okey[j] = M;
+    oid[j] = id;
   }
-  int ties = 0, base = 0;
-#pragma unroll
-  for (int i = 0; i < KPL; i++) {
-    bool take;
-    if (nge == 8) {
-      take = key[i] >= t;
-    } else {
-      const uint64_t tb = __ballot(key[i] == t);
-      take = key[i] > t || (key[i] == t && ties + lanes_below(tb) < need);
-      ties += __popcll(tb);
-    }
-    const uint64_t sb = __ballot(take);
-    if (take) {
-      const int pos = base + lanes_below(sb);
-      ckey[pos] = key[i];
-      cid[pos] = lane + kWave * i;
-    }
-    base += __popcll(sb);
-  }
-}
-
-// Rank of pick j among a row's 8 picks (unordered keys and IDs): the picks
-// with a larger key, or an equal key and a lower ID.
-__device__ __forceinline__ int rank8(const uint32_t* ckey, const int* cid, int j) {
-  const uint32_t k = ckey[j];
-  const int id = cid[j];
-  int rank = 0;
-#pragma unroll
-  for (int m = 0; m < 8; m++) {
-    const uint32_t km = ckey[m];
-    rank += (km > k || (km == k && cid[m] < id)) ? 1 : 0;
-  }
-  return rank;
 }
 
 // Gates of row r: softmax of its 8 picked logits in pick order (zsel), one
@@ -153,6 +117,15 @@ __device__ __forceinline__ void publish_gates(const Ws& ws, int r, const float* 
   }
 }
 
+// Wave 0 of the routing launch's block 0, once row 0's logits are loaded:
+// publishes the go records 0 .. go - 1 of the launch's shared-expert blocks.
+__device__ __forceinline__ void publish_go(const Ws& ws, int go, int lane) {
+  // the logits loads have returned (the wait), so the stores come after them
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int i = lane; i < go; i += kWave)
+    __hip_atomic_store(ws.blk_rec + i, (uint64_t)1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Runs with every thread of the block (it contains block barriers).  Fills
 // `rs` for rows 0..d.rows-1; when `publish`, also writes ids, gates and the
 // group table to the workspace.  KPL = key slots per lane, ceil(E / 64).
@@ -169,29 +142,21 @@ __device__ __forceinline__ void route_block(const Ws& ws, const Dims& d, RouteSm
   for (int r = wv; r < R; r += nw) {
     uint32_t key[KPL];
     load_keys<KPL>(ws.logits + (size_t)r * E, E, lane, key);
-    if (go > 0 && r == 0) {
-      // the logits loads have returned (the wait), so the stores come after them
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      for (int i = lane; i < go; i += kWave)
-        __hip_atomic_store(ws.blk_rec + i, (uint64_t)1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-    select8<KPL>(key, lane, rs.ckey[r], rs.cid[r]);
+    if (go > 0 && r == 0) publish_go(ws, go, lane);
+    uint32_t okey[8];
+    int oid[8];
+    top8_sorted<KPL>(key, lane, okey, oid);
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      if (lane == j) {
+        rs.ids[r][j] = oid[j];
+        rs.zsel[r][j] = topk_vkey_value(okey[j]);
+      }
   }
   if (tid < 64) {
     rs.g_mask[tid] = 0u;
 #pragma unroll
     for (int r = 0; r < 8; r++) rs.g_slot[tid][r] = 0xFF;
-  }
-  __syncthreads();
-
-  // order the 8 picks of each row: rank = picks with a larger key, or an equal
-  // key and a lower ID
-  if (tid < 8 * R) {
-    const int r = tid >> 3, j = tid & 7;
-    const int rank = rank8(rs.ckey[r], rs.cid[r], j);
-    rs.ids[r][rank] = rs.cid[r][j];
-    rs.zsel[r][rank] = topk_vkey_value(rs.ckey[r][j]);
   }
   __syncthreads();
 
