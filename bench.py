@@ -17,7 +17,8 @@ another step's weights in the 256 MB MALL or the L2s; a pool of 16 token rows
 varies the routing.
 
 One step = one moe_decode_step call: router, routing (up to 4 rows with the
-shared expert's up/gate beside it), up/gate (with mid), down (with the mid
+up/gate of the shared and the routed experts, with mid, in the same launch;
+else the routing alone, then the up/gate launch), down (with the mid
 quantisation) and combine kernels.  Value =
 algorithmic bytes of the step (each distinct expert counted once, read from
 the step's own dedup table, plus the shared expert, router, gamma, x and out)
@@ -28,9 +29,12 @@ trials of 50 steps.  Context figures: the step with one weight copy reused
 (hot), torch's copy of 2 GiB (read + write), lowbit_gemv against its VALU floor (one
 lane-op per weight), and the oracle on one thread with the host CPU model.  A second pass over
 the same steps has the library record HIP events around each kernel on the
-step's stream.  The roofline figure is the dominant kernel's (up/gate)
-algorithmic bytes over its average launch duration, timed by HIP events
-around 64 back-to-back relaunches of it (moe_decode_relaunch) after one step,
+step's stream.  The roofline figure is the dominant kernel's (the launch
+that runs the up/gate: at 1 row the routing launch, with the routing block
+and the shared and routed up/gate) algorithmic bytes over its average launch
+duration, timed by HIP events around 64 back-to-back relaunches of it
+(moe_decode_relaunch; a relaunched routing launch routes again from the
+step's logits and its routed blocks wait for the new records) after one step,
 each over another weight copy (an event pair per kernel inside a step adds
 about 3-5 us).  The fp64 CPU oracle is timed on the host for a bounded sample of the
 1-row workload.
@@ -52,6 +56,7 @@ VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9  # fp32 lane-ops per second (157.3 TFLOP/s 
 POOL = 16
 GSTEPS = 2 * POOL  # steps per captured graph
 RELAUNCH = 64  # back-to-back launches of one kernel for its average duration
+FUSED_MAX_ROWS = 4  # steps of up to 4 rows run their up/gate in the routing launch
 
 
 def log(*a):
@@ -82,13 +87,20 @@ def step_bytes(layer, rows, d):
 
 
 def upgate_bytes(layer, rows, d):
-    """Algorithmic bytes of one up/gate launch: the D distinct experts' gate
-    and up matrices, the activation codes and scales, and above 4 rows the
-    shared expert's gate and up (up to 4 rows the library runs those beside
-    the routing, in the routing launch)."""
-    H, I, Is = layer.hidden, layer.inter, layer.shared_inter
-    shared = 2 * fp8_matrix_bytes(Is, H) if (Is and rows > 4) else 0
-    return d * 2 * routed_matrix_bytes(layer, I, H) + shared + rows * H + rows * (H // 128) * 4
+    """Algorithmic bytes of the launch that runs the up/gate: the D distinct
+    experts' gate and up matrices, the shared expert's gate and up, the
+    activation codes and scales, and up to 4 rows (the routing launch) the
+    router logits the routing block reads."""
+    H, I, E, Is = layer.hidden, layer.inter, layer.n_experts, layer.shared_inter
+    shared = 2 * fp8_matrix_bytes(Is, H) if Is else 0
+    logits = rows * E * 4 if rows <= FUSED_MAX_ROWS else 0
+    return (d * 2 * routed_matrix_bytes(layer, I, H) + shared + rows * H
+            + rows * (H // 128) * 4 + logits)
+
+
+def upgate_launch_us(kernel_us, rows):
+    """In-step event span of the launch that runs the up/gate."""
+    return kernel_us["route"] if rows <= FUSED_MAX_ROWS else kernel_us["upgate"]
 
 
 def layer_copies(S, base, n):
@@ -108,17 +120,22 @@ def layer_copies(S, base, n):
     return copies
 
 
+# the sources of the routing launch's code (the counter record's hash)
+TRAFFIC_SOURCES = ("route.hip", "route.h", "upgate.h", "device_common.h")
+
+
 def measured_traffic():
-    """HBM bytes per up/gate launch at one row from the committed counter
-    record, or None when the kernel source changed since it was taken."""
+    """HBM bytes per routing launch (routing + up/gate) at one row from the
+    committed counter record, or None when the kernel source changed since it
+    was taken."""
     import hashlib
-    rec = os.path.join(ROOT, "profiles", "moe_upgate_glm_rows1_traffic.json")
+    rec = os.path.join(ROOT, "profiles", "moe_route_upgate_glm_rows1_traffic.json")
     if not os.path.exists(rec):
         return None
     with open(rec) as f:
         r = json.load(f)
     h = hashlib.sha256()
-    for name in ("upgate.hip", "device_common.h"):
+    for name in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, "bit_moe_decode_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return int(r["traffic_bytes"]) if h.hexdigest() == r["source_sha256"] else None
@@ -261,7 +278,7 @@ def time_rows(torch, B, S, layer, copies, rows, steps, warmup, seed_base, mode="
     ug_bytes = sum(upgate_bytes(layer, rows, dvals[i % POOL]) for i in range(steps)) / steps
     gbs = nbytes / (ms * 1e-3) / 1e9
     kernel_us = {name: kern[k] * 1e3 for k, name in enumerate(B.KERNEL_NAMES)}
-    ug_gbs = ug_bytes / (kernel_us["upgate"] * 1e-6) / 1e9
+    ug_gbs = ug_bytes / (upgate_launch_us(kernel_us, rows) * 1e-6) / 1e9
     gd = sum(dvals[i % POOL] for i in range(GSTEPS)) / GSTEPS
     gbytes = sum(step_bytes(layer, rows, dvals[i % POOL]) for i in range(GSTEPS)) / GSTEPS
     graph = dict(us_per_step=graph_ms * 1e3, gbs=gbytes / (graph_ms * 1e-3) / 1e9,
@@ -523,6 +540,9 @@ def main():
     ap.add_argument("--no-tp-share", action="store_true")
     ap.add_argument("--no-tiny", action="store_true")
     ap.add_argument("--no-q1", action="store_true")
+    ap.add_argument("--counter-calibration", action="store_true",
+                    help="also run torch's elementwise abs over 12,582,912 fp32 (50,331,648 B "
+                         "read and written): the reference dispatch that scales HBM counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the decode step has no multi-GPU path in this "
@@ -536,6 +556,11 @@ def main():
 
     B.lib()
     torch.cuda.set_device(0)
+    if args.counter_calibration:
+        a = torch.randn(12582912, device="cuda")
+        torch.abs(a)
+        torch.cuda.synchronize()
+        del a
     log("generating GLM-scale layer")
     base = S.make_layer("glm", seed=1001, device="cuda")
     copies = layer_copies(S, base, args.copies)
@@ -704,7 +729,9 @@ def main():
                                "expert of 2048, FP8 E4M3 weights with 128x128 fp32 scales, "
                                "FP8 activations and mid, bf16 in/out",
                    "rows": main_rows, "layer_copies": ncopies, "x_pool": POOL},
-        "roofline": {"bound": "hbm", "kernel": "moe_upgate_kernel",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("moe_route_kernel (routing block + shared and routed up/gate)"
+                                if main_rows <= FUSED_MAX_ROWS else "moe_upgate_kernel"),
                      "achieved": round(m["upgate_alone_bytes"] / (m["alone_us"]["upgate"] * 1e-6) / 1e9, 1),
                      "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(m["upgate_alone_bytes"] / (m["alone_us"]["upgate"] * 1e-6) / 1e9
@@ -712,7 +739,8 @@ def main():
                      "bytes_per_launch": int(m["upgate_alone_bytes"]),
                      "us_per_launch": round(m["alone_us"]["upgate"], 2),
                      "launches_timed": RELAUNCH,
-                     "us_per_launch_in_step_events": round(m["kernel_us"]["upgate"], 2),
+                     "us_per_launch_in_step_events": round(upgate_launch_us(m["kernel_us"],
+                                                                            main_rows), 2),
                      "traffic": measured_traffic() if main_rows == 1 else None},
         "cpu_baseline": cpu,
         "oracle_check_out_err_rel_max": err,
