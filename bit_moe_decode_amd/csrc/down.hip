@@ -32,9 +32,11 @@
 //
 // MXFP4 routed experts (mid kept in fp32, as the oracle does): the block
 // splits its columns' mid into bf16 hi + lo (mid = hi + lo to about 2^-17) in
-// LDS; a wave converts each 32 inputs of E2M1 weights (one E8M0 block) to bf16
-// with the hardware's scaled conversion and runs two 16x16x32 bf16 MFMAs, one
-// against hi and one against lo, accumulating in fp32.  From 6 rows a wave
+// LDS; a wave streams its rows in whole 128-byte lines (256 inputs; half
+// lines when I % 256 != 0), converts each lane's 8 E2M1 weights of an MFMA
+// step to bf16 with the hardware's scaled conversion (the lane's E8M0 as the
+// scale) and runs two 16x16x32 bf16 MFMAs, one against hi and one against
+// lo, accumulating in fp32.  From 3 rows a wave
 // takes two 16-row tiles, so that each LDS read of the mid operand serves
 // both (the block's LDS, 4 bytes per mid element and column, then allows only
 // two or three blocks a CU).
@@ -131,8 +133,9 @@ __host__ __device__ inline size_t dn4_lds_bytes(int rows, int inter) {
 
 // The MXFP4 down GEMV of one wave: output rows h0 .. h0 + 16*T of routed
 // expert e over the whole K, against the block's nrows mid columns (fp32 mid,
-// unquantised, split into bf16 hi + lo in LDS by the block).  Item k = the
-// 128 inputs 128k .. +128 of every row (64 bytes a row): per tile, lane L
+// unquantised, split into bf16 hi + lo in LDS by the block).  This form, for
+// I % 256 != 0, takes half-line items: item k = the 128 inputs 128k .. +128
+// of every row (64 bytes a row): per tile, lane L
 // loads row L/4, 16-byte chunk L%4 (row-contiguous), re-laid through the
 // wave's LDS tile into MFMA operand order; then per 32 inputs (one E8M0
 // block) lane l converts 8 E2M1 of row l%16 to bf16 scaled by 2^(E8M0-127)
@@ -196,6 +199,103 @@ __device__ __forceinline__ void down_fp4_wave(const Weights& w, const Dims& d, i
     }
   };
   // ring of P items (P divides I/128): every issued load is used
+  It st[P];
+#pragma unroll
+  for (int p = 0; p < P; p++) issue(st[p], p);
+  for (int k0 = 0; k0 < nki - P; k0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+      consume(st[p], k0 + p);
+      issue(st[p], k0 + P + p);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; p++) consume(st[p], nki - P + p);
+#pragma unroll
+  for (int t = 0; t < T; t++) {
+    acc[t][0] = c[t][0];
+    acc[t][1] = c[t][1];
+    acc[t][2] = c[t][2];
+    acc[t][3] = c[t][3];
+  }
+}
+
+// The same GEMV with whole-line items (I % 256 == 0), which stream faster
+// than half lines: item k = the 256 inputs 256k .. +256 of every row (a
+// 128-byte line a row).  Per tile, lane L loads rows L/8 and 8 + L/8, 16-byte
+// chunk L%8 (row-contiguous, as the FP8 path), re-laid through the wave's LDS
+// tile; lane l then reads the 16 bytes of row l%16 at 64h + 16(l/16), h = 0, 1:
+// the 32 inputs of E8M0 block 4h + l/16 of the item.  The item's 8 MFMA steps
+// give each lane 8 of those 32 inputs in turn (step 4h + j: inputs 8j .. +8),
+// so the 32 K terms of one step come from four E8M0 blocks, each lane
+// converting its own 8 with its own block's exponent; the mid operand is read
+// at the same K indices, so the sum is the same set of products.
+template <int P, int T>
+__device__ __forceinline__ void down_fp4_wave_line(const Weights& w, const Dims& d, int e,
+                                                   int nrows, int h0, uint8_t* tile,
+                                                   const uint8_t* smid, const float* e8tab,
+                                                   float (*acc)[4]) {
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+  const int H = d.H, I = d.I, nki = I / 256;
+  const size_t rbytes = I / 2, ebytes = I / 32, r8 = 8 * rbytes;
+  const uint8_t* wrow = w.down_c + ((size_t)e * H + h0 + (lane >> 3)) * rbytes + (lane & 7) * 16;
+  const uint8_t* erow =
+      reinterpret_cast<const uint8_t*>(w.down_s) + ((size_t)e * H + h0 + col) * ebytes;
+  const int cc = col < nrows ? col : 0;  // columns past the rows reuse column 0
+  const uint8_t* mh = smid + cc * dn4_col_stride(I) + 64 * g;  // hi at inputs 32g of each 128
+  const uint8_t* ml = mh + 2 * I;                               // lo
+  struct It {
+    u32x4 w0[T], w1[T];
+    uint2 e[T];  // the 8 E8M0 of the lane's MFMA row in the item
+  };
+  auto issue = [&](It& s, int k) {
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+      const uint8_t* p = wrow + (size_t)t * 16 * rbytes + (size_t)k * 128;
+      s.w0[t] = ld_nt16(p);
+      s.w1[t] = ld_nt16(p + r8);
+      s.e[t] = *reinterpret_cast<const uint2*>(erow + (size_t)t * 16 * ebytes + 8 * k);
+    }
+  };
+  v4f c[T];
+#pragma unroll
+  for (int t = 0; t < T; t++) c[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](It& s, int k) {
+    u32x4 a4[T][2];
+#pragma unroll
+    for (int t = 0; t < T; t++) {  // re-lay each tile through the wave's LDS tile
+      tile_put(tile, lane, s.w0[t], s.w1[t]);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+        a4[t][h] = *reinterpret_cast<const u32x4*>(tile + col * kTileStride + 64 * h + 16 * g);
+      asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      float sc[T];
+#pragma unroll
+      for (int t = 0; t < T; t++) sc[t] = e8tab[__builtin_amdgcn_ubfe(h ? s.e[t].y : s.e[t].x, 8 * g, 8)];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int ko = 512 * k + 256 * h + 16 * j;
+        const v8bf bh = *reinterpret_cast<const v8bf*>(mh + ko);
+        const v8bf bl = *reinterpret_cast<const v8bf*>(ml + ko);
+#pragma unroll
+        for (int t = 0; t < T; t++) {
+          const uint32_t q = a4[t][h][j];
+          const v2bf_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc[t], 0);
+          const v2bf_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc[t], 1);
+          const v2bf_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc[t], 2);
+          const v2bf_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc[t], 3);
+          const v8bf a = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          c[t] = mfma_bf16(a, bh, c[t]);
+          c[t] = mfma_bf16(a, bl, c[t]);
+        }
+      }
+    }
+  };
+  // ring of P items (P divides I/256): every issued load is used
   It st[P];
 #pragma unroll
   for (int p = 0; p < P; p++) issue(st[p], p);
@@ -346,7 +446,14 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
     __syncthreads();
     float acc[T4][4];
     const int h0 = (b * WPB + wv) * 16 * T4;
-    down_fp4_wave<P, T4>(w, d, e, nrows, h0, s_tile[wv], dyn, s_e8tab, acc);
+    // whole-line items when I % 256 == 0 (then P, which divides I/128, is
+    // even): P/2 of them hold the bytes of P half-line items (a ring of P
+    // whole-line items measured slower: 8 rows 225.2 -> 229.1 us a step)
+    if (I % 256 == 0)
+      down_fp4_wave_line<(P > 1 ? P / 2 : 1), T4>(w, d, e, nrows, h0, s_tile[wv], dyn, s_e8tab,
+                                                  acc);
+    else
+      down_fp4_wave<P, T4>(w, d, e, nrows, h0, s_tile[wv], dyn, s_e8tab, acc);
 #pragma unroll
     for (int t = 0; t < T4; t++) pin4(acc[t]);
     if (col < nrows) {
@@ -509,9 +616,10 @@ static hipError_t launch_one(int max_groups, size_t lds, const Weights& w, const
 // GLM step at 3, 4, 6 and 8 rows; half the ring with two tiles was between).
 // MXFP4 routed waves take 2 tiles of 16 rows from kDn4TwoTileRows rows up
 // (the mid operand's LDS reads then serve 32 rows), else 1 (more blocks for
-// the few experts of small steps); measured: 2 tiles are faster from 6 rows,
-// slower at 4 and 5.
-constexpr int kDn4TwoTileRows = 6;
+// the few experts of small steps); measured with whole-line items: 2 tiles
+// are faster from 3 rows (4 rows 136.1 -> 132.8, 5 rows 163.3 -> 158.8, 8
+// rows 245.4 -> 225.1 us a step).
+constexpr int kDn4TwoTileRows = 3;
 
 template <int RF, int P>
 static hipError_t launch_wpb(int max_groups, size_t lds, const Weights& w, const Ws& ws,

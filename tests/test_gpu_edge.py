@@ -179,11 +179,11 @@ def _mx_matrix(rng, n, k, base, cls_of_row):
     return packed, e8
 
 
-def _mx_edge_layer(seed):
-    shape = dict(hidden=512, inter=256, n_experts=48, shared_inter=0, router_std=0.02)
+def _mx_edge_layer(seed, inter):
+    shape = dict(hidden=512, inter=inter, n_experts=48, shared_inter=0, router_std=0.02)
     base = S.make_layer(shape, routed_fmt=S.FMT_MXFP4, seed=seed, device="cpu")
     rng = np.random.default_rng(seed)
-    E, H, I = 48, 512, 256
+    E, H, I = 48, 512, inter
     mats = {"gate": [], "up": [], "down": []}
     for e in range(E):
         cg, cu, cd = MX_CLASSES[e % len(MX_CLASSES)]
@@ -195,8 +195,11 @@ def _mx_edge_layer(seed):
     return S.Layer("custom", H, I, E, 0, 1e-6, base.gamma.cuda(), base.router_w.cuda(), routed, None)
 
 
-def test_mxfp4_exponent_range_and_negative_zero_nibbles():
-    layer = _mx_edge_layer(4800)
+# intermediate 256: the down GEMV's whole-line items (I % 256 == 0); 384: its
+# half-line items
+@pytest.mark.parametrize("inter", [256, 384])
+def test_mxfp4_exponent_range_and_negative_zero_nibbles(inter):
+    layer = _mx_edge_layer(4800, inter)
     codes = set()
     for m in (layer.routed.gate, layer.routed.up, layer.routed.down):
         codes |= set(np.unique(m[1].cpu().numpy()).tolist())
@@ -207,7 +210,7 @@ def test_mxfp4_exponent_range_and_negative_zero_nibbles():
     for rows, mode, seed in ((8, "indep", 4900), (8, "corr", 4901), (4, "indep", 4902),
                              (1, "indep", 4903), (8, "indep", 4904)):
         x = S.make_x(rows, 512, seed=seed, mode=mode)
-        _say(f"mxfp4 exponent range rows={rows} mode={mode}")
+        _say(f"mxfp4 exponent range inter={inter} rows={rows} mode={mode}")
         _, gpu, rep = _run(layer, x, cache=cache)
         _say(rep)
         seen |= {int(e) % len(MX_CLASSES) for e in gpu["ids"].ravel()}

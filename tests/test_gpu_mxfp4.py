@@ -53,10 +53,12 @@ def test_tiny_mxfp4_parity(tiny4, rows, mode):
     _say(_run(tiny4, x))
 
 
-@pytest.mark.parametrize("inter", [256, 512, 1024])
+@pytest.mark.parametrize("inter", [256, 384, 512, 1024])
 def test_mxfp4_other_intermediate_sizes(inter):
-    """MXFP4 down rings of 2, 4 and 8 items (I/128 of them) and up/gate items
-    per K part of one and two, with a shared expert, at 1, 3 and 8 rows."""
+    """MXFP4 down waves with whole-line items (256 inputs: rings of 1, 2 and 4
+    items) and with half-line items (128 inputs, I = 384: a ring of 1), and
+    up/gate items per K part of one and two, with a shared expert, at 1, 3
+    and 8 rows."""
     shape = dict(hidden=512, inter=inter, n_experts=32, shared_inter=inter, router_std=0.02)
     layer = S.make_layer(shape, routed_fmt=S.FMT_MXFP4, seed=4200 + inter, device="cuda")
     for rows in (1, 3, 8):
