@@ -65,12 +65,13 @@ template <int KPL, int RF, int P, int P4, bool AB>
 __global__ __launch_bounds__(256) void moe_route_kernel(Weights w, Ws ws, Dims d) {
   __shared__ RouteSmem rs;
   __shared__ __align__(16) UgTiles s_tile;
+  __shared__ __align__(16) uint8_t s_e8[ug_e8_lds<RF>()];
   __shared__ uint64_t s_rec;
   if (blockIdx.x == 0) {
     route_block<KPL>(ws, d, rs, true, shared_blocks(d));
     if (!d.withhold) publish_records(ws, d, rs);
   } else {
-    upgate_block<RF, P, P4, AB, true>(w, ws, d, blockIdx.x - 1, s_tile, &s_rec);
+    upgate_block<RF, P, P4, AB, true>(w, ws, d, blockIdx.x - 1, s_tile, s_e8, &s_rec);
   }
 }
 

@@ -226,10 +226,17 @@ __device__ __forceinline__ void ug_fp8_bf16a(const Weights& w, const Ws& ws, con
 }
 
 // MXFP4 weights: items (pairs of K blocks) it0 .. it0 + ni of the slab.
-template <int P>
+// E8 (ni <= kUgE8Items): the wave's E8M0 bytes (16 rows x ni x 8 per matrix)
+// are loaded once, before its first weight loads, as 8-byte pieces (lane l
+// of round r: piece 64r + l, clamped), and kept in its LDS area se8 as
+// [matrix][row][item] (measured: the per-item E8M0 loads, four 4-byte loads a
+// lane touching 16 rows each, had cost about as much as a tenth of the 8-row
+// step); else each item loads its exponents in the ring.
+constexpr int kUgE8Items = 8;
+template <int P, bool E8>
 __device__ __forceinline__ void ug_fp4(const Weights& w, const Ws& ws, const Dims& d, UgJob j,
                                        int it0, int ni, uint8_t* tg, uint8_t* tu, int lane,
-                                       float* accg, float* accu) {
+                                       float* accg, float* accu, uint8_t* se8) {
   const int H = d.H, nkbh = H / 128;
   const size_t rbytes = H / 2;  // one row of codes
   const size_t ebytes = (size_t)d.I * rbytes, escl = (size_t)d.I * (H / 32);
@@ -250,6 +257,23 @@ __device__ __forceinline__ void ug_fp4(const Weights& w, const Ws& ws, const Dim
   const float* psa = ws.act_s + (size_t)j.row * nkbh + 2 * it0;
   const int sh = 8 * (lane >> 4);  // the lane's byte of each E8M0 word
 
+  // E8: the wave's exponents, 4 rounds of 64 pieces of 8 bytes (32 ni pieces)
+  constexpr int kRounds = kUgE8Items / 2;
+  uint2 ev[E8 ? kRounds : 1];
+  const int npc = 32 * ni;
+  if constexpr (E8) {
+#pragma unroll
+    for (int r = 0; r < kRounds; r++) {
+      int c = r * kWave + lane;
+      c = c < npc ? c : npc - 1;
+      const int m = c >= 16 * ni, rem = c - m * 16 * ni, row = rem / ni, k = rem - row * ni;
+      ev[r] = *reinterpret_cast<const uint2*>((m ? eu : eg) + (size_t)(j.n0 + row) * (H / 32) +
+                                              (size_t)(it0 + k) * 8);
+    }
+    asm volatile("" ::: "memory");  // keep them ahead of the ring's loads
+  }
+  const uint8_t* pe = se8 + (size_t)(lane & 15) * ni * 8;  // row l%16 of gate; up at +16 ni * 8
+
   auto issue = [&](UgStage4& st, int k) {
     const size_t o = (size_t)k * 128;
     st.g0 = ld_nt16(pg + o);
@@ -261,22 +285,33 @@ __device__ __forceinline__ void ug_fp4(const Weights& w, const Ws& ws, const Dim
     st.a1 = ld16(pa + oa + 64);
     st.a2 = ld16(pa + oa + 128);
     st.a3 = ld16(pa + oa + 192);
-    st.eg0 = *reinterpret_cast<const uint32_t*>(peg + 8 * k);
-    st.eg1 = *reinterpret_cast<const uint32_t*>(peg + 8 * k + 4);
-    st.eu0 = *reinterpret_cast<const uint32_t*>(peu + 8 * k);
-    st.eu1 = *reinterpret_cast<const uint32_t*>(peu + 8 * k + 4);
+    if constexpr (!E8) {
+      st.eg0 = *reinterpret_cast<const uint32_t*>(peg + 8 * k);
+      st.eg1 = *reinterpret_cast<const uint32_t*>(peg + 8 * k + 4);
+      st.eu0 = *reinterpret_cast<const uint32_t*>(peu + 8 * k);
+      st.eu1 = *reinterpret_cast<const uint32_t*>(peu + 8 * k + 4);
+    }
     st.sa0 = psa[2 * k];
     st.sa1 = psa[2 * k + 1];
   };
-  auto consume = [&](UgStage4& st) {
+  auto consume = [&](UgStage4& st, int k) {
     tile_put(tg, lane, st.g0, st.g1);
     tile_put(tu, lane, st.u0, st.u1);
     asm volatile("" ::: "memory");
+    uint32_t eg0 = st.eg0, eg1 = st.eg1, eu0 = st.eu0, eu1 = st.eu1;
+    if constexpr (E8) {
+      const uint2 vg = *reinterpret_cast<const uint2*>(pe + 8 * k);
+      const uint2 vu = *reinterpret_cast<const uint2*>(pe + 16 * ni * 8 + 8 * k);
+      eg0 = vg.x;
+      eg1 = vg.y;
+      eu0 = vu.x;
+      eu1 = vu.y;
+    }
     const v8i b0 = cat8(st.a0, st.a1), b1 = cat8(st.a2, st.a3);
-    const v4f cg0 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tg, lane, 0)), b0, (st.eg0 >> sh) & 0xFF);
-    const v4f cu0 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tu, lane, 0)), b0, (st.eu0 >> sh) & 0xFF);
-    const v4f cg1 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tg, lane, 1)), b1, (st.eg1 >> sh) & 0xFF);
-    const v4f cu1 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tu, lane, 1)), b1, (st.eu1 >> sh) & 0xFF);
+    const v4f cg0 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tg, lane, 0)), b0, (eg0 >> sh) & 0xFF);
+    const v4f cu0 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tu, lane, 0)), b0, (eu0 >> sh) & 0xFF);
+    const v4f cg1 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tg, lane, 1)), b1, (eg1 >> sh) & 0xFF);
+    const v4f cu1 = mfma_fp4_fp8(fp4_operand(tile_get_fp4(tu, lane, 1)), b1, (eu1 >> sh) & 0xFF);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int v = 0; v < 4; v++) {
@@ -288,15 +323,23 @@ __device__ __forceinline__ void ug_fp4(const Weights& w, const Ws& ws, const Dim
   UgStage4 st[P];
 #pragma unroll
   for (int p = 0; p < P; p++) issue(st[p], p);
+  if constexpr (E8) {  // the exponents (loaded before the ring) into the wave's area;
+    // unconditional (pieces past 32 ni land in slots nothing reads), so that
+    // the compiler keeps the loads ahead of the ring instead of sinking one
+    // into a branch with a wait for every load in flight
+#pragma unroll
+    for (int r = 0; r < kRounds; r++)
+      *reinterpret_cast<uint2*>(se8 + (size_t)(r * kWave + lane) * 8) = ev[r];
+  }
   for (int k0 = 0; k0 < ni - P; k0 += P) {
 #pragma unroll
     for (int p = 0; p < P; p++) {
-      consume(st[p]);
+      consume(st[p], k0 + p);
       issue(st[p], k0 + P + p);
     }
   }
 #pragma unroll
-  for (int p = 0; p < P; p++) consume(st[p]);
+  for (int p = 0; p < P; p++) consume(st[p], ni - P + p);
 }
 
 // 1-bit weights (Q1_0_G128): groups kb0 .. kb0 + nk of the slab (nk a
@@ -384,6 +427,10 @@ __device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims
 }
 
 typedef uint8_t UgTiles[4][2][kTileBytes];  // per wave: gate and up weight tiles
+constexpr int kUgE8Bytes = 32 * kUgE8Items * 8;  // per wave: MXFP4 exponents (ug_fp4, E8)
+// LDS of the block's exponent areas (4 waves; a token size for other formats)
+template <int RF>
+constexpr int ug_e8_lds() { return RF == kFmtMxfp4 ? 4 * kUgE8Bytes : 16; }
 
 // Items in flight per wave: the largest of 4, 2, 1 (3, 2, 1 for MXFP4 and
 // 1-bit items) that divides the wave's items.
@@ -432,7 +479,8 @@ __device__ __forceinline__ uint64_t await_record(const Ws& ws, const Dims& d, in
 // group from its record; else the routed blocks read the published table.
 template <int RF, int P, int P4, bool AB, bool WAIT>
 __device__ __forceinline__ void upgate_block(const Weights& w, const Ws& ws, const Dims& d,
-                                             int blk, UgTiles& s_tile, uint64_t* s_rec) {
+                                             int blk, UgTiles& s_tile, uint8_t* s_e8,
+                                             uint64_t* s_rec) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int KS = d.ks;
   const int spb = 4 / KS;  // slabs per block
@@ -482,7 +530,12 @@ __device__ __forceinline__ void upgate_block(const Weights& w, const Ws& ws, con
     ug_fp8_bf16a<P>(w, ws, d, j, kp * nk, nk, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
   } else if (RF == kFmtMxfp4 && e >= 0) {
     const int ni = d.H / 256 / KS;  // items of two K blocks per part
-    ug_fp4<P4>(w, ws, d, j, kp * ni, ni, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
+    if (ni <= kUgE8Items)
+      ug_fp4<P4, true>(w, ws, d, j, kp * ni, ni, s_tile[wv][0], s_tile[wv][1], lane, accg, accu,
+                       s_e8 + wv * kUgE8Bytes);
+    else
+      ug_fp4<P4, false>(w, ws, d, j, kp * ni, ni, s_tile[wv][0], s_tile[wv][1], lane, accg, accu,
+                        s_e8 + wv * kUgE8Bytes);
   } else if (RF == kFmtQ1 && e >= 0) {
     const int nk = d.H / 128 / KS;  // groups per part, a multiple of 4
     ug_q1<P4>(w, ws, d, j, kp * nk, nk, reinterpret_cast<uint32_t*>(s_tile[wv][0]), lane, accg,

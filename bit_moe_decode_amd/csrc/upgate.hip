@@ -9,8 +9,9 @@ namespace moe {
 template <int RF, int P, int P4, bool AB>
 __global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims d) {
   __shared__ __align__(16) UgTiles s_tile;
+  __shared__ __align__(16) uint8_t s_e8[ug_e8_lds<RF>()];
   __shared__ uint64_t s_rec;
-  upgate_block<RF, P, P4, AB, false>(w, ws, d, blockIdx.x, s_tile, &s_rec);
+  upgate_block<RF, P, P4, AB, false>(w, ws, d, blockIdx.x, s_tile, s_e8, &s_rec);
 }
 
 // K parts of the up/gate slabs: the largest of 4, 2, 1 dividing H/128, or
