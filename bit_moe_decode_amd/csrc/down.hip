@@ -230,11 +230,11 @@ __device__ __forceinline__ void down_fp4_wave(const Weights& w, const Dims& d, i
 // so the 32 K terms of one step come from four E8M0 blocks, each lane
 // converting its own 8 with its own block's exponent; the mid operand is read
 // at the same K indices, so the sum is the same set of products.
-template <int P, int T>
+template <int P, int T, typename Pro>
 __device__ __forceinline__ void down_fp4_wave_line(const Weights& w, const Dims& d, int e,
                                                    int nrows, int h0, uint8_t* tile,
                                                    const uint8_t* smid, const float* e8tab,
-                                                   float (*acc)[4]) {
+                                                   float (*acc)[4], Pro pro) {
   const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
   const int H = d.H, I = d.I, nki = I / 256;
   const size_t rbytes = I / 2, ebytes = I / 32, r8 = 8 * rbytes;
@@ -271,11 +271,20 @@ __device__ __forceinline__ void down_fp4_wave_line(const Weights& w, const Dims&
         a4[t][h] = *reinterpret_cast<const u32x4*>(tile + col * kTileStride + 64 * h + 16 * g);
       asm volatile("" ::: "memory");
     }
+    // the item's exponents are used here, not earlier: without this the
+    // compiler hoisted every ring item's extraction to the top of the loop,
+    // which waited for all loads in flight (the ring drained each round)
+    uint2 ev[T];
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+      ev[t] = s.e[t];
+      asm volatile("" : "+v"(ev[t].x), "+v"(ev[t].y));
+    }
 #pragma unroll
     for (int h = 0; h < 2; h++) {
       float sc[T];
 #pragma unroll
-      for (int t = 0; t < T; t++) sc[t] = e8tab[__builtin_amdgcn_ubfe(h ? s.e[t].y : s.e[t].x, 8 * g, 8)];
+      for (int t = 0; t < T; t++) sc[t] = e8tab[__builtin_amdgcn_ubfe(h ? ev[t].y : ev[t].x, 8 * g, 8)];
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const int ko = 512 * k + 256 * h + 16 * j;
@@ -299,6 +308,7 @@ __device__ __forceinline__ void down_fp4_wave_line(const Weights& w, const Dims&
   It st[P];
 #pragma unroll
   for (int p = 0; p < P; p++) issue(st[p], p);
+  pro();  // the block's mid split and barrier, with the first items in flight
   for (int k0 = 0; k0 < nki - P; k0 += P) {
 #pragma unroll
     for (int p = 0; p < P; p++) {
@@ -319,22 +329,25 @@ __device__ __forceinline__ void down_fp4_wave_line(const Weights& w, const Dims&
 
 // The block's mid columns as bf16 hi + lo: hi = bf16(m), lo = bf16(m - hi)
 // (m - hi is exact in fp32), 4 values a thread per pass.
+__device__ __forceinline__ void dn4_store_split(uint8_t* smid, int I, int c, int k, const v4f& m) {
+  uint16_t hi[4], lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    hi[i] = f32_to_bf16(m[i]);
+    lo[i] = f32_to_bf16(m[i] - bf16_to_f32(hi[i]));
+  }
+  uint8_t* p = smid + c * dn4_col_stride(I) + 2 * k;
+  *reinterpret_cast<uint2*>(p) = uint2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
+  *reinterpret_cast<uint2*>(p + 2 * I) =
+      uint2{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
+}
 __device__ __forceinline__ void dn4_split_mid(const Ws& ws, const Dims& d, int nrows,
                                               const DnCols& cols, uint8_t* smid) {
   const int I = d.I, n4 = I / 4;
   for (int t = threadIdx.x; t < nrows * n4; t += blockDim.x) {
     const int c = t / n4, k = 4 * (t - c * n4);
-    const v4f m = *reinterpret_cast<const v4f*>(ws.mid + (size_t)cols.u(c) * d.imax + k);
-    uint16_t hi[4], lo[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      hi[i] = f32_to_bf16(m[i]);
-      lo[i] = f32_to_bf16(m[i] - bf16_to_f32(hi[i]));
-    }
-    uint8_t* p = smid + c * dn4_col_stride(I) + 2 * k;
-    *reinterpret_cast<uint2*>(p) = uint2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
-    *reinterpret_cast<uint2*>(p + 2 * I) =
-        uint2{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
+    dn4_store_split(smid, I, c, k,
+                    *reinterpret_cast<const v4f*>(ws.mid + (size_t)cols.u(c) * d.imax + k));
   }
 }
 
@@ -441,19 +454,55 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
     // MXFP4 routed expert: mid columns split into bf16 hi + lo in LDS while
     // the first weight items are in flight (issued inside down_fp4_wave after
     // the barrier below; the split is short next to the stream)
-    dn4_split_mid(ws, d, nrows, cols, dyn);
-    s_e8tab[tid] = e8m0_scale(tid);  // blockDim.x >= 256 for the MXFP4 path
-    __syncthreads();
     float acc[T4][4];
     const int h0 = (b * WPB + wv) * 16 * T4;
     // whole-line items when I % 256 == 0 (then P, which divides I/128, is
     // even): P/2 of them hold the bytes of P half-line items (a ring of P
     // whole-line items measured slower: 8 rows 225.2 -> 229.1 us a step)
-    if (I % 256 == 0)
+    if (I % 256 == 0) {
+      // a block whose mid is at most 4 x 4 values a thread loads it before
+      // its weight ring and splits it once the ring is out; else it splits
+      // first (loads with a runtime count would make the split wait for the
+      // whole ring)
+      const int n4 = I / 4, tot = nrows * n4;
+      const bool early = tot <= 4 * 256;  // blockDim.x == 256 here
+      v4f mv[4];
+      if (early) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          int t = tid + 256 * i;
+          t = t < tot ? t : tot - 1;
+          const int c = t / n4;
+          mv[i] = *reinterpret_cast<const v4f*>(ws.mid + (size_t)cols.u(c) * d.imax + 4 * (t - c * n4));
+        }
+        asm volatile("" ::: "memory");  // keep them ahead of the weight ring
+      }
+      if (!early) {
+        dn4_split_mid(ws, d, nrows, cols, dyn);
+        s_e8tab[tid] = e8m0_scale(tid);  // blockDim.x >= 256 for the MXFP4 path
+        __syncthreads();
+      }
+      auto pro = [&]() {
+        if (early) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) {  // unconditional: clamped slots rewrite their own value
+            int t = tid + 256 * i;
+            t = t < tot ? t : tot - 1;
+            const int c = t / n4;
+            dn4_store_split(dyn, I, c, 4 * (t - c * n4), mv[i]);
+          }
+          s_e8tab[tid] = e8m0_scale(tid);
+          __syncthreads();
+        }
+      };
       down_fp4_wave_line<(P > 1 ? P / 2 : 1), T4>(w, d, e, nrows, h0, s_tile[wv], dyn, s_e8tab,
-                                                  acc);
-    else
+                                                  acc, pro);
+    } else {
+      dn4_split_mid(ws, d, nrows, cols, dyn);
+      s_e8tab[tid] = e8m0_scale(tid);
+      __syncthreads();
       down_fp4_wave<P, T4>(w, d, e, nrows, h0, s_tile[wv], dyn, s_e8tab, acc);
+    }
 #pragma unroll
     for (int t = 0; t < T4; t++) pin4(acc[t]);
     if (col < nrows) {
