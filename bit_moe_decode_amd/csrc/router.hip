@@ -8,8 +8,8 @@
 // derives the top-8, gates and dedup table from these logits in one block
 // (route.h).
 //
-// Grid E/EB blocks of 16 waves.  A block owns EB experts (1 at one row, else
-// 2) over the whole hidden dimension, so its logits need no partial sums from
+// Grid E/EB blocks of 16 waves.  A block owns EB experts (1) over the whole
+// hidden dimension, so its logits need no partial sums from
 // other blocks: lane (wave w, q = lane/16, s = lane%16) takes columns
 // 8s..8s+7 of the 128-blocks w + 16*(q + 4*it), keeps fp32 dots for its EB
 // experts and every row and the row's sum of x^2; the 16 lanes of a DPP row
@@ -32,9 +32,10 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ v2bf as_bf16x2(uint32_t v) { return __builtin_bit_cast(v2bf, v); }
 
 constexpr int kRtWaves = 16;   // waves per block
-// experts per block: 1 at one row, else 2 (more blocks spread the router's
-// bytes over more CUs; above 4 rows the registers would not hold 4 anyway)
-__host__ __device__ constexpr int router_experts(int rows) { return rows == 1 ? 1 : 2; }
+// experts per block: 1 at every width (E blocks spread the router's bytes
+// over more CUs; against 2 a block from 2 rows up: 4 rows 188.0 -> 187.2,
+// 8 rows 336.5 -> 335.9 us a step, outputs bitwise equal)
+__host__ __device__ constexpr int router_experts(int rows) { return 1 + 0 * rows; }
 
 // Element j (0..7) of eight packed bf16 values.
 __device__ __forceinline__ float bf16_elem(const u32x4& v, int j) {
@@ -102,11 +103,18 @@ __global__ __launch_bounds__(1024) void moe_router_kernel(const uint16_t* __rest
     }
     // The owner of (row, 128-block) quantises it from the 16 lanes that hold
     // it: s = amax/448, q = e4m3(u/s).
-    if (on) {
-#pragma unroll 1
-      for (int r = 0; r < R; r++) {
-        if ((uint32_t)(kb * R + r) % gridDim.x != blockIdx.x) continue;  // uniform over 16 lanes
-        const u32x4 xr = ld16(x + ((uint32_t)r * H + col));  // cache hit
+    // With at least R blocks, the R pairs (row, kb) of a 128-block go to R
+    // different blocks, so this block owns at most one of them: row r with
+    // kb * R + r = blockIdx.x (mod grid).  Its 8 inputs are still in
+    // registers (picked by a select chain: an indexed register array would
+    // go to scratch).
+    const int r = (int)(((uint32_t)blockIdx.x + gridDim.x - ((uint32_t)(kb * R) % gridDim.x)) %
+                        gridDim.x);
+    if (on && r < R) {  // uniform over 16 lanes
+      u32x4 xr = xv[0];
+#pragma unroll
+      for (int i = 1; i < R; i++) xr = i == r ? xv[i] : xr;
+      do {
         if (d.act_bf16) {  // the experts take u itself: store its 8 bf16
           u32x4 ub;
 #pragma unroll
@@ -115,7 +123,7 @@ __global__ __launch_bounds__(1024) void moe_router_kernel(const uint16_t* __rest
                     ((uint32_t)f32_to_bf16(bf16_elem(xr, 2 * p + 1) * bf16_elem(gm, 2 * p + 1))
                      << 16);
           *reinterpret_cast<u32x4*>(ws.act_u + ((uint32_t)r * H + col)) = ub;
-          continue;
+          break;
         }
         float u[8], m = 0.f;
 #pragma unroll
@@ -135,7 +143,7 @@ __global__ __launch_bounds__(1024) void moe_router_kernel(const uint16_t* __rest
         pk.y = c[2] | (c[3] << 16);
         *reinterpret_cast<uint2*>(ws.act_q + ((uint32_t)r * H + col)) = pk;
         if (s == 0) ws.act_s[r * nkb + kb] = sc;
-      }
+      } while (false);
     }
   }
 
