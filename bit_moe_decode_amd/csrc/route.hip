@@ -140,8 +140,8 @@ static hipError_t launch_route_k(int rfmt, const Weights& w, const Ws& ws, const
     case kFmtMxfp4:
       launch_fused_p<KPL, kFmtMxfp4>(p, ring_depth4(d.H / 256 / d.ks), grid, w, ws, d, stream);
       break;
-    case kFmtQ1:
-      launch_fused_p<KPL, kFmtQ1>(p, ring_depth4(d.H / 512 / d.ks), grid, w, ws, d, stream);
+    case kFmtQ1:  // rings of 1 (1-bit) and at most 2 (FP8 shared): see launch_upgate
+      launch_fused_p<KPL, kFmtQ1>(p > 2 ? 2 : p, 1, grid, w, ws, d, stream);
       break;
     default: return hipErrorInvalidValue;
   }

@@ -379,18 +379,30 @@ __device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims
   const uint8_t* base = (m ? w.up_c : w.gate_c) + (size_t)j.e * ebytes;
   const uint32_t* src =
       reinterpret_cast<const uint32_t*>(base + (size_t)(j.n0 + lrow) * rb) + 9 * (kb0 / 2 + lq);
-  const uint8_t* pa = ws.act_q + (size_t)j.row * H + (lane >> 4) * 32 + (size_t)kb0 * 128;
-  const float* psa = ws.act_s + (size_t)j.row * nkbh + kb0;
+  // activation codes and block scales through buffer resources over the
+  // step's rows: lanes of columns past the expert's using rows take offsets
+  // past the range, so their loads return zeros without a memory access
+  // (as in ug_fp4; their MFMA columns are never stored)
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(ws.act_q), (short)0, d.rows * H, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(ws.act_s), (short)0, d.rows * nkbh * 4, 0x00020000);
+  const uint32_t aoff =
+      j.live ? (uint32_t)(j.row * H + (lane >> 4) * 32 + kb0 * 128) : 0x80000000u;
+  const uint32_t soff = j.live ? (uint32_t)((j.row * nkbh + kb0) * 4) : 0x80000000u;
   const uint32_t one = q1_in_vgpr(d.q1k[3]);
 
   auto issue = [&](UgStageQ1& st, int it) {
     ld_nt_chunk36(src + 18 * it, st.w);
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const size_t o = (size_t)(4 * it + q) * 128;
-      st.a[q][0] = ld16(pa + o);
-      st.a[q][1] = ld16(pa + o + 16);
-      st.sa[q] = psa[4 * it + q];
+      const int o = (int)(aoff + (uint32_t)(4 * it + q) * 128);
+      st.a[q][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, o, 0, 0));
+      st.a[q][1] =
+          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, o + 16, 0, 0));
+      st.sa[q] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(soff + (uint32_t)(4 * it + q) * 4),
+                                                      0, 0));
     }
   };
   auto consume = [&](UgStageQ1& st) {

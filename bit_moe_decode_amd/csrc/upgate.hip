@@ -66,9 +66,13 @@ hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& w
       default: launch_p4<kFmtMxfp4, 1>(p4, grid, w, ws, d, stream); break;
     }
   } else if (rfmt == kFmtQ1) {
-    // 1-bit items (4 groups) in flight: the largest of 3, 2, 1 dividing a part's items
-    const int pq = ring_depth4(d.H / 512 / d.ks);
-    switch (p) {
+    // one 1-bit item (4 groups) in flight and at most 2 K blocks of the FP8
+    // shared expert: the 1-bit path gains from more waves, not from deeper
+    // rings (4 waves a SIMD against 2 with rings of 3 and 4: GLM step 238.8 ->
+    // 230.0 us at 8 rows, 145.3 -> 135.2 at 4, 58.1 -> 56.7 at 1, outputs
+    // bitwise equal); longer waves (2 or 1 K parts) were slower (248.0 / 257.0)
+    const int pq = 1;
+    switch (p > 2 ? 2 : p) {
       case 4: launch_p4<kFmtQ1, 4>(pq, grid, w, ws, d, stream); break;
       case 2: launch_p4<kFmtQ1, 2>(pq, grid, w, ws, d, stream); break;
       default: launch_p4<kFmtQ1, 1>(pq, grid, w, ws, d, stream); break;
