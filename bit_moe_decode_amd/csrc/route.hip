@@ -99,11 +99,10 @@ static void launch_fused(dim3 grid, const Weights& w, const Ws& ws, const Dims& 
 template <int KPL, int RF, int P>
 static void launch_fused_p4(int p4, dim3 grid, const Weights& w, const Ws& ws, const Dims& d,
                             hipStream_t stream) {
-  switch (p4) {
-    case 3: launch_fused<KPL, RF, P, 3>(grid, w, ws, d, stream); break;
-    case 2: launch_fused<KPL, RF, P, 2>(grid, w, ws, d, stream); break;
-    default: launch_fused<KPL, RF, P, 1>(grid, w, ws, d, stream); break;
-  }
+  if (p4 == 2)
+    launch_fused<KPL, RF, P, 2>(grid, w, ws, d, stream);
+  else
+    launch_fused<KPL, RF, P, 1>(grid, w, ws, d, stream);
 }
 
 template <int KPL, int RF>
@@ -115,12 +114,11 @@ static void launch_fused_p(int p, int p4, dim3 grid, const Weights& w, const Ws&
       case 2: launch_fused<KPL, RF, 2, 1>(grid, w, ws, d, stream); break;
       default: launch_fused<KPL, RF, 1, 1>(grid, w, ws, d, stream); break;
     }
-  } else {
-    switch (p) {
-      case 4: launch_fused_p4<KPL, RF, 4>(p4, grid, w, ws, d, stream); break;
-      case 2: launch_fused_p4<KPL, RF, 2>(p4, grid, w, ws, d, stream); break;
-      default: launch_fused_p4<KPL, RF, 1>(p4, grid, w, ws, d, stream); break;
-    }
+  } else {  // MXFP4 and 1-bit layers: shared rings of at most 2
+    if (p >= 2)
+      launch_fused_p4<KPL, RF, 2>(p4, grid, w, ws, d, stream);
+    else
+      launch_fused_p4<KPL, RF, 1>(p4, grid, w, ws, d, stream);
   }
 }
 
@@ -137,8 +135,9 @@ static hipError_t launch_route_k(int rfmt, const Weights& w, const Ws& ws, const
   const int p = ring_depth(d.H / 128 / d.ks);
   switch (rfmt) {
     case kFmtFp8: launch_fused_p<KPL, kFmtFp8>(p, 1, grid, w, ws, d, stream); break;
-    case kFmtMxfp4:
-      launch_fused_p<KPL, kFmtMxfp4>(p, ring_depth4(d.H / 256 / d.ks), grid, w, ws, d, stream);
+    case kFmtMxfp4:  // rings of at most 2 (MXFP4 items and FP8 shared): see launch_upgate
+      launch_fused_p<KPL, kFmtMxfp4>(p > 2 ? 2 : p, ring_depth2(d.H / 256 / d.ks), grid, w, ws,
+                                     d, stream);
       break;
     case kFmtQ1:  // rings of 1 (1-bit) and at most 2 (FP8 shared): see launch_upgate
       launch_fused_p<KPL, kFmtQ1>(p > 2 ? 2 : p, 1, grid, w, ws, d, stream);

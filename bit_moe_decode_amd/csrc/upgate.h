@@ -455,10 +455,11 @@ constexpr int kUgE8Bytes = 32 * kUgE8Items * 8;  // per wave: MXFP4 exponents (u
 template <int RF>
 constexpr int ug_e8_lds() { return RF == kFmtMxfp4 ? 4 * kUgE8Bytes : 16; }
 
-// Items in flight per wave: the largest of 4, 2, 1 (3, 2, 1 for MXFP4 and
-// 1-bit items) that divides the wave's items.
+// Items in flight per wave, dividing the wave's items: FP8 K blocks the
+// largest of 4, 2, 1 (ring_depth); in MXFP4 and 1-bit layers, where more
+// waves a SIMD pay more than deeper rings, at most 2 (launch_upgate).
 inline int ring_depth(int nk) { return nk % 4 == 0 ? 4 : (nk % 2 == 0 ? 2 : 1); }
-inline int ring_depth4(int ni) { return ni % 3 == 0 ? 3 : (ni % 2 == 0 ? 2 : 1); }
+inline int ring_depth2(int ni) { return ni % 2 == 0 ? 2 : 1; }
 
 // Up/gate block `rb` of moe_route_kernel waits for its record: lane 0 of wave
 // 0 polls it with relaxed agent-scope loads, a short sleep between them, until

@@ -40,11 +40,10 @@ static void launch_one(dim3 grid, const Weights& w, const Ws& ws, const Dims& d,
 template <int RF, int P>
 static void launch_p4(int p4, dim3 grid, const Weights& w, const Ws& ws,
                       const Dims& d, hipStream_t stream) {
-  switch (p4) {
-    case 3: launch_one<RF, P, 3>(grid, w, ws, d, stream); break;
-    case 2: launch_one<RF, P, 2>(grid, w, ws, d, stream); break;
-    default: launch_one<RF, P, 1>(grid, w, ws, d, stream); break;
-  }
+  if (p4 == 2)
+    launch_one<RF, P, 2>(grid, w, ws, d, stream);
+  else
+    launch_one<RF, P, 1>(grid, w, ws, d, stream);
 }
 
 hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& ws,
@@ -59,24 +58,25 @@ hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& w
       default: launch_one<kFmtFp8, 1, 1>(grid, w, ws, d, stream); break;
     }
   } else if (rfmt == kFmtMxfp4) {
-    const int p4 = ring_depth4(d.H / 256 / d.ks);
-    switch (p) {
-      case 4: launch_p4<kFmtMxfp4, 4>(p4, grid, w, ws, d, stream); break;
-      case 2: launch_p4<kFmtMxfp4, 2>(p4, grid, w, ws, d, stream); break;
-      default: launch_p4<kFmtMxfp4, 1>(p4, grid, w, ws, d, stream); break;
-    }
+    // at most 2 MXFP4 items and 2 FP8 shared K blocks in flight: 164
+    // registers, 3 waves a SIMD against 216 and 2 with rings of 3 and 4 (GLM
+    // step 209.5 -> 202.8 us at 8 rows, 123.5 -> 118.4 at 4, 49.6 -> 48.4 at
+    // 1, outputs bitwise equal; rings of 1 were between)
+    const int p4 = ring_depth2(d.H / 256 / d.ks);
+    if (p >= 2)
+      launch_p4<kFmtMxfp4, 2>(p4, grid, w, ws, d, stream);
+    else
+      launch_p4<kFmtMxfp4, 1>(p4, grid, w, ws, d, stream);
   } else if (rfmt == kFmtQ1) {
     // one 1-bit item (4 groups) in flight and at most 2 K blocks of the FP8
     // shared expert: the 1-bit path gains from more waves, not from deeper
     // rings (4 waves a SIMD against 2 with rings of 3 and 4: GLM step 238.8 ->
     // 230.0 us at 8 rows, 145.3 -> 135.2 at 4, 58.1 -> 56.7 at 1, outputs
     // bitwise equal); longer waves (2 or 1 K parts) were slower (248.0 / 257.0)
-    const int pq = 1;
-    switch (p > 2 ? 2 : p) {
-      case 4: launch_p4<kFmtQ1, 4>(pq, grid, w, ws, d, stream); break;
-      case 2: launch_p4<kFmtQ1, 2>(pq, grid, w, ws, d, stream); break;
-      default: launch_p4<kFmtQ1, 1>(pq, grid, w, ws, d, stream); break;
-    }
+    if (p >= 2)
+      launch_p4<kFmtQ1, 2>(1, grid, w, ws, d, stream);
+    else
+      launch_p4<kFmtQ1, 1>(1, grid, w, ws, d, stream);
   } else {
     return hipErrorInvalidValue;
   }
