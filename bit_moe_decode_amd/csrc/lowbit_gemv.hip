@@ -78,32 +78,45 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_kernel(const uint8_t* __re
 // and thread (row r, part q) adds T[p][nibble] over the 64 nibbles of chunks
 // c0 + q, c0 + q + KP, ... of its row, scales each group's sum by its d and
 // accumulates in fp32: one table read per 4 weights.  The parts of a row are
-// added in part order at the end.  The lanes of a wave read one position's
-// 16 entries at a time (a broadcast or a distinct bank each), and the tables
-// of different parts are offset by 16 floats so that they use different banks.
-constexpr int kLbTab = 64 * 16 + 16;  // floats per chunk table, padded
-// chunks whose tables one round may hold (19 x 4160 bytes: two blocks a CU)
+// added in part order at the end.
+//
+// LDS layout: the tables of the KP parts' m-th chunks are interleaved per
+// position, slot P = 64 m + p holding part q's 16 entries at floats
+// S P + 16 q .. +16 (S = 16 KP + 4: the fill writes one chunk's positions
+// from consecutive lanes, S floats apart, and S mod 64 = 4 or 36 puts the 16
+// lanes of a b128 pass on distinct banks).  A lookup's
+// address is then 4 (16 q + nibble) + 4 S P: the sign dword, masked to its
+// even or odd nibbles with 16 q or'ed into every byte, gives the first term
+// for one byte in one SDWA shift, and 4 S P is the read's immediate offset
+// (so 2 VALU operations per 4 weights: the shift and the add).  The lanes of
+// a wave read one slot's 16 entries at a time (a broadcast or a distinct bank
+// each).  The kernel declares no static LDS, so its dynamic LDS starts at
+// address 0, and tables and part sums are addressed from there.
+template <int KP>
+constexpr int lb_slot() { return 16 * KP + 4; }
+// chunks whose tables one round may hold (KP * M, at most 16 for the M and KP
+// the launcher picks: about 70 KB, two blocks a CU)
 constexpr int kLbRoundChunks = 19;
 
-// Bits o .. o+3 of v as one v_bfe_u32 (the compiler would otherwise split a
-// constant-offset field extract into a shift and a mask).
-template <int O>
-__device__ __forceinline__ uint32_t nib4_at(uint32_t v) {
+typedef __attribute__((address_space(3))) float lds_float;
+__device__ __forceinline__ float lds_ld(uint32_t a) { return *(lds_float*)(uintptr_t)a; }
+__device__ __forceinline__ void lds_st(uint32_t a, float v) { *(lds_float*)(uintptr_t)a = v; }
+
+
+// Byte B of e, times 4 (one v_lshlrev_b32 with an SDWA byte select; the
+// compiler emits a shift and a mask for it otherwise).
+template <int B>
+__device__ __forceinline__ uint32_t byte_x4(uint32_t e) {
   uint32_t r;
-  asm("v_bfe_u32 %0, %1, %2, 4" : "=v"(r) : "v"(v), "n"(O));
+  if constexpr (B == 0)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(e));
+  else if constexpr (B == 1)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(e));
+  else if constexpr (B == 2)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(e));
+  else
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(e));
   return r;
-}
-__device__ __forceinline__ uint32_t nib4(uint32_t v, int o) {
-  switch (o) {
-    case 0: return nib4_at<0>(v);
-    case 4: return nib4_at<4>(v);
-    case 8: return nib4_at<8>(v);
-    case 12: return nib4_at<12>(v);
-    case 16: return nib4_at<16>(v);
-    case 20: return nib4_at<20>(v);
-    case 24: return nib4_at<24>(v);
-    default: return v >> 28;
-  }
 }
 
 __device__ __forceinline__ float lb_f16(uint32_t h) {
@@ -111,10 +124,12 @@ __device__ __forceinline__ float lb_f16(uint32_t h) {
 }
 
 // One chunk (two groups) of a row: w = its 9 dwords (d of group 0, 16 bit
-// bytes, d of group 1, 16 bit bytes), tab = the chunk's 64 positions x 16
-// entries.  Returns acc + d0 * s0 + d1 * s1, s = the sum of the entries of
-// the group's 32 nibbles.
-__device__ __forceinline__ float lb_chunk(const uint32_t* w, const float* tab, float acc) {
+// bytes, d of group 1, 16 bit bytes), the chunk the thread's m-th of the
+// round; pb = 16 q in every byte.  Returns acc + d0 * s0 + d1 * s1, s = the
+// sum of the entries of the group's 32 nibbles.
+template <int KP, int MI>
+__device__ __forceinline__ float lb_chunk(const uint32_t* w, uint32_t pb, float acc) {
+  constexpr uint32_t kSlotB = 4 * lb_slot<KP>();  // bytes per slot
   // the 16 bit-bytes of each group as 4 aligned dwords (group 0 starts 2
   // bytes in)
   uint32_t u[8];
@@ -123,26 +138,52 @@ __device__ __forceinline__ float lb_chunk(const uint32_t* w, const float* tab, f
     u[q] = __builtin_amdgcn_alignbyte(w[q + 1], w[q], 2);
     u[4 + q] = w[5 + q];
   }
-  // nibble t of dword q is the 4 inputs of position 8(q%4) + t of its group;
-  // its entry is float `nibble` of that position's 16
-  const float* tg[2] = {tab, tab + 32 * 16};
+  // nibble t of dword q is the 4 inputs of position 32(q/4) + 8(q%4) + t;
+  // even nibbles are the low halves of the bytes of ev, odd ones of od
+  // two dwords (16 reads) in flight before their sums
   float s[2] = {0.f, 0.f};
 #pragma unroll
-  for (int q = 0; q < 8; q++) {
+  for (int q = 0; q < 8; q += 2) {
+    float v[2][8];
 #pragma unroll
-    for (int t = 0; t < 8; t += 2) {
-      const int pos = 8 * (q & 3) + t;
-      const uint32_t n0 = nib4(u[q], 4 * t), n1 = nib4(u[q], 4 * t + 4);
-      s[q >> 2] += tg[q >> 2][pos * 16 + n0] + tg[q >> 2][pos * 16 + 16 + n1];
+    for (int h = 0; h < 2; h++) {
+      const uint32_t ev = (u[q + h] & 0x0F0F0F0Fu) | pb, od = ((u[q + h] >> 4) & 0x0F0F0F0Fu) | pb;
+      const uint32_t p0 = (uint32_t)(64 * MI + 32 * (q >> 2) + 8 * ((q + h) & 3)) * kSlotB;
+      v[h][0] = lds_ld(byte_x4<0>(ev) + p0);
+      v[h][1] = lds_ld(byte_x4<0>(od) + p0 + kSlotB);
+      v[h][2] = lds_ld(byte_x4<1>(ev) + p0 + 2 * kSlotB);
+      v[h][3] = lds_ld(byte_x4<1>(od) + p0 + 3 * kSlotB);
+      v[h][4] = lds_ld(byte_x4<2>(ev) + p0 + 4 * kSlotB);
+      v[h][5] = lds_ld(byte_x4<2>(od) + p0 + 5 * kSlotB);
+      v[h][6] = lds_ld(byte_x4<3>(ev) + p0 + 6 * kSlotB);
+      v[h][7] = lds_ld(byte_x4<3>(od) + p0 + 7 * kSlotB);
     }
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) s[q >> 2] += v[h][t] + v[h][t + 1];
   }
   acc = fmaf(lb_f16(w[0] & 0xFFFFu), s[0], acc);
   return fmaf(lb_f16(w[4] >> 16), s[1], acc);
 }
 
+// The thread's chunks of a round, the m-th being chunk c + KP m, while below
+// nch.
+template <int KP, int M, int MI = 0>
+__device__ __forceinline__ float lb_chunks(const uint32_t (*w9)[9], uint32_t pb, int c, int nch,
+                                           float acc) {
+  if constexpr (MI < M) {
+    if (c + KP * MI < nch) acc = lb_chunk<KP, MI>(w9[MI], pb, acc);
+    return lb_chunks<KP, M, MI + 1>(w9, pb, c, nch, acc);
+  } else {
+    return acc;
+  }
+}
+
 // The 16 entries of one position, t[v] = sum_{i<4} (bit i of v ? -x : +x)[i],
-// from its 4 bf16 inputs (packed in xv, input 0 in the low half of xv.x).
-__device__ __forceinline__ void lb_fill_pos(float* t, uint2 xv) {
+// from its 4 bf16 inputs (packed in xv, input 0 in the low half of xv.x), to
+// LDS bytes a .. a + 64 (a % 16 == 0) of smem, the kernel's dynamic LDS.
+__device__ __forceinline__ void lb_fill_pos(uint8_t* smem, uint32_t a, uint2 xv) {
   const float x0 = bf16_to_f32((uint16_t)(xv.x & 0xFFFFu)), x1 = bf16_to_f32((uint16_t)(xv.x >> 16));
   const float x2 = bf16_to_f32((uint16_t)(xv.y & 0xFFFFu)), x3 = bf16_to_f32((uint16_t)(xv.y >> 16));
   // bits 0-1 and bits 2-3 of the nibble
@@ -150,29 +191,39 @@ __device__ __forceinline__ void lb_fill_pos(float* t, uint2 xv) {
   const float b[4] = {x2 + x3, -x2 + x3, x2 - x3, -x2 - x3};
 #pragma unroll
   for (int hb = 0; hb < 4; hb++)
-    *reinterpret_cast<float4*>(t + 4 * hb) = float4{a0 + b[hb], a1 + b[hb], a2 + b[hb], a3 + b[hb]};
+    *reinterpret_cast<float4*>(smem + a + 16 * hb) = float4{a0 + b[hb], a1 + b[hb], a2 + b[hb], a3 + b[hb]};
 }
 
+// (its LDS allows 3 blocks a CU, so the compiler may schedule for 3 waves a SIMD)
 template <int RB, int M>
-__global__ __launch_bounds__(256) void lowbit_gemv_q1_nib_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) void lowbit_gemv_q1_nib_kernel(
     const uint8_t* __restrict__ blocks, const uint16_t* __restrict__ x,
     uint16_t* __restrict__ y, int n, int k) {
   constexpr int KP = 256 / RB;
   constexpr int CH = KP * M;  // chunks a round: part q takes q, q + KP, ..
+  constexpr uint32_t kSlotB = 4 * lb_slot<KP>();
+  constexpr uint32_t kRed = 64 * M * kSlotB;  // LDS bytes of the tables; then [KP][RB] sums
   extern __shared__ __align__(16) uint8_t smem[];
-  float* tab = reinterpret_cast<float*>(smem);                    // [CH][kLbTab]
-  float* red = tab + CH * kLbTab;                                  // [KP][RB]
   const int tid = threadIdx.x;
   const int G = k / 128, nch = G / 2, rb = 18 * G;
   const int r0 = blockIdx.x * RB;
   const int nr = n - r0 < RB ? n - r0 : RB;
+  // the lookups address LDS from 0 (immediate offsets), the table fill from
+  // smem: with no static LDS in this kernel they coincide; were they ever to
+  // differ, every output is NaN rather than silently wrong
+  if ((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem != 0u) {
+    if (tid < nr) y[r0 + tid] = 0x7FC0;
+    return;
+  }
 
   const int rl = tid % RB, part = tid / RB;
   const int rowl = rl < nr ? rl : nr - 1;  // threads past n decode the last row
   const uint32_t* myrow = reinterpret_cast<const uint32_t*>(blocks + (size_t)(r0 + rowl) * rb);
+  const uint32_t pb = (uint32_t)(16 * part) * 0x01010101u;
 
-  // table positions of this thread in a round: e = tid + 256 j (j < NE), the
-  // inputs of each loaded one round ahead
+  // table positions of this thread in a round: e = tid + 256 j (j < NE) is
+  // position e % 64 of chunk c0 + e / 64 (part (e / 64) % KP's chunk
+  // (e / 64) / KP), the inputs of each loaded one round ahead
   constexpr int NE = (CH * 64 + 255) / 256;
   uint2 xn[NE];
   auto xload = [&](int c0) {
@@ -200,27 +251,30 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_nib_kernel(
 #pragma unroll
     for (int j = 0; j < NE; j++) {
       const int e = tid + 256 * j;
-      if (e < CH * 64 && c0 + (e >> 6) < nch)
-        lb_fill_pos(tab + (e >> 6) * kLbTab + (e & 63) * 16, xn[j]);
+      if (e < CH * 64 && c0 + (e >> 6) < nch) {
+        const int c = e >> 6;
+        lb_fill_pos(smem, (uint32_t)(64 * (c / KP) + (e & 63)) * kSlotB + 64u * (uint32_t)(c % KP),
+                    xn[j]);
+      }
     }
     if (c0 + CH < nch) xload(c0 + CH);
     __syncthreads();
-#pragma unroll
-    for (int m = 0; m < M; m++)
-      if (c0 + part + KP * m < nch) acc = lb_chunk(w9[m], tab + (part + KP * m) * kLbTab, acc);
+    acc = lb_chunks<KP, M>(w9, pb, c0 + part, nch, acc);
     if (c0 + CH < nch) __syncthreads();
   }
-  red[part * RB + rl] = acc;
+  lds_st(kRed + 4u * (uint32_t)(part * RB + rl), acc);
   __syncthreads();
   if (tid < nr) {
-    float v = red[tid];
+    float v = lds_ld(kRed + 4u * (uint32_t)tid);
 #pragma unroll
-    for (int q = 1; q < KP; q++) v += red[q * RB + tid];
+    for (int q = 1; q < KP; q++) v += lds_ld(kRed + 4u * (uint32_t)(q * RB + tid));
     y[r0 + tid] = f32_to_bf16(v);
   }
 }
 
-static size_t lb_nib_lds(int rbk, int m) { return (size_t)(256 / rbk) * m * kLbTab * 4 + 256 * 4; }
+static size_t lb_nib_lds(int rbk, int m) {
+  return (size_t)64 * m * 4 * (16 * (256 / rbk) + 4) + 256 * 4;  // tables + part sums
+}
 
 template <int RB, int M>
 static hipError_t lb_nib_launch(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int n,
