@@ -53,7 +53,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct Plan {
   int H, I, E, Is, R, imax, groups, ks;
   size_t off_logits, off_rstd, off_ids, off_gates, off_ngroups, off_gexpert,
-      off_gowner, off_gmask, off_gslot, off_grows, off_gnrows, off_actq, off_acts, off_mid,
+      off_gowner, off_gmask, off_gslot, off_grows, off_gnrows, off_actq, off_actqp, off_acts, off_mid,
       off_midq, off_midqs, off_ypart, off_actu, off_blkrec, off_waitto, total;
 };
 
@@ -119,6 +119,7 @@ moe_status plan_config(const moe_decode_config* c, Plan* p) {
   p->off_grows = take(G * 8);
   p->off_gnrows = take(G);
   p->off_actq = take(R * H);
+  p->off_actqp = take(c->routed_fmt == MOE_FMT_Q1_G128 ? R * H : 0);  // 1-bit operand order
   p->off_acts = take(R * (H / 128) * 4);
   const size_t U = R * 9;  // (row, pick) pairs, pick 8 = the shared expert
   p->off_mid = take(U * IM * 4);
@@ -150,6 +151,7 @@ Ws make_view(char* b, const Plan& p) {
   v.grp_rows = reinterpret_cast<uint8_t*>(b + p.off_grows);
   v.grp_nrows = reinterpret_cast<uint8_t*>(b + p.off_gnrows);
   v.act_q = reinterpret_cast<uint8_t*>(b + p.off_actq);
+  v.act_qp = reinterpret_cast<uint8_t*>(b + p.off_actqp);
   v.act_s = reinterpret_cast<float*>(b + p.off_acts);
   v.mid = reinterpret_cast<float*>(b + p.off_mid);
   v.midq = reinterpret_cast<uint8_t*>(b + p.off_midq);
@@ -267,6 +269,7 @@ moe_status step_args(const moe_decode_config& cfg, const Plan& p, int rows,
   d.no_dedup = (cfg.flags & MOE_F_NO_DEDUP) ? 1 : 0;
   d.eps = cfg.rms_eps;
   d.act_bf16 = cfg.act_fmt == MOE_ACT_BF16 ? 1 : 0;
+  d.act_q1 = cfg.routed_fmt == MOE_FMT_Q1_G128 ? 1 : 0;
   const int picks = 8 * rows;
   d.groups = d.no_dedup ? picks : (picks < p.E ? picks : p.E);
   d.wait_ticks = kDefaultWaitTicks;

@@ -53,6 +53,7 @@ struct Ws {
   uint8_t* grp_rows;      // [G][8] using rows, ascending
   uint8_t* grp_nrows;     // [G]
   uint8_t* act_q;         // [max_rows][H]
+  uint8_t* act_qp;        // [max_rows][H] act_q with each 128-block in 1-bit operand order (1-bit experts)
   float* act_s;           // [max_rows][H/128]
   uint16_t* act_u;        // [max_rows][H] u = bf16(x * gamma) (bf16 activations only)
   // per (row, pick) with pick 8 = the shared expert: u = row * 9 + pick
@@ -75,6 +76,7 @@ struct Dims {
   int ks;              // up/gate K parts (divides H/128)
   int no_dedup;        // 1: one group per (row, pick)
   int act_bf16;        // 1: the experts take u (bf16), not FP8 activation blocks
+  int act_q1;          // 1: the router also writes act_qp (1-bit routed experts)
   int groups;          // routed groups the up/gate grid covers (8 * rows, or E if fewer)
   uint32_t wait_ticks; // cap of a routed block's wait for its record (100 MHz ticks)
   int withhold;        // 1: the routing block publishes no records (failure tests)
@@ -288,6 +290,46 @@ __device__ __forceinline__ v8i q1_fp8_operand(uint32_t w, const uint32_t* k, uin
     a[j] = (int)((__builtin_amdgcn_alignbit(z, z, (4 * j - 14) & 31) & k[2]) | t);
   }
   return a;
+}
+
+// ---- 1-bit weights as FP4 (E2M1) MFMA operands, against FP8 codes.
+// +-1 in E2M1 is 0x2 / 0xA, so a weight is a nibble with its sign bit at bit
+// 3.  In the 16x16x128 f8f6f4 MFMA, lane group g = l/16 of an FP4 A operand
+// holds K 32g .. 32g+31 (nibble s%8 of dword s/8 is K 32g + s), while an FP8 B
+// operand's 32 bytes hold K 16g .. 16g+15 (bytes 0-15) and 64+16g .. +15
+// (bytes 16-31); the pairing of A and B is by that K.  Lane group g's A is
+// built from the sign dword g of the group (weights 32g .. 32g+31) with the
+// weights permuted: dword d, nibble i (K 32g + 8d + i) takes weight
+// 32g + d + 4i, so dword d is the sign word shifted left by 3 - d, masked to
+// the nibble sign bits and or'ed with 1.0 in every nibble (two operations a
+// dword).  The activation codes then go to the B operand permuted the same
+// way, which the router writes once per step (q1_act_pos, act_qp): lane group
+// g reads bytes 32g .. 32g+31 of each 128-block of that copy as its B.
+// `m8` and `o2` are 0x88888888 and 0x22222222 held in vector registers (see
+// q1_in_vgpr), so that the mask and the or are one v_and_or_b32.
+__device__ __forceinline__ v8i q1_fp4_operand(uint32_t w, uint32_t m8, uint32_t o2) {
+  v8i a;
+  a[0] = (int)(((w << 3) & m8) | o2);
+  a[1] = (int)(((w << 2) & m8) | o2);
+  a[2] = (int)(((w << 1) & m8) | o2);
+  a[3] = (int)((w & m8) | o2);
+  a[4] = a[5] = a[6] = a[7] = 0;  // not read for an FP4 operand
+  return a;
+}
+// Byte offset, inside a 128-block of act_qp, of the pair of activations
+// 8t + j and 8t + j + 4 (t < 16, j < 4; the two are adjacent there): the K of
+// the A slot holding activation n = 32g + r is h = 32g + 8(r%4) + r/4, and h
+// sits at byte 32(h/16) + h%16 of the copy for h < 64, else at
+// 32((h-64)/16) + 16 + h%16.
+__device__ __forceinline__ uint32_t q1_act_pos(int t, int j) {
+  const int g = t >> 2, tt = t & 3;
+  return g < 2 ? (uint32_t)(32 * (2 * g + (j >> 1)) + 8 * (j & 1) + 2 * tt)
+               : (uint32_t)(32 * (2 * (g - 2) + (j >> 1)) + 16 + 8 * (j & 1) + 2 * tt);
+}
+// 16x16x128 FP4 (A) x FP8 (B) -> fp32 MFMA, unit scales.
+__device__ __forceinline__ v4f mfma_fp4_fp8(const v8i& a, const v8i& b) {
+  v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 4, 0, 0, 127, 0, 127);
 }
 
 // One 36-byte chunk (9 dwords, as loaded) re-aligned: the 16 sign bytes of

@@ -142,6 +142,14 @@ __global__ __launch_bounds__(1024) void moe_router_kernel(const uint16_t* __rest
         pk.x = c[0] | (c[1] << 16);
         pk.y = c[2] | (c[3] << 16);
         *reinterpret_cast<uint2*>(ws.act_q + ((uint32_t)r * H + col)) = pk;
+        if (d.act_q1) {  // the same codes in 1-bit operand order: 4 adjacent pairs
+          uint8_t* qb = ws.act_qp + ((uint32_t)r * H + (col & ~127));
+          const int t = (col & 127) >> 3;
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            *reinterpret_cast<uint16_t*>(qb + q1_act_pos(t, j)) =
+                (uint16_t)__builtin_amdgcn_perm(pk.y, pk.x, (uint32_t)((4 + j) << 8 | j));
+        }
         if (s == 0) ws.act_s[r * nkb + kb] = sc;
       } while (false);
     }

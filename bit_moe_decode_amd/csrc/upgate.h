@@ -384,13 +384,13 @@ __device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims
   // past the range, so their loads return zeros without a memory access
   // (as in ug_fp4; their MFMA columns are never stored)
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(ws.act_q), (short)0, d.rows * H, 0x00020000);
+      const_cast<uint8_t*>(ws.act_qp), (short)0, d.rows * H, 0x00020000);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(ws.act_s), (short)0, d.rows * nkbh * 4, 0x00020000);
   const uint32_t aoff =
       j.live ? (uint32_t)(j.row * H + (lane >> 4) * 32 + kb0 * 128) : 0x80000000u;
   const uint32_t soff = j.live ? (uint32_t)((j.row * nkbh + kb0) * 4) : 0x80000000u;
-  const uint32_t one = q1_in_vgpr(d.q1k[3]);
+  const uint32_t m8 = q1_in_vgpr(0x88888888u), o2 = q1_in_vgpr(0x22222222u);
 
   auto issue = [&](UgStageQ1& st, int it) {
     ld_nt_chunk36(src + 18 * it, st.w);
@@ -423,8 +423,8 @@ __device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims
         const uint32_t wg = lds[((0 * 2 + q) * 8 + 4 * h + g) * 16 + col];
         const uint32_t wu = lds[((1 * 2 + q) * 8 + 4 * h + g) * 16 + col];
         const v8i bv = cat8(st.a[gi][0], st.a[gi][1]);
-        const v4f cg = mfma_fp8(q1_fp8_operand(wg, d.q1k, one), bv);
-        const v4f cu = mfma_fp8(q1_fp8_operand(wu, d.q1k, one), bv);
+        const v4f cg = mfma_fp4_fp8(q1_fp4_operand(wg, m8, o2), bv);
+        const v4f cu = mfma_fp4_fp8(q1_fp4_operand(wu, m8, o2), bv);
 #pragma unroll
         for (int v = 0; v < 4; v++) {
           accg[v] = fmaf(cg[v], q1_d(dg[v], h) * st.sa[gi], accg[v]);
