@@ -274,10 +274,6 @@ moe_status step_args(const moe_decode_config& cfg, const Plan& p, int rows,
   d.groups = d.no_dedup ? picks : (picks < p.E ? picks : p.E);
   d.wait_ticks = kDefaultWaitTicks;
   d.withhold = 0;
-  d.q1k[0] = 0x0000FFFFu;  // 1-bit operand constants (see q1_fp8_operand)
-  d.q1k[1] = 0x00800080u;
-  d.q1k[2] = 0x80008000u;
-  d.q1k[3] = 0x38383838u;
   return MOE_OK;
 }
 

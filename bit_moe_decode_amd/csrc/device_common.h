@@ -81,9 +81,6 @@ struct Dims {
   uint32_t wait_ticks; // cap of a routed block's wait for its record (100 MHz ticks)
   int withhold;        // 1: the routing block publishes no records (failure tests)
   float eps;
-  // 1-bit expert operand constants (0x0000FFFF, 0x00800080, 0x80008000,
-  // 0x38383838), passed in so that they sit in registers: see q1_fp8_operand
-  uint32_t q1k[4];
 };
 
 struct Weights {
@@ -259,37 +256,16 @@ __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// ---- 1-bit (Q1_0_G128) weights as FP8 MFMA operands.
-// A group of 128 weights is an fp16 d and 16 sign bytes; weight k of the
-// group is -d when bit k%8 of byte k/8 is set, else +d.  Two groups (36
-// bytes) make a dword-aligned chunk.  The FP8 MFMA takes the weights as E4M3
-// +-1 (0x38 / 0xB8) and the group's sum is scaled by d afterwards.
+// ---- 1-bit (Q1_0_G128) weights.  A group of 128 weights is an fp16 d and
+// 16 sign bytes; weight k of the group is -d when bit k%8 of byte k/8 is set,
+// else +d.  Two groups (36 bytes) make a dword-aligned chunk.  The MFMA takes
+// the weights as +-1 and the group's sum is scaled by d afterwards.
 //
-// Lane l's A operand of a 16x16x128 MFMA is 32 weights of its row, 4 to a
-// dword: the 32 sign bits w of sign dword l/16 of the group.  Dword j (weights
-// 4j .. 4j+3) needs bit 4j+i at bit 8i+7 over 0x38 in every byte.  With
-// R = rotl(w, 14) holding bit i+2 at i+16 (mod 32), Z = the half of w that
-// holds bits 4j .. 4j+3 merged with the other half of R holds bit i at i and
-// bit i+2 at i+16, so rotr(Z, 4j-7) puts bits 4j and 4j+2 at 7 and 23 and
-// rotr(Z, 4j-14) puts bits 4j+1 and 4j+3 at 15 and 31.  The masks and 1.0
-// come in registers (Dims::q1k: gfx950's three-operand instructions take no
-// literal, and with the constants in sight the compiler folds the rotations
-// into quarter-rate multiplies); `one` is q1k[3] in a vector register.
+// A constant copied into a vector register (a DPP move the compiler does not
+// fold back): gfx950's three-operand instructions take no literal, and with
+// both operand constants in registers a mask and an or are one v_and_or_b32.
 __device__ __forceinline__ uint32_t q1_in_vgpr(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xE4, 0xF, 0xF, false);
-}
-__device__ __forceinline__ v8i q1_fp8_operand(uint32_t w, const uint32_t* k, uint32_t one) {
-  const uint32_t r = __builtin_amdgcn_alignbit(w, w, 18);  // rotl(w, 14)
-  const uint32_t zl = (w & k[0]) | (r & ~k[0]);              // bits 0..15 and their +2 partners
-  const uint32_t zh = (w & ~k[0]) | (r & k[0]);              // bits 16..31
-  v8i a;
-#pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const uint32_t z = j < 4 ? zl : zh;
-    const uint32_t t = (__builtin_amdgcn_alignbit(z, z, (4 * j - 7) & 31) & k[1]) | one;
-    a[j] = (int)((__builtin_amdgcn_alignbit(z, z, (4 * j - 14) & 31) & k[2]) | t);
-  }
-  return a;
 }
 
 // ---- 1-bit weights as FP4 (E2M1) MFMA operands, against FP8 codes.

@@ -88,7 +88,7 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, flo
 // step's midq / midqs.
 __device__ __forceinline__ void dn_quant_mid(const Ws& ws, const Dims& d, int nrows,
                                              const DnCols& cols, bool publish, uint8_t* s_q,
-                                             float* s_qs) {
+                                             float* s_qs, bool q1_order = false) {
   const int tid = threadIdx.x, hw = tid >> 5, l = tid & 31, nhw = blockDim.x >> 5;
   const int nkb = d.I / 128, cs = dn_code_stride(d.I), T = nrows * nkb;
   for (int t = hw; t < T; t += nhw) {
@@ -102,7 +102,19 @@ __device__ __forceinline__ void dn_quant_mid(const Ws& ws, const Dims& d, int nr
     m = max(m, (uint32_t)__shfl_xor((int)m, 16, kWave));
     const float s = __uint_as_float(m) / 448.0f;
     const uint32_t q = s > 0.f ? f32x4_to_e4m3(v[0] / s, v[1] / s, v[2] / s, v[3] / s) : 0u;
-    *reinterpret_cast<uint32_t*>(s_q + c * cs + kb * 128 + 4 * l) = q;
+    if (!q1_order) {
+      *reinterpret_cast<uint32_t*>(s_q + c * cs + kb * 128 + 4 * l) = q;
+    } else {
+      // the 1-bit operand order of the block (as the router's act_qp): code
+      // 4l + j sits at the B byte of K h = 32(l/8) + 8j + l%8
+      uint8_t* qb = s_q + c * cs + kb * 128;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int h = 32 * (l >> 3) + 8 * j + (l & 7);
+        const int pos = h < 64 ? 32 * (h >> 4) + (h & 15) : 32 * ((h - 64) >> 4) + 16 + (h & 15);
+        qb[pos] = (uint8_t)(q >> (8 * j));
+      }
+    }
     if (l == 0) s_qs[c * nkb + kb] = s;
     if (publish) {
       *reinterpret_cast<uint32_t*>(ws.midq + src) = q;
@@ -385,7 +397,7 @@ __device__ __forceinline__ void down_q1_consume(const Dims& d, const DnQ1Items& 
   const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
   const int lrow = lane >> 2, lq = lane & 3;
   const int nchunk = d.I / 256;
-  const uint32_t one = q1_in_vgpr(d.q1k[3]);
+  const uint32_t m8 = q1_in_vgpr(0x88888888u), o2 = q1_in_vgpr(0x22222222u);
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     if (4 * i >= nchunk) break;  // wave-uniform
@@ -402,8 +414,8 @@ __device__ __forceinline__ void down_q1_consume(const Dims& d, const DnQ1Items& 
       for (int h = 0; h < 2; h++) {
         const int kb = 2 * (4 * i + q) + h;  // group = mid block
         const uint32_t ws = lds[(q * 8 + 4 * h + g) * 16 + col];
-        const v4f c = mfma_fp8(q1_fp8_operand(ws, d.q1k, one),
-                               cat8(ld16(pm + kb * 128), ld16(pm + kb * 128 + 16)));
+        const v4f c = mfma_fp4_fp8(q1_fp4_operand(ws, m8, o2),
+                                   cat8(ld16(pm + kb * 128), ld16(pm + kb * 128 + 16)));
         const float sm = psm[kb];
 #pragma unroll
         for (int v = 0; v < 4; v++) acc[v] = fmaf(c[v], q1_d(dv[v], h) * sm, acc[v]);
@@ -521,7 +533,7 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
     down_q1_issue(w, d, e, h0, it);
     uint8_t* s_q = dyn;
     float* s_qs = reinterpret_cast<float*>(dyn + (size_t)d.rows * dn_code_stride(I));
-    dn_quant_mid(ws, d, nrows, cols, b == 0, s_q, s_qs);
+    dn_quant_mid(ws, d, nrows, cols, b == 0, s_q, s_qs, true);
     __syncthreads();
     const int cq = col < nrows ? col : 0;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
