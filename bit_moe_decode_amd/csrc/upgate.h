@@ -82,6 +82,8 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const v8i& a, const v8i& b, int scal
 struct UgJob {
   int e, row, n0;  // expert (-1: shared), activation row of the lane's column, first row
   bool live;       // the lane's column is one of the expert's using rows
+  int nrows;       // the expert's using rows (the block's columns)
+  uint64_t rows8;  // their activation rows, one byte each (routed experts)
 };
 
 // FP8 weights: K blocks kb0 .. kb0 + nk of the slab.
@@ -362,15 +364,26 @@ __device__ __forceinline__ void ug_fp4(const Weights& w, const Ws& ws, const Dim
 // E4M3 +-1 operands from it and runs one FP8 MFMA per matrix against the
 // using rows' activation codes; each row's sum is scaled by its group d and
 // the activation block scale and accumulated.
+// Per wave: the item's activation codes of up to 8 columns (512 bytes each:
+// its 4 groups of act_qp) and their 32 block scales, staged through LDS.
+constexpr int kUgQ1Bytes = 8 * 512 + 32 * 4;
+template <int NA>
 struct UgStageQ1 {
   uint32_t w[9];  // the lane's chunk
-  u32x4 a[4][2];  // activation codes of the item's 4 groups (operand order)
-  float sa[4];
+  u32x4 a[NA];    // 16 bytes of columns 2i + l/32 of the item (act_qp)
+  float s;        // scale of column l/4, group l%4 (l < 32)
 };
-template <int P>
+// 1-bit weights: groups kb0 .. kb0 + nk of the slab, items of 4 groups.  The
+// activation operand of a lane is 32 bytes a group of its column; loaded by
+// each lane from memory that is 9 loads an item (for 16 columns, most of them
+// unused), which kept the texture units busy 85% of the launch.  Instead the
+// wave loads only its NA pairs of using columns' 512 bytes an item (one
+// 16-byte load a lane each) and one scale a lane, parks them in its LDS area
+// `sq`, and each lane reads its operands from there.
+template <int P, int NA>
 __device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims& d, UgJob j,
-                                      int kb0, int nk, uint32_t* lds, int lane, float* accg,
-                                      float* accu) {
+                                      int kb0, int nk, uint32_t* lds, uint8_t* sq, int lane,
+                                      float* accg, float* accu) {
   const int H = d.H, nkbh = H / 128;
   const size_t rb = (size_t)18 * nkbh;  // bytes per row
   const size_t ebytes = (size_t)d.I * rb;
@@ -380,38 +393,49 @@ __device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims
   const uint32_t* src =
       reinterpret_cast<const uint32_t*>(base + (size_t)(j.n0 + lrow) * rb) + 9 * (kb0 / 2 + lq);
   // activation codes and block scales through buffer resources over the
-  // step's rows: lanes of columns past the expert's using rows take offsets
+  // step's rows: lanes for columns past the expert's using rows take offsets
   // past the range, so their loads return zeros without a memory access
-  // (as in ug_fp4; their MFMA columns are never stored)
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(ws.act_qp), (short)0, d.rows * H, 0x00020000);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(ws.act_s), (short)0, d.rows * nkbh * 4, 0x00020000);
-  const uint32_t aoff =
-      j.live ? (uint32_t)(j.row * H + (lane >> 4) * 32 + kb0 * 128) : 0x80000000u;
-  const uint32_t soff = j.live ? (uint32_t)((j.row * nkbh + kb0) * 4) : 0x80000000u;
+  auto crow = [&](int c) { return (int)((j.rows8 >> (8 * c)) & 0xFF); };
+  uint32_t aoff[NA];
+#pragma unroll
+  for (int i = 0; i < NA; i++) {
+    const int c = 2 * i + (lane >> 5);
+    aoff[i] = c < j.nrows ? (uint32_t)(crow(c) * H + kb0 * 128 + 16 * (lane & 31)) : 0x80000000u;
+  }
+  const int sc = lane >> 2;
+  const uint32_t soff =
+      lane < 32 && sc < j.nrows ? (uint32_t)((crow(sc) * nkbh + kb0 + (lane & 3)) * 4) : 0x80000000u;
   const uint32_t m8 = q1_in_vgpr(0x88888888u), o2 = q1_in_vgpr(0x22222222u);
+  // the lane's operand column in the staged area (columns past the rows read
+  // column 0; their MFMA columns are never stored)
+  const int cq = j.live ? col : 0;
+  const uint8_t* pa = sq + cq * 512 + 32 * g;
+  const float* ps = reinterpret_cast<const float*>(sq + 8 * 512) + 4 * cq;
 
-  auto issue = [&](UgStageQ1& st, int it) {
+  auto issue = [&](UgStageQ1<NA>& st, int it) {
     ld_nt_chunk36(src + 18 * it, st.w);
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const int o = (int)(aoff + (uint32_t)(4 * it + q) * 128);
-      st.a[q][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, o, 0, 0));
-      st.a[q][1] =
-          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, o + 16, 0, 0));
-      st.sa[q] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(soff + (uint32_t)(4 * it + q) * 4),
-                                                      0, 0));
-    }
+    for (int i = 0; i < NA; i++)
+      st.a[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)(aoff[i] + 512u * it), 0, 0));
+    st.s = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(soff + 16u * it), 0, 0));
   };
-  auto consume = [&](UgStageQ1& st) {
+  auto consume = [&](UgStageQ1<NA>& st) {
     uint32_t u[8], dd;
     q1_chunk_split(st.w, u, &dd);
     const int area = (m * 2 + lq);
 #pragma unroll
     for (int i = 0; i < 8; i++) lds[(area * 8 + i) * 16 + lrow] = u[i];
     lds[512 + area * 16 + lrow] = dd;
+#pragma unroll
+    for (int i = 0; i < NA; i++)
+      *reinterpret_cast<u32x4*>(sq + (2 * i + (lane >> 5)) * 512 + 16 * (lane & 31)) = st.a[i];
+    if (lane < 32) reinterpret_cast<float*>(sq + 8 * 512)[lane] = st.s;
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int q = 0; q < 2; q++) {
@@ -422,20 +446,22 @@ __device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims
         const int gi = 2 * q + h;  // group of the item
         const uint32_t wg = lds[((0 * 2 + q) * 8 + 4 * h + g) * 16 + col];
         const uint32_t wu = lds[((1 * 2 + q) * 8 + 4 * h + g) * 16 + col];
-        const v8i bv = cat8(st.a[gi][0], st.a[gi][1]);
+        const v8i bv = cat8(*reinterpret_cast<const u32x4*>(pa + 128 * gi),
+                            *reinterpret_cast<const u32x4*>(pa + 128 * gi + 16));
+        const float sa = ps[gi];
         const v4f cg = mfma_fp4_fp8(q1_fp4_operand(wg, m8, o2), bv);
         const v4f cu = mfma_fp4_fp8(q1_fp4_operand(wu, m8, o2), bv);
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-          accg[v] = fmaf(cg[v], q1_d(dg[v], h) * st.sa[gi], accg[v]);
-          accu[v] = fmaf(cu[v], q1_d(du[v], h) * st.sa[gi], accu[v]);
+          accg[v] = fmaf(cg[v], q1_d(dg[v], h) * sa, accg[v]);
+          accu[v] = fmaf(cu[v], q1_d(du[v], h) * sa, accu[v]);
         }
       }
     }
     asm volatile("" ::: "memory");
   };
   const int ni = nk / 4;
-  UgStageQ1 st[P];
+  UgStageQ1<NA> st[P];
 #pragma unroll
   for (int p = 0; p < P; p++) issue(st[p], p);
   for (int k0 = 0; k0 < ni - P; k0 += P) {
@@ -451,9 +477,12 @@ __device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims
 
 typedef uint8_t UgTiles[4][2][kTileBytes];  // per wave: gate and up weight tiles
 constexpr int kUgE8Bytes = 32 * kUgE8Items * 8;  // per wave: MXFP4 exponents (ug_fp4, E8)
-// LDS of the block's exponent areas (4 waves; a token size for other formats)
+// LDS of the block's per-wave areas: MXFP4 exponents, 1-bit staged activations
+// (4 waves; a token size for FP8)
 template <int RF>
-constexpr int ug_e8_lds() { return RF == kFmtMxfp4 ? 4 * kUgE8Bytes : 16; }
+constexpr int ug_e8_lds() {
+  return RF == kFmtMxfp4 ? 4 * kUgE8Bytes : (RF == kFmtQ1 ? 4 * kUgQ1Bytes : 16);
+}
 
 // Items in flight per wave, dividing the wave's items: FP8 K blocks the
 // largest of 4, 2, 1 (ring_depth); in MXFP4 and 1-bit layers, where more
@@ -547,7 +576,7 @@ __device__ __forceinline__ void upgate_block(const Weights& w, const Ws& ws, con
     row = col < nrows ? (int)((rows8 >> (8 * (col & 7))) & 0xFF) : 0;
   }
   const int slab = b * spb + wv / KS, kp = wv % KS;
-  const UgJob j{e, row, slab * 16, col < nrows};
+  const UgJob j{e, row, slab * 16, col < nrows, nrows, rows8};
   float accg[4] = {0.f, 0.f, 0.f, 0.f}, accu[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (AB) {  // bf16 activations (FP8 weights only)
     const int nk = d.H / 128 / KS;
@@ -562,8 +591,14 @@ __device__ __forceinline__ void upgate_block(const Weights& w, const Ws& ws, con
                         s_e8 + wv * kUgE8Bytes);
   } else if (RF == kFmtQ1 && e >= 0) {
     const int nk = d.H / 128 / KS;  // groups per part, a multiple of 4
-    ug_q1<P4>(w, ws, d, j, kp * nk, nk, reinterpret_cast<uint32_t*>(s_tile[wv][0]), lane, accg,
-              accu);
+    uint32_t* tl = reinterpret_cast<uint32_t*>(s_tile[wv][0]);
+    uint8_t* sq = s_e8 + wv * kUgQ1Bytes;
+    if (nrows <= 2)
+      ug_q1<P4, 1>(w, ws, d, j, kp * nk, nk, tl, sq, lane, accg, accu);
+    else if (nrows <= 4)
+      ug_q1<P4, 2>(w, ws, d, j, kp * nk, nk, tl, sq, lane, accg, accu);
+    else  // 5 to 8 using rows (rare): one item in flight
+      ug_q1<1, 4>(w, ws, d, j, kp * nk, nk, tl, sq, lane, accg, accu);
   } else {
     const int nk = d.H / 128 / KS;
     ug_fp8<P>(w, ws, d, j, kp * nk, nk, s_tile[wv][0], s_tile[wv][1], lane, accg, accu);
