@@ -62,7 +62,7 @@ __device__ __forceinline__ void publish_records(const Ws& ws, const Dims& d,
 }
 
 template <int KPL, int RF, int P, int P4, bool AB>
-__global__ __launch_bounds__(256) void moe_route_kernel(Weights w, Ws ws, Dims d) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RF == kFmtQ1 ? 4 : 1))) void moe_route_kernel(Weights w, Ws ws, Dims d) {
   __shared__ RouteSmem rs;
   __shared__ __align__(16) UgTiles s_tile;
   __shared__ __align__(16) uint8_t s_e8[ug_e8_lds<RF>()];
@@ -99,10 +99,13 @@ static void launch_fused(dim3 grid, const Weights& w, const Ws& ws, const Dims& 
 template <int KPL, int RF, int P>
 static void launch_fused_p4(int p4, dim3 grid, const Weights& w, const Ws& ws, const Dims& d,
                             hipStream_t stream) {
-  if (p4 == 2)
-    launch_fused<KPL, RF, P, 2>(grid, w, ws, d, stream);
-  else
-    launch_fused<KPL, RF, P, 1>(grid, w, ws, d, stream);
+  if constexpr (RF != kFmtQ1) {  // 1-bit items are never two deep
+    if (p4 == 2) {
+      launch_fused<KPL, RF, P, 2>(grid, w, ws, d, stream);
+      return;
+    }
+  }
+  launch_fused<KPL, RF, P, 1>(grid, w, ws, d, stream);
 }
 
 template <int KPL, int RF>
@@ -114,11 +117,13 @@ static void launch_fused_p(int p, int p4, dim3 grid, const Weights& w, const Ws&
       case 2: launch_fused<KPL, RF, 2, 1>(grid, w, ws, d, stream); break;
       default: launch_fused<KPL, RF, 1, 1>(grid, w, ws, d, stream); break;
     }
-  } else {  // MXFP4 and 1-bit layers: shared rings of at most 2
+  } else if constexpr (RF == kFmtMxfp4) {  // shared rings of at most 2
     if (p >= 2)
       launch_fused_p4<KPL, RF, 2>(p4, grid, w, ws, d, stream);
     else
       launch_fused_p4<KPL, RF, 1>(p4, grid, w, ws, d, stream);
+  } else {  // 1-bit layers: a shared ring of 1 (see launch_upgate)
+    launch_fused_p4<KPL, RF, 1>(p4, grid, w, ws, d, stream);
   }
 }
 
@@ -139,8 +144,8 @@ static hipError_t launch_route_k(int rfmt, const Weights& w, const Ws& ws, const
       launch_fused_p<KPL, kFmtMxfp4>(p > 2 ? 2 : p, ring_depth2(d.H / 256 / d.ks), grid, w, ws,
                                      d, stream);
       break;
-    case kFmtQ1:  // rings of 1 (1-bit) and at most 2 (FP8 shared): see launch_upgate
-      launch_fused_p<KPL, kFmtQ1>(p > 2 ? 2 : p, 1, grid, w, ws, d, stream);
+    case kFmtQ1:  // rings of 1 (1-bit and FP8 shared): see launch_upgate
+      launch_fused_p<KPL, kFmtQ1>(1, 1, grid, w, ws, d, stream);
       break;
     default: return hipErrorInvalidValue;
   }

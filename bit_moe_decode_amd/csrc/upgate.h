@@ -475,6 +475,127 @@ __device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims
   for (int p = 0; p < P; p++) consume(st[p]);
 }
 
+// 1-bit weights, blocks whose 4 waves split K (KS = 4) and hidden % 2048 ==
+// 0: the block's 16 rows are contiguous, so it loads them together, a round
+// at a time: round r is items 4r .. 4r+3 (288 bytes of each row of gate and
+// of up), loaded by consecutive lanes in consecutive 16-byte units (about 11
+// lines an instruction, against 32-64 when each lane fetches 36 bytes of its
+// own row: the per-wave form kept the texture units' data path stalled on the
+// cache) into the block's tile area, and wave w takes item 4r + w of every
+// row from there while the next round's loads are in flight.  Its activations
+// are staged as in ug_q1 (one item ahead).  Pieces of a round sit 304 bytes
+// apart in LDS (16-byte aligned; rows on distinct banks).
+constexpr int kQ1Piece = 304;
+template <int NA>
+__device__ __forceinline__ void ug_q1_blk(const Weights& w, const Ws& ws, const Dims& d, UgJob j,
+                                          uint8_t* sw, uint8_t* sq, int wv, int lane,
+                                          float* accg, float* accu) {
+  const int H = d.H, nkbh = H / 128, tid = threadIdx.x;
+  const size_t rb = (size_t)18 * nkbh;  // bytes per row
+  const size_t ebytes = (size_t)d.I * rb;
+  const int col = lane & 15, g = lane >> 4;
+  const int R = H / 2048;  // rounds of 4 items
+  const uint8_t* bg = w.gate_c + (size_t)j.e * ebytes + (size_t)j.n0 * rb;
+  const uint8_t* bu = w.up_c + (size_t)j.e * ebytes + (size_t)j.n0 * rb;
+  // this thread's 16-byte units of a round: u = tid + 256 i, piece u / 18
+  // (matrix, row), unit u % 18 of its 288 bytes; units past 576 load unit
+  // 575 again and are not stored
+  const uint8_t* up[3];
+  uint32_t lo[3];
+  bool uv[3];
+#pragma unroll
+  for (int i = 0; i < 3; i++) {
+    const int u0 = tid + 256 * i;
+    uv[i] = u0 < 576;
+    const int u = uv[i] ? u0 : 575, pc = u / 18, k = u - pc * 18;
+    up[i] = (pc < 16 ? bg : bu) + (size_t)(pc & 15) * rb + 16 * k;
+    lo[i] = (uint32_t)(pc * kQ1Piece + 16 * k);
+  }
+  // activations of the wave's items (as in ug_q1; item q = 4r + wv)
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(ws.act_qp), (short)0, d.rows * H, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(ws.act_s), (short)0, d.rows * nkbh * 4, 0x00020000);
+  auto crow = [&](int c) { return (int)((j.rows8 >> (8 * c)) & 0xFF); };
+  uint32_t aoff[NA];
+#pragma unroll
+  for (int i = 0; i < NA; i++) {
+    const int c = 2 * i + (lane >> 5);
+    aoff[i] = c < j.nrows ? (uint32_t)(crow(c) * H + 16 * (lane & 31)) : 0x80000000u;
+  }
+  const int sc = lane >> 2;
+  const uint32_t soff =
+      lane < 32 && sc < j.nrows ? (uint32_t)((crow(sc) * nkbh + (lane & 3)) * 4) : 0x80000000u;
+  const uint32_t m8 = q1_in_vgpr(0x88888888u), o2 = q1_in_vgpr(0x22222222u);
+  const int cq = j.live ? col : 0;
+  const uint8_t* pa = sq + cq * 512 + 32 * g;
+  const float* ps = reinterpret_cast<const float*>(sq + 8 * 512) + 4 * cq;
+
+  u32x4 wr[3];
+  u32x4 av[NA];
+  float sv;
+  auto issue = [&](int r) {
+#pragma unroll
+    for (int i = 0; i < 3; i++) wr[i] = ld_nt16(up[i] + 288 * r);
+    const uint32_t q = (uint32_t)(4 * r + wv);  // the wave's item
+#pragma unroll
+    for (int i = 0; i < NA; i++)
+      av[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)(aoff[i] + 512u * q), 0, 0));
+    sv = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(soff + 16u * q), 0, 0));
+  };
+  issue(0);
+  for (int r = 0; r < R; r++) {
+    if (r > 0) __syncthreads();  // the previous round is consumed
+#pragma unroll
+    for (int i = 0; i < 3; i++)
+      if (uv[i]) *reinterpret_cast<u32x4*>(sw + lo[i]) = wr[i];
+#pragma unroll
+    for (int i = 0; i < NA; i++)
+      *reinterpret_cast<u32x4*>(sq + (2 * i + (lane >> 5)) * 512 + 16 * (lane & 31)) = av[i];
+    if (lane < 32) reinterpret_cast<float*>(sq + 8 * 512)[lane] = sv;
+    __syncthreads();
+    if (r + 1 < R) issue(r + 1);
+    // item 4r + wv: 72 bytes at 72 wv of every piece; group gi at 18 gi (its
+    // fp16 d, then 16 sign bytes)
+#pragma unroll
+    for (int gi = 0; gi < 4; gi++) {
+      const int go = 72 * wv + 18 * gi;  // even gi: go % 4 == 0, odd: 2
+      uint32_t wg, wu;
+      {
+        const int so = go + 2 + 4 * g;  // sign dword g: % 4 == 2 for even gi
+        const uint8_t* pg = sw + col * kQ1Piece;
+        const uint8_t* pu = sw + (16 + col) * kQ1Piece;
+        if (gi % 2 == 0) {
+          wg = __builtin_amdgcn_alignbyte(*reinterpret_cast<const uint32_t*>(pg + so + 2),
+                                          *reinterpret_cast<const uint32_t*>(pg + so - 2), 2);
+          wu = __builtin_amdgcn_alignbyte(*reinterpret_cast<const uint32_t*>(pu + so + 2),
+                                          *reinterpret_cast<const uint32_t*>(pu + so - 2), 2);
+        } else {
+          wg = *reinterpret_cast<const uint32_t*>(pg + so);
+          wu = *reinterpret_cast<const uint32_t*>(pu + so);
+        }
+      }
+      const v8i bv = cat8(*reinterpret_cast<const u32x4*>(pa + 128 * gi),
+                          *reinterpret_cast<const u32x4*>(pa + 128 * gi + 16));
+      const float sa = ps[gi];
+      const v4f cg = mfma_fp4_fp8(q1_fp4_operand(wg, m8, o2), bv);
+      const v4f cu = mfma_fp4_fp8(q1_fp4_operand(wu, m8, o2), bv);
+      const int dq = go & ~3, dh = (go & 2) * 8;  // the dword holding d, its half
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int n = 4 * g + v;  // output row of this lane's value v
+        const uint32_t dgw = *reinterpret_cast<const uint32_t*>(sw + n * kQ1Piece + dq);
+        const uint32_t duw = *reinterpret_cast<const uint32_t*>(sw + (16 + n) * kQ1Piece + dq);
+        accg[v] = fmaf(cg[v], q1_d(dgw >> dh, 0) * sa, accg[v]);
+        accu[v] = fmaf(cu[v], q1_d(duw >> dh, 0) * sa, accu[v]);
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with the tile area before the K-part sums
+}
+
 typedef uint8_t UgTiles[4][2][kTileBytes];  // per wave: gate and up weight tiles
 constexpr int kUgE8Bytes = 32 * kUgE8Items * 8;  // per wave: MXFP4 exponents (ug_fp4, E8)
 // LDS of the block's per-wave areas: MXFP4 exponents, 1-bit staged activations
@@ -593,7 +714,13 @@ __device__ __forceinline__ void upgate_block(const Weights& w, const Ws& ws, con
     const int nk = d.H / 128 / KS;  // groups per part, a multiple of 4
     uint32_t* tl = reinterpret_cast<uint32_t*>(s_tile[wv][0]);
     uint8_t* sq = s_e8 + wv * kUgQ1Bytes;
-    if (nrows <= 2)
+    if (KS == 4 && d.H % 2048 == 0 && nrows <= 4) {  // block-uniform
+      uint8_t* sw = &s_tile[0][0][0];
+      if (nrows <= 2)
+        ug_q1_blk<1>(w, ws, d, j, sw, sq, wv, lane, accg, accu);
+      else
+        ug_q1_blk<2>(w, ws, d, j, sw, sq, wv, lane, accg, accu);
+    } else if (nrows <= 2)
       ug_q1<P4, 1>(w, ws, d, j, kp * nk, nk, tl, sq, lane, accg, accu);
     else if (nrows <= 4)
       ug_q1<P4, 2>(w, ws, d, j, kp * nk, nk, tl, sq, lane, accg, accu);

@@ -7,7 +7,7 @@ namespace moe {
 
 // Up/gate blocks: the shared expert's slabs, then the routed groups'.
 template <int RF, int P, int P4, bool AB>
-__global__ __launch_bounds__(256) void moe_upgate_kernel(Weights w, Ws ws, Dims d) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RF == kFmtQ1 ? 4 : 1))) void moe_upgate_kernel(Weights w, Ws ws, Dims d) {
   __shared__ __align__(16) UgTiles s_tile;
   __shared__ __align__(16) uint8_t s_e8[ug_e8_lds<RF>()];
   __shared__ uint64_t s_rec;
@@ -40,10 +40,13 @@ static void launch_one(dim3 grid, const Weights& w, const Ws& ws, const Dims& d,
 template <int RF, int P>
 static void launch_p4(int p4, dim3 grid, const Weights& w, const Ws& ws,
                       const Dims& d, hipStream_t stream) {
-  if (p4 == 2)
-    launch_one<RF, P, 2>(grid, w, ws, d, stream);
-  else
-    launch_one<RF, P, 1>(grid, w, ws, d, stream);
+  if constexpr (RF != kFmtQ1) {  // 1-bit items are never two deep
+    if (p4 == 2) {
+      launch_one<RF, P, 2>(grid, w, ws, d, stream);
+      return;
+    }
+  }
+  launch_one<RF, P, 1>(grid, w, ws, d, stream);
 }
 
 hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& ws,
@@ -68,15 +71,12 @@ hipError_t launch_upgate(int rfmt, int max_groups, const Weights& w, const Ws& w
     else
       launch_p4<kFmtMxfp4, 1>(p4, grid, w, ws, d, stream);
   } else if (rfmt == kFmtQ1) {
-    // one 1-bit item (4 groups) in flight and at most 2 K blocks of the FP8
-    // shared expert: the 1-bit path gains from more waves, not from deeper
-    // rings (4 waves a SIMD against 2 with rings of 3 and 4: GLM step 238.8 ->
-    // 230.0 us at 8 rows, 145.3 -> 135.2 at 4, 58.1 -> 56.7 at 1, outputs
-    // bitwise equal); longer waves (2 or 1 K parts) were slower (248.0 / 257.0)
-    if (p >= 2)
-      launch_p4<kFmtQ1, 2>(1, grid, w, ws, d, stream);
-    else
-      launch_p4<kFmtQ1, 1>(1, grid, w, ws, d, stream);
+    // one 1-bit item in flight (a round of the block's rows, or a wave's
+    // item) and one K block of the FP8 shared expert: the 1-bit path gains
+    // from more waves, not from deeper rings; at 4 waves a SIMD (the kernels'
+    // register cap) a shared ring of 2 spilled registers and ran no faster
+    // (GLM step 130.2 against 130.6 us at 8 rows, 39.8 against 40.1 at 1)
+    launch_p4<kFmtQ1, 1>(1, grid, w, ws, d, stream);
   } else {
     return hipErrorInvalidValue;
   }
