@@ -425,8 +425,61 @@ __device__ __forceinline__ void down_q1_consume(const Dims& d, const DnQ1Items& 
   }
 }
 
+// 1-bit routed down when I % 1024 == 0: a wave's 16 output rows are
+// contiguous, so it loads them in octets of 8 groups (144 bytes a row, 2304
+// bytes a wave: 144 consecutive 16-byte units, lane l taking units l, l + 64
+// and l + 128) instead of 36-byte chunks of 16 rows a load, parks each octet
+// in its tile (rows 144 bytes = 36 dwords apart: distinct banks) and reads its
+// MFMA operands from there; two octets are in flight (octets past K load the
+// last one again and are not used).
+struct DnQ1Oct {
+  u32x4 v[3];
+};
+__device__ __forceinline__ void dn_q1_oct_load(const uint8_t* wb, size_t rb, int o, int lane,
+                                               DnQ1Oct& t) {
+#pragma unroll
+  for (int i = 0; i < 3; i++) {
+    int u = lane + 64 * i;
+    u = u < 144 ? u : 143;
+    const int row = u / 9, k = u - row * 9;
+    t.v[i] = ld_nt16(wb + (size_t)row * rb + 144 * o + 16 * k);
+  }
+}
+__device__ __forceinline__ void dn_q1_oct_consume(const DnQ1Oct& t, uint8_t* tile, int o,
+                                                  const uint8_t* pm, const float* psm,
+                                                  uint32_t m8, uint32_t o2, float* acc) {
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 3; i++)
+    if (lane + 64 * i < 144) *reinterpret_cast<u32x4*>(tile + 16 * (lane + 64 * i)) = t.v[i];
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int gi = 0; gi < 8; gi++) {
+    const int go = 18 * gi;  // the group's d, then its 16 sign bytes
+    const int so = go + 2 + 4 * g;
+    const uint8_t* pr = tile + col * 144;
+    const uint32_t ws = gi % 2 == 0
+                            ? __builtin_amdgcn_alignbyte(*reinterpret_cast<const uint32_t*>(pr + so + 2),
+                                                         *reinterpret_cast<const uint32_t*>(pr + so - 2), 2)
+                            : *reinterpret_cast<const uint32_t*>(pr + so);
+    const int kb = 8 * o + gi;  // group = mid block
+    const v4f c = mfma_fp4_fp8(q1_fp4_operand(ws, m8, o2),
+                               cat8(ld16(pm + kb * 128), ld16(pm + kb * 128 + 16)));
+    const float sm = psm[kb];
+    const int dq = go & ~3, dh = (go & 2) * 8;
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const uint32_t dw = *reinterpret_cast<const uint32_t*>(tile + (4 * g + v) * 144 + dq);
+      acc[v] = fmaf(c[v], q1_d(dw >> dh, 0) * sm, acc[v]);
+    }
+  }
+  asm volatile("" ::: "memory");  // this octet's reads before the next octet's writes
+}
+
+// (1-bit layers' down blocks held to 4 waves a SIMD: their octet loads need
+// more registers than the one-row step pays for in occupancy)
 template <int RF, int P, int WPB, int T4>
-__global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Dims d) {
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(RF == kFmtQ1 ? 4 : 1))) void moe_down_kernel(Weights w, Ws ws, Dims d) {
   __shared__ __align__(16) uint8_t s_tile[WPB][kTileBytes];
   __shared__ float s_e8tab[RF == kFmtMxfp4 ? 256 : 1];  // 2^(e-127) for each E8M0 code
   static_assert(RF != kFmtMxfp4 || WPB == 4, "the E8M0 table takes one code a thread");
@@ -523,6 +576,37 @@ __global__ __launch_bounds__(64 * WPB) void moe_down_kernel(Weights w, Ws ws, Di
         *reinterpret_cast<v4f*>(ws.ypart + (size_t)cols.u(col) * H + h0 + 16 * t +
                                 4 * (lane >> 4)) = v4f{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
     }
+    return;
+  }
+  if (RF == kFmtQ1 && g >= 0 && I % 1024 == 0) {
+    // 1-bit routed expert, octets of the wave's contiguous rows (above): the
+    // first two in flight while the block quantises mid into LDS
+    const int h0 = (b * WPB + wv) * 16;
+    const size_t rb = (size_t)18 * nkb;
+    const uint8_t* wb = w.down_c + ((size_t)e * H + h0) * rb;
+    const int no = I / 1024;
+    DnQ1Oct t0, t1;
+    dn_q1_oct_load(wb, rb, 0, lane, t0);
+    dn_q1_oct_load(wb, rb, no > 1 ? 1 : 0, lane, t1);
+    uint8_t* s_q = dyn;
+    float* s_qs = reinterpret_cast<float*>(dyn + (size_t)d.rows * dn_code_stride(I));
+    dn_quant_mid(ws, d, nrows, cols, b == 0, s_q, s_qs, true);
+    __syncthreads();
+    const int cq = col < nrows ? col : 0;
+    const uint8_t* pm = s_q + cq * dn_code_stride(I) + (lane >> 4) * 32;
+    const float* psm = s_qs + cq * nkb;
+    const uint32_t m8 = q1_in_vgpr(0x88888888u), o2 = q1_in_vgpr(0x22222222u);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int o = 0; o < no; o += 2) {
+      dn_q1_oct_consume(t0, s_tile[wv], o, pm, psm, m8, o2, acc);
+      dn_q1_oct_load(wb, rb, o + 2 < no ? o + 2 : no - 1, lane, t0);
+      if (o + 1 < no) dn_q1_oct_consume(t1, s_tile[wv], o + 1, pm, psm, m8, o2, acc);
+      dn_q1_oct_load(wb, rb, o + 3 < no ? o + 3 : no - 1, lane, t1);
+    }
+    pin4(acc);  // the MFMAs run with every lane, before the divergent store
+    if (col < nrows)
+      *reinterpret_cast<v4f*>(ws.ypart + (size_t)cols.u(col) * H + h0 + 4 * (lane >> 4)) =
+          v4f{acc[0], acc[1], acc[2], acc[3]};
     return;
   }
   if (RF == kFmtQ1 && g >= 0) {
