@@ -36,7 +36,10 @@ def _run(layer, x, cache=None, flags=0):
     dict(hidden=512, inter=256, n_experts=32, shared_inter=256, router_std=0.02),
     dict(hidden=1024, inter=768, n_experts=64, shared_inter=0, router_std=0.02),
     dict(hidden=2048, inter=4096, n_experts=32, shared_inter=4096, router_std=0.02),
-], ids=["h512-i256", "h1024-i768-noshared", "h2048-i4096"])
+    # two rounds of the up/gate's block loads (hidden / 2048), one octet of the
+    # down's (inter / 1024): the second octet in flight is a clamped reload
+    dict(hidden=4096, inter=1024, n_experts=32, shared_inter=1024, router_std=0.02),
+], ids=["h512-i256", "h1024-i768-noshared", "h2048-i4096", "h4096-i1024"])
 def test_q1_experts_small(shape):
     layer = S.make_layer(shape, routed_fmt=S.FMT_Q1, seed=5300 + shape["inter"], device="cuda")
     cache = {}
