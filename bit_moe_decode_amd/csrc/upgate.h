@@ -486,6 +486,7 @@ __device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims
 // are staged as in ug_q1 (one item ahead).  Pieces of a round sit 304 bytes
 // apart in LDS (16-byte aligned; rows on distinct banks).
 constexpr int kQ1Piece = 304;
+constexpr int kQ1Col = 528;  // staged activation columns of the block form
 template <int NA>
 __device__ __forceinline__ void ug_q1_blk(const Weights& w, const Ws& ws, const Dims& d, UgJob j,
                                           uint8_t* sw, uint8_t* sq, int wv, int lane,
@@ -527,9 +528,14 @@ __device__ __forceinline__ void ug_q1_blk(const Weights& w, const Ws& ws, const 
   const uint32_t soff =
       lane < 32 && sc < j.nrows ? (uint32_t)((crow(sc) * nkbh + (lane & 3)) * 4) : 0x80000000u;
   const uint32_t m8 = q1_in_vgpr(0x88888888u), o2 = q1_in_vgpr(0x22222222u);
+  // the wave's area: up to 4 staged columns 528 bytes apart (distinct banks
+  // for the lanes of different columns), their 32 scales, then the d table of
+  // the wave's item: entry (group gi, matrix m, row n) at float 32 gi + 16 m + n
   const int cq = j.live ? col : 0;
-  const uint8_t* pa = sq + cq * 512 + 32 * g;
-  const float* ps = reinterpret_cast<const float*>(sq + 8 * 512) + 4 * cq;
+  const uint8_t* pa = sq + cq * kQ1Col + 32 * g;
+  float* sst = reinterpret_cast<float*>(sq + 4 * kQ1Col);
+  const float* ps = sst + 4 * cq;
+  float* dt = sst + 32;
 
   u32x4 wr[3];
   u32x4 av[NA];
@@ -553,12 +559,19 @@ __device__ __forceinline__ void ug_q1_blk(const Weights& w, const Ws& ws, const 
       if (uv[i]) *reinterpret_cast<u32x4*>(sw + lo[i]) = wr[i];
 #pragma unroll
     for (int i = 0; i < NA; i++)
-      *reinterpret_cast<u32x4*>(sq + (2 * i + (lane >> 5)) * 512 + 16 * (lane & 31)) = av[i];
-    if (lane < 32) reinterpret_cast<float*>(sq + 8 * 512)[lane] = sv;
+      *reinterpret_cast<u32x4*>(sq + (2 * i + (lane >> 5)) * kQ1Col + 16 * (lane & 31)) = av[i];
+    if (lane < 32) sst[lane] = sv;
     __syncthreads();
     if (r + 1 < R) issue(r + 1);
     // item 4r + wv: 72 bytes at 72 wv of every piece; group gi at 18 gi (its
-    // fp16 d, then 16 sign bytes)
+    // fp16 d, then 16 sign bytes).  The wave's 128 d values first go to its
+    // table (two a lane), so a lane reads its 4 output rows' d in one load.
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const int e = lane + 64 * k, gi = e >> 5, pc = e & 31;  // pc = 16 m + n
+      dt[e] = q1_d(*reinterpret_cast<const uint16_t*>(sw + pc * kQ1Piece + 72 * wv + 18 * gi), 0);
+    }
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int gi = 0; gi < 4; gi++) {
       const int go = 72 * wv + 18 * gi;  // even gi: go % 4 == 0, odd: 2
@@ -582,16 +595,15 @@ __device__ __forceinline__ void ug_q1_blk(const Weights& w, const Ws& ws, const 
       const float sa = ps[gi];
       const v4f cg = mfma_fp4_fp8(q1_fp4_operand(wg, m8, o2), bv);
       const v4f cu = mfma_fp4_fp8(q1_fp4_operand(wu, m8, o2), bv);
-      const int dq = go & ~3, dh = (go & 2) * 8;  // the dword holding d, its half
+      const v4f dg = *reinterpret_cast<const v4f*>(dt + 32 * gi + 4 * g);
+      const v4f du = *reinterpret_cast<const v4f*>(dt + 32 * gi + 16 + 4 * g);
 #pragma unroll
       for (int v = 0; v < 4; v++) {
-        const int n = 4 * g + v;  // output row of this lane's value v
-        const uint32_t dgw = *reinterpret_cast<const uint32_t*>(sw + n * kQ1Piece + dq);
-        const uint32_t duw = *reinterpret_cast<const uint32_t*>(sw + (16 + n) * kQ1Piece + dq);
-        accg[v] = fmaf(cg[v], q1_d(dgw >> dh, 0) * sa, accg[v]);
-        accu[v] = fmaf(cu[v], q1_d(duw >> dh, 0) * sa, accu[v]);
+        accg[v] = fmaf(cg[v], dg[v] * sa, accg[v]);
+        accu[v] = fmaf(cu[v], du[v] * sa, accu[v]);
       }
     }
+    asm volatile("" ::: "memory");  // this item's table reads before the next round's writes
   }
   __syncthreads();  // every wave is done with the tile area before the K-part sums
 }
