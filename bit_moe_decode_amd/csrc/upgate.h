@@ -475,16 +475,17 @@ __device__ __forceinline__ void ug_q1(const Weights& w, const Ws& ws, const Dims
   for (int p = 0; p < P; p++) consume(st[p]);
 }
 
-// 1-bit weights, blocks whose 4 waves split K (KS = 4) and hidden % 2048 ==
-// 0: the block's 16 rows are contiguous, so it loads them together, a round
-// at a time: round r is items 4r .. 4r+3 (288 bytes of each row of gate and
-// of up), loaded by consecutive lanes in consecutive 16-byte units (about 11
-// lines an instruction, against 32-64 when each lane fetches 36 bytes of its
-// own row: the per-wave form kept the texture units' data path stalled on the
-// cache) into the block's tile area, and wave w takes item 4r + w of every
-// row from there while the next round's loads are in flight.  Its activations
-// are staged as in ug_q1 (one item ahead).  Pieces of a round sit 304 bytes
-// apart in LDS (16-byte aligned; rows on distinct banks).
+// 1-bit weights, blocks whose 4 waves split K (KS = 4), hidden % 2048 == 0
+// and up to 4 using rows: the block's 16 rows are contiguous, so it loads
+// them together, a round at a time: round r is items 4r .. 4r+3 (288 bytes of
+// each row of gate and of up), loaded by consecutive lanes in consecutive
+// 16-byte units (about 11 lines an instruction, against 32-64 when each lane
+// fetches 36 bytes of its own row: the per-wave form kept the texture units'
+// data path stalled on the cache) into the block's tile area, and wave w takes
+// item 4r + w of every row from there while the next round's loads are in
+// flight.  Its activations are staged as in ug_q1 (one item ahead).  Pieces
+// of a round sit 304 bytes apart in LDS (16-byte aligned; rows on distinct
+// banks).
 constexpr int kQ1Piece = 304;
 constexpr int kQ1Col = 528;  // staged activation columns of the block form
 template <int NA>
