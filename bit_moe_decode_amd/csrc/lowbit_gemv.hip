@@ -95,8 +95,11 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_kernel(const uint8_t* __re
 template <int KP>
 constexpr int lb_slot() { return 16 * KP + 4; }
 // chunks whose tables one round may hold (KP * M, at most 16 for the M and KP
-// the launcher picks: about 70 KB, two blocks a CU)
+// the launcher picks: about 70 KB, two blocks a CU); grids of at most one
+// block a CU (gfx950: 256 CUs) may take 32 (at most 136 KB), for fewer rounds
 constexpr int kLbRoundChunks = 19;
+constexpr int kLbRoundChunksOne = 32;
+constexpr int kLbCus = 256;
 
 typedef __attribute__((address_space(3))) float lds_float;
 __device__ __forceinline__ float lds_ld(uint32_t a) { return *(lds_float*)(uintptr_t)a; }
@@ -668,6 +671,7 @@ hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* 
   // gives 2048 blocks, else the largest that gives 256, else 16; chunks per
   // thread and round M the fewest (up to 5) that take all of K in one round,
   // as long as the round's tables stay within kLbRoundChunks chunks
+  // (kLbRoundChunksOne when the grid has at most one block a CU)
   if (k % 256 == 0) {
     int rbk = 16;
     for (int want : {2048, 256}) {
@@ -678,7 +682,8 @@ hipError_t launch_lowbit_q1(const uint8_t* blocks, const uint16_t* x, uint16_t* 
     const int nch = k / 256, kp = 256 / rbk;
     int m = (nch + kp - 1) / kp;
     if (m > 5) m = 5;
-    while (m > 1 && kp * m > kLbRoundChunks) m--;
+    const int lim = (n + rbk - 1) / rbk <= kLbCus ? kLbRoundChunksOne : kLbRoundChunks;
+    while (m > 1 && kp * m > lim) m--;
 #define LB_CASE(R)                                                           \
   case R:                                                                    \
     switch (m) {                                                             \
