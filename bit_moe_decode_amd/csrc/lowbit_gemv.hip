@@ -357,7 +357,8 @@ __global__ __launch_bounds__(256) void lowbit_gemv_q1_mfma_kernel(
   const int col = lane & 15, g = lane >> 4;
   const int spb = 4 / ks;
   const int slab = blockIdx.x * spb + wv / ks, kp = wv % ks;
-  const int nch = k / 256, nc = nch / ks, c0 = kp * nc;
+  // part kp: chunks kp nch / ks .. (kp + 1) nch / ks - 1 (at least one: ks <= nch)
+  const int nch = k / 256, c0 = kp * nch / ks, nc = (kp + 1) * nch / ks - c0;
   const int row = slab * 16 + col;
   const int rowc = row < n ? row : n - 1;  // rows past n decode the last row (not stored)
   const uint32_t* wrow = reinterpret_cast<const uint32_t*>(blocks + (size_t)rowc * 36 * nch);
@@ -636,18 +637,20 @@ static hipError_t lb_mfma4_launch(const uint8_t* blocks, const uint16_t* x, uint
 static hipError_t lb_mfma_launch(const uint8_t* blocks, const uint16_t* x, uint16_t* y, int rows,
                                  int n, int k, hipStream_t stream) {
   const int nch = k / 256, slabs = (n + 15) / 16;
-  int ks = 0;
-  for (int c : {1, 2, 4}) {
-    if (nch % c) continue;
+  // K parts a block (4 waves: 4 / ks slabs of ks parts): the fewest of 1 and
+  // 2 that give 512 blocks, else 4 (more waves for few weight rows), at most
+  // nch; parts of nch / ks chunks rounded down or up.  A ring of 2 chunks
+  // when every part's count is even, else 1.
+  int ks = 4;
+  for (int c : {1, 2})
     if ((slabs + 4 / c - 1) / (4 / c) >= 512) {
       ks = c;
       break;
     }
-  }
-  if (ks == 0) ks = nch % 4 == 0 ? 4 : (nch % 2 == 0 ? 2 : 1);
+  while (ks > nch) ks >>= 1;
   const int spb = 4 / ks;
   const dim3 grid((slabs + spb - 1) / spb);
-  if ((nch / ks) % 2 == 0)
+  if (nch % ks == 0 && (nch / ks) % 2 == 0)
     hipLaunchKernelGGL(lowbit_gemv_q1_mfma_kernel<2>, grid, dim3(256), 0, stream, blocks, x, y,
                        rows, n, k, ks, kSignK);
   else
