@@ -348,14 +348,14 @@ struct QmStage {
   u32x4 xb[8];    // the lane's input row at inputs 128h + 32s + 8(l/16) .. +8
 };
 
-template <int P>
-__global__ __launch_bounds__(256) void lowbit_gemv_q1_mfma_kernel(
+template <int P, int WPB>
+__global__ __launch_bounds__(64 * WPB) void lowbit_gemv_q1_mfma_kernel(
     const uint8_t* __restrict__ blocks, const uint16_t* __restrict__ x,
     uint16_t* __restrict__ y, int rows, int n, int k, int ks, SignK sk) {
-  __shared__ __align__(16) float s_part[4][256];    // per wave 16 x 16 sums, column-major
+  __shared__ __align__(16) float s_part[WPB][256];  // per wave 16 x 16 sums, column-major
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
-  const int spb = 4 / ks;
+  const int spb = WPB / ks;
   const int slab = blockIdx.x * spb + wv / ks, kp = wv % ks;
   // part kp: chunks kp nch / ks .. (kp + 1) nch / ks - 1 (at least one: ks <= nch)
   const int nch = k / 256, c0 = kp * nch / ks, nc = (kp + 1) * nch / ks - c0;
@@ -639,23 +639,35 @@ static hipError_t lb_mfma_launch(const uint8_t* blocks, const uint16_t* x, uint1
   const int nch = k / 256, slabs = (n + 15) / 16;
   // K parts a block (4 waves: 4 / ks slabs of ks parts): the fewest of 1 and
   // 2 that give 512 blocks, else 4 (more waves for few weight rows), at most
-  // nch; parts of nch / ks chunks rounded down or up.  A ring of 2 chunks
-  // when every part's count is even, else 1.
+  // nch; parts of nch / ks chunks rounded down or up.  Fewer than 256 slabs
+  // (a block a slab would leave CUs idle): blocks of 8 waves, one slab of 8
+  // parts.  A ring of 2 chunks when every part's count is even, else 1.
   int ks = 4;
   for (int c : {1, 2})
     if ((slabs + 4 / c - 1) / (4 / c) >= 512) {
       ks = c;
       break;
     }
+  const bool w8 = ks == 4 && slabs < 256 && nch >= 8;
+  if (w8) ks = 8;
   while (ks > nch) ks >>= 1;
-  const int spb = 4 / ks;
+  const int spb = (w8 ? 8 : 4) / ks;
   const dim3 grid((slabs + spb - 1) / spb);
-  if (nch % ks == 0 && (nch / ks) % 2 == 0)
-    hipLaunchKernelGGL(lowbit_gemv_q1_mfma_kernel<2>, grid, dim3(256), 0, stream, blocks, x, y,
-                       rows, n, k, ks, kSignK);
-  else
-    hipLaunchKernelGGL(lowbit_gemv_q1_mfma_kernel<1>, grid, dim3(256), 0, stream, blocks, x, y,
-                       rows, n, k, ks, kSignK);
+  const bool p2 = nch % ks == 0 && (nch / ks) % 2 == 0;
+  if (w8) {
+    if (p2)
+      hipLaunchKernelGGL((lowbit_gemv_q1_mfma_kernel<2, 8>), grid, dim3(512), 0, stream, blocks,
+                         x, y, rows, n, k, ks, kSignK);
+    else
+      hipLaunchKernelGGL((lowbit_gemv_q1_mfma_kernel<1, 8>), grid, dim3(512), 0, stream, blocks,
+                         x, y, rows, n, k, ks, kSignK);
+  } else if (p2) {
+    hipLaunchKernelGGL((lowbit_gemv_q1_mfma_kernel<2, 4>), grid, dim3(256), 0, stream, blocks, x,
+                       y, rows, n, k, ks, kSignK);
+  } else {
+    hipLaunchKernelGGL((lowbit_gemv_q1_mfma_kernel<1, 4>), grid, dim3(256), 0, stream, blocks, x,
+                       y, rows, n, k, ks, kSignK);
+  }
   return hipGetLastError();
 }
 
